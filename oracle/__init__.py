@@ -1,0 +1,166 @@
+"""fp64 CPU oracle for the Mamba-2 SSD chunked forward (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+import this package.  The product path (the HIP library and its Python
+binding) never imports, links or runs it, and the two share no code.
+
+The arithmetic lives in ``ssd_oracle.c`` (plain C, fp64, OpenMP over
+(batch, head) pairs); this module compiles it with gcc and marshals numpy
+arrays.  See the C file's header for what is computed and which passages of
+the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB = os.path.join(_HERE, "libssd_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ssd_oracle.c into libssd_oracle.so with gcc (-O2, OpenMP)."""
+    if (not force and os.path.exists(_LIB)
+            and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC)):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB)
+            i64, f32p, f64p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+            lib.oracle_chunk_cumsum.argtypes = [f32p, f32p, f64p, i64, i64,
+                                                i64, i64, ctypes.c_void_p, i64]
+            lib.oracle_chunk_cumsum.restype = None
+            lib.oracle_forward.argtypes = ([f32p] * 6 + [f64p] * 4 + [i64] * 7
+                                           + [ctypes.c_void_p, i64,
+                                              ctypes.c_int])
+            lib.oracle_forward.restype = None
+            lib.oracle_chunk_out.argtypes = ([f32p] * 6 + [f64p, f64p]
+                                             + [i64] * 7
+                                             + [ctypes.c_void_p, i64,
+                                                ctypes.c_int])
+            lib.oracle_chunk_out.restype = None
+            lib.oracle_max_threads.argtypes = []
+            lib.oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _pairs(pairs, batch, nheads):
+    if pairs is None:
+        return None, batch * nheads
+    p = np.ascontiguousarray(pairs, dtype=np.int64)
+    if p.ndim != 1 or (p.size and (p.min() < 0 or p.max() >= batch * nheads)):
+        raise ValueError("pairs must be indices b*nheads + h in range")
+    return p, int(p.size)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def chunk_cumsum(dt: np.ndarray, A: np.ndarray, chunk_size: int,
+                 pairs: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Stage 1: log2(e) * per-chunk inclusive cumsum of A_h * dt.
+
+    dt [b, L, H], A [H] -> g.  With pairs=None returns [b, H, L]; otherwise
+    [len(pairs), L] in the order given.
+    """
+    lib = _load()
+    dt, A = _f32(dt), _f32(A)
+    b, L, H = dt.shape
+    p, npairs = _pairs(pairs, b, H)
+    g = np.empty((npairs, L), dtype=np.float64)
+    lib.oracle_chunk_cumsum(_ptr(dt), _ptr(A), _ptr(g), b, L, H, chunk_size,
+                            _ptr(p), npairs)
+    return g.reshape(b, H, L) if pairs is None else g
+
+
+def forward(x, dt, A, B, C, D, init_state=None, *, chunk_size: int,
+            pairs: Optional[Sequence[int]] = None, want_y: bool = True,
+            want_states: bool = True, nthreads: int = 0) -> Dict[str, np.ndarray]:
+    """Token-by-token recurrence in fp64.
+
+    Returns a dict with
+      y      [b, L, H, P]      (pairs=None) or [npairs, L, P]
+      states [b, H, nc, P, N]  (pairs=None) or [npairs, nc, P, N]
+      final  [b, H, P, N]      (pairs=None) or [npairs, P, N]
+    """
+    lib = _load()
+    x, dt, A, B, C, D = map(_f32, (x, dt, A, B, C, D))
+    init = (None if init_state is None
+            else np.ascontiguousarray(init_state, dtype=np.float64))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nc = -(-L // chunk_size)
+    p, npairs = _pairs(pairs, b, H)
+    y = np.empty((npairs, L, P), np.float64) if want_y else None
+    st = np.empty((npairs, nc, P, N), np.float64) if want_states else None
+    fin = np.empty((npairs, P, N), np.float64)
+    lib.oracle_forward(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                       _ptr(init), _ptr(y), _ptr(st), _ptr(fin), b, L, H, P,
+                       N, G, chunk_size, _ptr(p), npairs, nthreads)
+    out = {"final": fin}
+    if pairs is None:
+        out["final"] = fin.reshape(b, H, P, N)
+        if want_y:
+            out["y"] = y.reshape(b, H, L, P).transpose(0, 2, 1, 3)
+        if want_states:
+            out["states"] = st.reshape(b, H, nc, P, N)
+    else:
+        if want_y:
+            out["y"] = y
+        if want_states:
+            out["states"] = st
+    return out
+
+
+def chunk_out(x, dt, A, B, C, D, states, *, chunk_size: int,
+              pairs: Optional[Sequence[int]] = None, nthreads: int = 0):
+    """Per-chunk outputs, restarting the recurrence from given states.
+
+    states: [b, H, nc, P, N] when pairs=None, else [npairs, nc, P, N]
+    (any float dtype; used in fp64).  Returns y in the same convention as
+    ``forward``.
+    """
+    lib = _load()
+    x, dt, A, B, C, D = map(_f32, (x, dt, A, B, C, D))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    nc = -(-L // chunk_size)
+    p, npairs = _pairs(pairs, b, H)
+    st = np.ascontiguousarray(states, dtype=np.float64).reshape(npairs, nc,
+                                                                 P, N)
+    y = np.empty((npairs, L, P), np.float64)
+    lib.oracle_chunk_out(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                         _ptr(D), _ptr(st), _ptr(y), b, L, H, P, N, G,
+                         chunk_size, _ptr(p), npairs, nthreads)
+    if pairs is None:
+        return y.reshape(b, H, L, P).transpose(0, 2, 1, 3)
+    return y

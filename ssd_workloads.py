@@ -1,0 +1,140 @@
+"""Seeded synthetic inputs for the Mamba-2 SSD chunked forward.
+
+This module only draws random numbers and rounds them to the storage type.
+It holds none of the method's arithmetic (no decay, cumsum, state or output
+math), so the CPU oracle and the HIP path can both be fed from it without
+sharing any of the computation under test.
+
+Workloads
+---------
+The five named workloads below fix shapes and value distributions.  The
+distributions follow the domain the pages state for the recurrence's inputs
+("Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+CUDA Tile", section "The Mamba-2 Recurrence": dt is positive, A is negative,
+so exp(A*dt) lies in (0, 1]).  dt arrives already passed through softplus; the
+method applies no further preprocessing to it.
+
+Draw order (fixed, one ``numpy.random.Generator(PCG64(seed))`` per workload):
+x, B, C, z_dt, u_A, D, init_state.  bf16 tensors are float32 draws rounded to
+bfloat16 with round-to-nearest-even, then held as float32 (every bf16 value
+is exactly representable in float32), so both sides read identical values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int      # P: size of x_t per head
+    dstate: int       # N: size of B_t and C_t (the state size)
+    ngroups: int      # G: B and C are shared by nheads/ngroups heads
+    chunk_size: int   # T
+    dtype: str        # "fp32" or "bf16": storage type of x, B, C
+    dt_shift: float   # dt = softplus(N(0,1) + dt_shift)
+    a_low: float      # A = -exp(U(a_low, a_high))
+    a_high: float
+    init_std: Optional[float]  # None: zero initial state
+
+    @property
+    def nchunks(self) -> int:
+        return -(-self.seqlen // self.chunk_size)
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # Tiny fp32 case the oracle finishes instantly.
+    "tiny_fp32": Workload("tiny_fp32", 1, 256, 2, 64, 64, 1, 64, "fp32",
+                          -2.0, 0.0, 1.5, None),
+    # Small-model layer (d_model 768, expand 2 -> 24 heads of 64).
+    "small_bf16": Workload("small_bf16", 4, 2048, 24, 64, 128, 1, 64, "bf16",
+                           -2.0, 0.0, 1.5, None),
+    # Large-model layer (d_model 2560, expand 2 -> 80 heads of 64).
+    "large_bf16": Workload("large_bf16", 2, 8192, 80, 64, 128, 1, 256, "bf16",
+                           -2.0, 0.0, 1.5, None),
+    # Long-sequence streaming prefill with a carried-in state.
+    "long_bf16": Workload("long_bf16", 1, 65536, 32, 64, 128, 1, 128, "bf16",
+                          -2.0, 0.0, 1.5, 0.1),
+    # Wide batch, grouped B/C (8 groups of 6 heads), stronger decay, fp32.
+    "wide_fp32": Workload("wide_fp32", 64, 1024, 48, 64, 64, 8, 64, "fp32",
+                          -1.0, -1.0, 2.0, None),
+}
+
+# Seeds are fixed per workload so every consumer draws the same arrays.
+SEEDS: Dict[str, int] = {"tiny_fp32": 1, "small_bf16": 2, "large_bf16": 3,
+                         "long_bf16": 4, "wide_fp32": 5}
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return float32.
+
+    Finite inputs only (the generators never produce NaN or Inf).
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    r = (u + bias) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
+
+
+def _softplus(z: np.ndarray) -> np.ndarray:
+    # log(1 + e^z), computed without overflow.
+    return np.logaddexp(0.0, z)
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw the inputs of workload ``w``.
+
+    Returns float32 numpy arrays, contiguous, in the layouts the method uses:
+      x     [batch, seqlen, nheads, headdim]
+      B, C  [batch, seqlen, ngroups, dstate]
+      dt    [batch, seqlen, nheads]
+      A, D  [nheads]
+      init_state [batch, nheads, headdim, dstate] or None
+    For bf16 workloads x, B, C hold bf16-representable values.
+    """
+    if seed is None:
+        seed = SEEDS.get(w.name, 0)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    x = rng.standard_normal((b, L, H, P), dtype=np.float32)
+    B = rng.standard_normal((b, L, G, N), dtype=np.float32)
+    C = rng.standard_normal((b, L, G, N), dtype=np.float32)
+    z = rng.standard_normal((b, L, H), dtype=np.float32)
+    u = rng.uniform(w.a_low, w.a_high, size=H)
+    D = rng.standard_normal(H).astype(np.float32)
+    init = None
+    if w.init_std is not None:
+        init = (rng.standard_normal((b, H, P, N), dtype=np.float32)
+                * np.float32(w.init_std))
+    dt = _softplus(z.astype(np.float64) + w.dt_shift).astype(np.float32)
+    A = (-np.exp(u)).astype(np.float32)
+    if w.dtype == "bf16":
+        x, B, C = round_to_bf16(x), round_to_bf16(B), round_to_bf16(C)
+    elif w.dtype != "fp32":
+        raise ValueError(f"unknown dtype {w.dtype!r}")
+    return {"x": x, "B": B, "C": C, "dt": dt, "A": A, "D": D,
+            "init_state": init}
+
+
+def small_variant(w: Workload, **kw) -> Workload:
+    """A reduced copy of ``w`` (same dtype and distributions)."""
+    return w.with_(name=w.name + "_small", **kw)
+
+
+def shape_tuple(w: Workload) -> Tuple[int, ...]:
+    return (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups,
+            w.chunk_size)
