@@ -1,0 +1,152 @@
+/*
+ * ssd.h -- C ABI of libssd: the Mamba-2 SSD chunked forward pass on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [P1] "Accelerating Mamba-2 with High-Performance Forward Pass Kernels in
+ *        NVIDIA CUDA Tile" (trishampatil.com)
+ *   [P2] the zhiding.cn rendering of the same write-up, section
+ *        "Mamba-2架构" (where the display formulas survive)
+ *
+ * The method.  Per batch b and head h, with group g = h / (nheads/ngroups):
+ *     S_t = exp(A_h dt_t) S_{t-1} + dt_t x_t B_t^T      (state, headdim x dstate)
+ *     y_t = S_t C_t + D_h x_t
+ * [P1 "The Mamba-2 Recurrence"; P2 "Mamba-2架构"], evaluated chunk by chunk
+ * in three stages [P1 "From the Math to Three Kernels"]:
+ *   1. ssd_chunk_cumsum    g = log2(e) * per-chunk inclusive cumsum of A dt
+ *   2. ssd_fwd_pass_state  per-chunk starting states by the jump
+ *                          S_next = 2^{g_last} S + X^T (dt 2^{g_last-g} B)
+ *   3. ssd_compute_out     Y = 2^{g} (C S^T) + ((C B^T) o 2^{g_i-g_j} o M)(dt X) + D X
+ * and ssd_forward runs the three in order.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers to contiguous row-major arrays in the
+ *   layouts given below, each 16-byte aligned.  The caller owns every buffer;
+ *   the library allocates nothing, keeps no mutable global state and may be
+ *   called concurrently on different streams.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   Every call is stream-ordered and asynchronous: it only enqueues kernels
+ *   and never synchronises the host.
+ * - Every argument is checked on the host BEFORE any HIP call; a failed check
+ *   returns SSD_ERR_INVALID_ARGUMENT or SSD_ERR_UNSUPPORTED and touches
+ *   nothing.  A failed kernel launch returns SSD_ERR_HIP.  Faults during
+ *   execution surface at the caller's next synchronisation.
+ * - Dimensions: batch, seqlen, nheads, headdim (P), dstate (N), ngroups (G),
+ *   chunk_size (T), all >= 1, nheads % ngroups == 0.  seqlen need not be a
+ *   multiple of chunk_size: a ragged last chunk is handled as the recurrence
+ *   defines it.  Supported: P = 64; N in {64, 128}; T in {64, 128, 256};
+ *   x/B/C in fp32 or bf16.  Anything else returns SSD_ERR_UNSUPPORTED.
+ * - nc = ceil(seqlen / chunk_size) is the number of chunks.
+ * - Element types: x, B, C share `in_dtype`; y has `y_dtype`; dt, A, D, g,
+ *   states, final_state and init_state are always fp32.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad dim, misalignment   */
+    SSD_ERR_UNSUPPORTED = 2,      /* valid but not built: (P, N, T, dtype)  */
+    SSD_ERR_WORKSPACE = 3,        /* workspace null or smaller than needed  */
+    SSD_ERR_HIP = 4               /* a HIP launch reported an error         */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Problem shape; field names follow the problem statement of the pages'
+ * benchmark example [P1 "Mamba-2 Forward Pass Benchmarks: cuTile vs Triton
+ * on NVIDIA B300"] (batch size, tokens, groups, heads, state size, head
+ * size, chunk size). */
+typedef struct {
+    int64_t batch;      /* b                                           */
+    int64_t seqlen;     /* L, tokens per sequence                       */
+    int64_t nheads;     /* H                                            */
+    int64_t headdim;    /* P, size of x_t per head                      */
+    int64_t dstate;     /* N, size of B_t and C_t (the state size)      */
+    int64_t ngroups;    /* G, B/C shared by nheads/ngroups heads         */
+    int64_t chunk_size; /* T                                            */
+} ssd_dims;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *ssd_status_string(int status);
+
+/* Bytes of device workspace ssd_forward needs: the stage-1 output g,
+ * 4 * batch * nheads * seqlen.  Returns 0 when dims is NULL or invalid. */
+size_t ssd_forward_workspace_bytes(const ssd_dims *dims);
+
+/*
+ * Stage 1 [P1 "Kernel 1: chunk_cumsum, the Cumulative Decay Sums"]:
+ *   g[b,h,t] = log2(e) * sum_{s = T*floor(t/T)}^{t} A[h] * dt[b,s,h]
+ * the within-chunk inclusive cumsum of a = A dt, scaled so later stages use
+ * exp2.  g is stored head-major so per-head token runs are contiguous, the
+ * layout change the pages list among their optimizations [P1 "Mamba-2
+ * Performance Optimizations in cuTile"; P2 "Mamba-2性能优化"].
+ *   dt [b, L, H] fp32 (read)     A [H] fp32 (read)     g [b, H, L] fp32 (written)
+ * Only batch, seqlen, nheads and chunk_size of `dims` are read.
+ */
+ssd_status ssd_chunk_cumsum(const float *dt, const float *A, float *g,
+                            const ssd_dims *dims, void *stream);
+
+/*
+ * Stage 2 [P1 "Kernel 2: fwd_pass_state, Carrying the State Between Chunks";
+ * P1 "Step 3: Add Back the Decay, Safely, in Log-Space"]: for every (b, h),
+ * S = init_state[b,h] (zeros if init_state is NULL); for each chunk c in
+ * order: states[b,h,c] = S, then
+ *   S = 2^{g_last} S + X_c^T (w o B_c),   w_t = dt_t 2^{g_last - g_t}
+ * with g_last the value of g at the chunk's last token.  final_state = S
+ * after the last chunk.
+ *   x [b, L, H, P] in_dtype      B [b, L, G, N] in_dtype
+ *   dt [b, L, H] fp32            g [b, H, L] fp32 (from ssd_chunk_cumsum)
+ *   init_state [b, H, P, N] fp32 or NULL
+ *   states [b, H, nc, P, N] fp32 (written)   final_state [b, H, P, N] or NULL
+ */
+ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt,
+                              const float *g, const float *init_state,
+                              float *states, float *final_state, int in_dtype,
+                              const ssd_dims *dims, void *stream);
+
+/*
+ * Stage 3 [P1 "Kernel 3: compute_out, the Fused Output Kernel"; P1 "Step 2:
+ * Compute a Chunk of Outputs from One State"]: for every (b, c, h), with S_c
+ * = states[b,h,c], rows i and columns j tokens of chunk c:
+ *   Y = 2^{g_i} (C S_c^T) + L' X + D_h X,
+ *   L'[i,j] = (C B^T)[i,j] 2^{g_i - g_j} dt_j  for i >= j, else 0
+ * The masked entries are selected away, never multiplied by zero, so the
+ * positive exponents above the diagonal cannot turn into NaN [P1 "Step 3"].
+ * The chunk x chunk matrix never reaches memory.
+ *   x, B, C as above; dt, g as above; states [b, H, nc, P, N] fp32 (read)
+ *   D [H] fp32; y [b, L, H, P] in y_dtype (written)
+ */
+ssd_status ssd_compute_out(const void *x, const void *B, const void *C,
+                           const float *dt, const float *g,
+                           const float *states, const float *D, void *y,
+                           int in_dtype, int y_dtype, const ssd_dims *dims,
+                           void *stream);
+
+/*
+ * The whole forward [P1 "From the Math to Three Kernels"]: stage 1 into the
+ * caller's workspace (at least ssd_forward_workspace_bytes(dims) bytes, else
+ * SSD_ERR_WORKSPACE), then stages 2 and 3, all on `stream`.  Returns y, the
+ * per-chunk starting states and (if final_state != NULL) the final state,
+ * which a later call can take back as init_state to continue the sequence.
+ */
+ssd_status ssd_forward(const void *x, const float *dt, const float *A,
+                       const void *B, const void *C, const float *D,
+                       const float *init_state, void *y, float *states,
+                       float *final_state, void *workspace,
+                       size_t workspace_bytes, int in_dtype, int y_dtype,
+                       const ssd_dims *dims, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

@@ -1,0 +1,274 @@
+"""Mamba-2 SSD chunked forward on AMD Instinct MI355X (gfx950).
+
+A thin Python binding over libssd's C ABI (``include/ssd.h``).  Every step of
+the computation runs in the library's HIP kernels; this module only checks
+tensor shapes/dtypes, builds the dims struct and passes device pointers and
+the current HIP stream.  PyTorch supplies device memory and streams.
+
+Entry points (same names as the C ABI):
+  ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_compute_out, ssd_forward
+and the allocating convenience wrapper ``forward``.
+
+Importing fails loudly (ImportError) when libssd.so has not been built:
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ssd.h")
+
+SSD_OK = 0
+SSD_ERR_INVALID_ARGUMENT = 1
+SSD_ERR_UNSUPPORTED = 2
+SSD_ERR_WORKSPACE = 3
+SSD_ERR_HIP = 4
+SSD_F32 = 0
+SSD_BF16 = 1
+
+
+class SsdDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk_size", ctypes.c_int64)]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libssd.so not found at {LIB_PATH}; build it with "
+            "`python -m mamba_ssd_chunked_fwd_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    dims = ctypes.POINTER(SsdDims)
+    lib.ssd_status_string.argtypes = [i]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_forward_workspace_bytes.argtypes = [dims]
+    lib.ssd_forward_workspace_bytes.restype = sz
+    lib.ssd_chunk_cumsum.argtypes = [vp, vp, vp, dims, vp]
+    lib.ssd_chunk_cumsum.restype = i
+    lib.ssd_fwd_pass_state.argtypes = [vp] * 7 + [i, dims, vp]
+    lib.ssd_fwd_pass_state.restype = i
+    lib.ssd_compute_out.argtypes = [vp] * 8 + [i, i, dims, vp]
+    lib.ssd_compute_out.restype = i
+    lib.ssd_forward.argtypes = [vp] * 11 + [sz, i, i, dims, vp]
+    lib.ssd_forward.restype = i
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libssd handle."""
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/ssd.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
+                      r"(ssd_[a-z_]+)\s*\(", text, flags=re.M)
+
+
+def status_string(status: int) -> str:
+    return _lib.ssd_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return SSD_F32
+    if t == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"unsupported dtype {t}; expected float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: Optional[torch.Tensor], name: str, shape, dtypes,
+           device=None, optional=False) -> None:
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected "
+                         f"{tuple(shape)}")
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_dims(x: torch.Tensor, B: torch.Tensor, chunk_size: int) -> SsdDims:
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim] and B "
+                         "[batch, seqlen, ngroups, dstate]")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return SsdDims(b, L, H, P, N, G, int(chunk_size))
+
+
+def nchunks(d: SsdDims) -> int:
+    return -(-d.seqlen // d.chunk_size)
+
+
+def workspace_bytes(d: SsdDims) -> int:
+    return int(_lib.ssd_forward_workspace_bytes(ctypes.byref(d)))
+
+
+def _raise(st: int, where: str) -> None:
+    if st != SSD_OK:
+        raise SsdError(st, where)
+
+
+# ------------------------------------------------------------- C-ABI entries
+def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, g: torch.Tensor,
+                     chunk_size: int) -> None:
+    """Stage 1: g [b, H, L] = log2(e) * per-chunk inclusive cumsum of A dt."""
+    if dt.dim() != 3:
+        raise ValueError("dt must be [batch, seqlen, nheads]")
+    b, L, H = dt.shape
+    f32 = (torch.float32,)
+    _check(dt, "dt", None, f32)
+    _check(A, "A", (H,), f32, dt.device)
+    _check(g, "g", (b, H, L), f32, dt.device)
+    # stage 1 reads only batch, seqlen, nheads and chunk_size
+    d = SsdDims(b, L, H, 64, 64, 1, int(chunk_size))
+    _raise(_lib.ssd_chunk_cumsum(_ptr(dt), _ptr(A), _ptr(g), ctypes.byref(d),
+                                 _stream(dt.device)), "ssd_chunk_cumsum")
+
+
+def ssd_fwd_pass_state(x: torch.Tensor, B: torch.Tensor, dt: torch.Tensor,
+                       g: torch.Tensor, init_state: Optional[torch.Tensor],
+                       states: torch.Tensor,
+                       final_state: Optional[torch.Tensor],
+                       chunk_size: int) -> None:
+    """Stage 2: per-chunk starting states [b, H, nc, P, N] and the final state."""
+    d = make_dims(x, B, chunk_size)
+    dev = x.device
+    ins = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _check(x, "x", None, ins)
+    _check(B, "B", (d.batch, d.seqlen, d.ngroups, d.dstate), (x.dtype,), dev)
+    _check(dt, "dt", (d.batch, d.seqlen, d.nheads), f32, dev)
+    _check(g, "g", (d.batch, d.nheads, d.seqlen), f32, dev)
+    st_shape = (d.batch, d.nheads, d.headdim, d.dstate)
+    _check(init_state, "init_state", st_shape, f32, dev, optional=True)
+    _check(states, "states", (d.batch, d.nheads, nchunks(d), d.headdim,
+                              d.dstate), f32, dev)
+    _check(final_state, "final_state", st_shape, f32, dev, optional=True)
+    _raise(_lib.ssd_fwd_pass_state(
+        _ptr(x), _ptr(B), _ptr(dt), _ptr(g), _ptr(init_state), _ptr(states),
+        _ptr(final_state), _dtype_code(x.dtype), ctypes.byref(d),
+        _stream(dev)), "ssd_fwd_pass_state")
+
+
+def ssd_compute_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                    dt: torch.Tensor, g: torch.Tensor, states: torch.Tensor,
+                    D: torch.Tensor, y: torch.Tensor, chunk_size: int) -> None:
+    """Stage 3: y [b, L, H, P] from the per-chunk starting states."""
+    d = make_dims(x, B, chunk_size)
+    dev = x.device
+    ins = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _check(x, "x", None, ins)
+    bc = (d.batch, d.seqlen, d.ngroups, d.dstate)
+    _check(B, "B", bc, (x.dtype,), dev)
+    _check(C, "C", bc, (x.dtype,), dev)
+    _check(dt, "dt", (d.batch, d.seqlen, d.nheads), f32, dev)
+    _check(g, "g", (d.batch, d.nheads, d.seqlen), f32, dev)
+    _check(states, "states", (d.batch, d.nheads, nchunks(d), d.headdim,
+                              d.dstate), f32, dev)
+    _check(D, "D", (d.nheads,), f32, dev)
+    _check(y, "y", tuple(x.shape), ins, dev)
+    _raise(_lib.ssd_compute_out(
+        _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(g), _ptr(states), _ptr(D),
+        _ptr(y), _dtype_code(x.dtype), _dtype_code(y.dtype), ctypes.byref(d),
+        _stream(dev)), "ssd_compute_out")
+
+
+def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+                B: torch.Tensor, C: torch.Tensor, D: torch.Tensor,
+                init_state: Optional[torch.Tensor], y: torch.Tensor,
+                states: torch.Tensor, final_state: Optional[torch.Tensor],
+                workspace: torch.Tensor, chunk_size: int) -> None:
+    """All three stages on the current stream; g lives in ``workspace``."""
+    d = make_dims(x, B, chunk_size)
+    dev = x.device
+    ins = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _check(x, "x", None, ins)
+    bc = (d.batch, d.seqlen, d.ngroups, d.dstate)
+    _check(B, "B", bc, (x.dtype,), dev)
+    _check(C, "C", bc, (x.dtype,), dev)
+    _check(dt, "dt", (d.batch, d.seqlen, d.nheads), f32, dev)
+    _check(A, "A", (d.nheads,), f32, dev)
+    _check(D, "D", (d.nheads,), f32, dev)
+    st_shape = (d.batch, d.nheads, d.headdim, d.dstate)
+    _check(init_state, "init_state", st_shape, f32, dev, optional=True)
+    _check(y, "y", tuple(x.shape), ins, dev)
+    _check(states, "states", (d.batch, d.nheads, nchunks(d), d.headdim,
+                              d.dstate), f32, dev)
+    _check(final_state, "final_state", st_shape, f32, dev, optional=True)
+    _check(workspace, "workspace", None, (torch.uint8, torch.float32), dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    _raise(_lib.ssd_forward(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(init_state), _ptr(y), _ptr(states), _ptr(final_state),
+        _ptr(workspace), nbytes, _dtype_code(x.dtype), _dtype_code(y.dtype),
+        ctypes.byref(d), _stream(dev)), "ssd_forward")
+
+
+# ------------------------------------------------------------ convenience
+def forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+            B: torch.Tensor, C: torch.Tensor, D: torch.Tensor,
+            init_state: Optional[torch.Tensor] = None, chunk_size: int = 64,
+            y_dtype: torch.dtype = torch.float32
+            ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Allocate outputs with torch.empty and run ``ssd_forward``.
+
+    Returns (y [b, L, H, P] in y_dtype, states [b, H, nc, P, N] fp32,
+    final_state [b, H, P, N] fp32).
+    """
+    d = make_dims(x, B, chunk_size)
+    dev = x.device
+    y = torch.empty(tuple(x.shape), dtype=y_dtype, device=dev)
+    states = torch.empty((d.batch, d.nheads, nchunks(d), d.headdim, d.dstate),
+                         dtype=torch.float32, device=dev)
+    final = torch.empty((d.batch, d.nheads, d.headdim, d.dstate),
+                        dtype=torch.float32, device=dev)
+    # invalid or unsupported dims report 0 bytes; ssd_forward then returns the
+    # precise status before touching the (minimal) workspace
+    nbytes = max(workspace_bytes(d), 16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ssd_forward(x, dt, A, B, C, D, init_state, y, states, final, ws,
+                chunk_size)
+    return y, states, final

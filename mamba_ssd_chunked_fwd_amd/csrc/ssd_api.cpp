@@ -1,0 +1,148 @@
+// ssd_api.cpp -- the C ABI of libssd (declared in include/ssd.h).
+//
+// Every entry point validates its arguments on the host before any HIP call,
+// then enqueues the stage kernels on the caller's stream.  No allocation, no
+// host synchronisation, no global mutable state.
+#include <climits>
+#include <cstdint>
+
+#include "ssd.h"
+#include "ssd_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Required pointer: non-null and 16-byte aligned.
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+// Optional pointer: null, or 16-byte aligned.
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+ssd_status check_dims(const ssd_dims* d, ssd::Shape* out) {
+  if (d == nullptr) return SSD_ERR_INVALID_ARGUMENT;
+  const int64_t v[7] = {d->batch, d->seqlen, d->nheads, d->headdim,
+                        d->dstate, d->ngroups, d->chunk_size};
+  for (int64_t e : v)
+    if (e < 1 || e > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  if (d->nheads % d->ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
+  // Index arithmetic inside the kernels uses 32-bit block ids and token
+  // counts; keep every launch and every (batch * seqlen) within range.
+  const int64_t nc = (d->seqlen + d->chunk_size - 1) / d->chunk_size;
+  if (d->batch * d->seqlen > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  const int64_t per_head_blocks = nc * 4 > 8 ? nc * 4 : 8;
+  if (d->batch * d->nheads * per_head_blocks > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  if (d->headdim != 64) return SSD_ERR_UNSUPPORTED;
+  if (d->dstate != 64 && d->dstate != 128) return SSD_ERR_UNSUPPORTED;
+  if (d->chunk_size != 64 && d->chunk_size != 128 && d->chunk_size != 256)
+    return SSD_ERR_UNSUPPORTED;
+  if (out) {
+    *out = ssd::Shape{d->batch, d->seqlen, d->nheads, d->headdim,
+                      d->dstate, d->ngroups, d->chunk_size};
+  }
+  return SSD_OK;
+}
+
+bool ok_dtype(int t) { return t == SSD_F32 || t == SSD_BF16; }
+
+ssd_status from_hip(int err) { return err == 0 ? SSD_OK : SSD_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_string(int status) {
+  switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_INVALID_ARGUMENT: return "SSD_ERR_INVALID_ARGUMENT";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP";
+    default: return "SSD_ERR_UNKNOWN";
+  }
+}
+
+size_t ssd_forward_workspace_bytes(const ssd_dims* dims) {
+  if (check_dims(dims, nullptr) != SSD_OK) return 0;
+  return sizeof(float) * (size_t)dims->batch * (size_t)dims->nheads *
+         (size_t)dims->seqlen;
+}
+
+ssd_status ssd_chunk_cumsum(const float* dt, const float* A, float* g,
+                            const ssd_dims* dims, void* stream) {
+  if (dims == nullptr) return SSD_ERR_INVALID_ARGUMENT;
+  // Stage 1 reads only batch, seqlen, nheads and chunk_size; check those with
+  // a shape whose other fields are fixed to a supported value.
+  ssd_dims d1 = *dims;
+  d1.headdim = 64;
+  d1.dstate = 64;
+  d1.ngroups = 1;
+  ssd::Shape s;
+  const ssd_status st = check_dims(&d1, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(g)) return SSD_ERR_INVALID_ARGUMENT;
+  return from_hip(ssd::launch_chunk_cumsum(dt, A, g, s, stream));
+}
+
+ssd_status ssd_fwd_pass_state(const void* x, const void* B, const float* dt,
+                              const float* g, const float* init_state,
+                              float* states, float* final_state, int in_dtype,
+                              const ssd_dims* dims, void* stream) {
+  ssd::Shape s;
+  const ssd_status st = check_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(dt) || !ok_ptr(g) || !ok_ptr(states) ||
+      !ok_opt(init_state) || !ok_opt(final_state))
+    return SSD_ERR_INVALID_ARGUMENT;
+  return from_hip(ssd::launch_fwd_pass_state(x, B, dt, g, init_state, states,
+                                             final_state, in_dtype == SSD_BF16,
+                                             s, stream));
+}
+
+ssd_status ssd_compute_out(const void* x, const void* B, const void* C,
+                           const float* dt, const float* g,
+                           const float* states, const float* D, void* y,
+                           int in_dtype, int y_dtype, const ssd_dims* dims,
+                           void* stream) {
+  ssd::Shape s;
+  const ssd_status st = check_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype) || !ok_dtype(y_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt) || !ok_ptr(g) ||
+      !ok_ptr(states) || !ok_ptr(D) || !ok_ptr(y))
+    return SSD_ERR_INVALID_ARGUMENT;
+  return from_hip(ssd::launch_compute_out(x, B, C, dt, g, states, D, y,
+                                          in_dtype == SSD_BF16,
+                                          y_dtype == SSD_BF16, s, stream));
+}
+
+ssd_status ssd_forward(const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D,
+                       const float* init_state, void* y, float* states,
+                       float* final_state, void* workspace,
+                       size_t workspace_bytes, int in_dtype, int y_dtype,
+                       const ssd_dims* dims, void* stream) {
+  ssd::Shape s;
+  const ssd_status st = check_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype) || !ok_dtype(y_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(x) || !ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(B) || !ok_ptr(C) ||
+      !ok_ptr(D) || !ok_ptr(y) || !ok_ptr(states) || !ok_opt(init_state) ||
+      !ok_opt(final_state))
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < ssd_forward_workspace_bytes(dims))
+    return SSD_ERR_WORKSPACE;
+  float* g = static_cast<float*>(workspace);
+  const bool bf16 = in_dtype == SSD_BF16;
+  int err = ssd::launch_chunk_cumsum(dt, A, g, s, stream);
+  if (err == 0)
+    err = ssd::launch_fwd_pass_state(x, B, dt, g, init_state, states,
+                                     final_state, bf16, s, stream);
+  if (err == 0)
+    err = ssd::launch_compute_out(x, B, C, dt, g, states, D, y, bf16,
+                                  y_dtype == SSD_BF16, s, stream);
+  return from_hip(err);
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// ssd_device.h -- device-side building blocks shared by the three stage
+// kernels of libssd (gfx950 / CDNA4 only).
+//
+// Matrix-core conventions used throughout (64-lane wavefront, lane l):
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     A: lane l holds row (l % 16), eight k values (bf16x8)
+//     B: lane l holds column (l % 16), eight k values
+//     D: lane l holds column (l % 16), rows 4*(l/16) + r, r = 0..3
+//   v_mfma_f32_16x16x4_f32    D[16x16] += A[16x4] * B[4x16]
+//     A: lane l holds row (l % 16), one k value; B: column (l % 16), one k
+//     D: as above
+// The hardware pairs the k slots of A and B identically, so which token or
+// state index a slot carries is our choice as long as both operands agree;
+// every kernel documents the k <-> index map it uses.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 64;  // P: the only head size built
+// log2(e): exp(v) = exp2(v * log2(e)).
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Hardware base-2 exponential (v_exp_f32).  Large negative arguments
+// underflow to 0, which the method tolerates: those are decays below 2^-126.
+__device__ __forceinline__ float exp2_hw(float v) {
+  return __builtin_amdgcn_exp2f(v);
+}
+
+// Round two floats to bf16 (nearest-even) and pack: `a` in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t w) {
+  return __uint_as_float(w & 0xFFFF0000u);
+}
+
+// Two-term bf16 split of fp32 values: v ~= hi + lo with |v - hi - lo| about
+// 2^-17 |v|.  A product with an exact bf16 operand then costs two bf16 matrix
+// instructions and keeps ~16 mantissa bits, which the fp32 accumulate keeps.
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi,
+                                           uint32_t& lo) {
+  hi = pack_bf16(a, b);
+  lo = pack_bf16(a - bf16_lo(hi), b - bf16_hi(hi));
+}
+
+__device__ __forceinline__ u32x4 make_u32x4(const uint32_t (&a)[4]) {
+  return (u32x4){a[0], a[1], a[2], a[3]};
+}
+
+// Low / high bf16 halves of two words, packed: (lo16(a), lo16(b)) and
+// (hi16(a), hi16(b)).  Used to transpose 2x2 blocks of bf16.
+__device__ __forceinline__ uint32_t lo_halves(uint32_t a, uint32_t b) {
+  return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+}  // namespace ssd

@@ -1,0 +1,29 @@
+// ssd_launch.h -- host-side launchers of the three stage kernels (internal to
+// libssd).  Arguments arrive already validated by the C ABI layer; each
+// launcher returns the hipError_t of its launch as an int (0 = success).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct Shape {
+  int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+  int64_t nchunks() const { return (seqlen + chunk - 1) / chunk; }
+};
+
+int launch_chunk_cumsum(const float* dt, const float* A, float* g,
+                        const Shape& s, void* stream);
+
+int launch_fwd_pass_state(const void* x, const void* B, const float* dt,
+                          const float* g, const float* init_state,
+                          float* states, float* final_state, bool bf16_in,
+                          const Shape& s, void* stream);
+
+int launch_compute_out(const void* x, const void* B, const void* C,
+                       const float* dt, const float* g, const float* states,
+                       const float* D, void* y, bool bf16_in, bool bf16_out,
+                       const Shape& s, void* stream);
+
+}  // namespace ssd

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+Every call below fails argument validation, which the library performs on the
+host before any HIP call, so nothing is launched and no pointer is touched.
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+import mamba_ssd_chunked_fwd_amd as ssd
+from mamba_ssd_chunked_fwd_amd import SsdDims
+
+OK, INV, UNS, WS = (ssd.SSD_OK, ssd.SSD_ERR_INVALID_ARGUMENT,
+                    ssd.SSD_ERR_UNSUPPORTED, ssd.SSD_ERR_WORKSPACE)
+lib = ssd.library()
+FAKE = ctypes.c_void_p(0x7F0000000000)       # 16-byte aligned, never used
+MISALIGNED = ctypes.c_void_p(0x7F0000000004)
+
+
+def dims(**kw):
+    base = dict(batch=2, seqlen=256, nheads=4, headdim=64, dstate=128,
+                ngroups=2, chunk_size=64)
+    base.update(kw)
+    return SsdDims(**base)
+
+
+def test_every_declared_function_is_exported():
+    names = ssd.header_functions()
+    assert set(names) == {"ssd_status_string", "ssd_forward_workspace_bytes",
+                          "ssd_chunk_cumsum", "ssd_fwd_pass_state",
+                          "ssd_compute_out", "ssd_forward"}
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings():
+    assert ssd.status_string(OK) == "SSD_OK"
+    assert ssd.status_string(INV) == "SSD_ERR_INVALID_ARGUMENT"
+    assert ssd.status_string(UNS) == "SSD_ERR_UNSUPPORTED"
+    assert ssd.status_string(WS) == "SSD_ERR_WORKSPACE"
+    assert ssd.status_string(ssd.SSD_ERR_HIP) == "SSD_ERR_HIP"
+    assert ssd.status_string(99) == "SSD_ERR_UNKNOWN"
+
+
+def test_workspace_bytes():
+    d = dims()
+    assert ssd.workspace_bytes(d) == 4 * 2 * 4 * 256
+    assert ssd.workspace_bytes(dims(seqlen=1000, chunk_size=256)) == 4 * 2 * 4 * 1000
+    assert ssd.workspace_bytes(dims(headdim=32)) == 0
+    assert ssd.workspace_bytes(dims(nheads=5)) == 0
+    assert lib.ssd_forward_workspace_bytes(None) == 0
+
+
+def _fwd(d, **over):
+    need = ssd.workspace_bytes(d) if d is not None else 0
+    args = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=FAKE, init=None,
+                y=FAKE, states=FAKE, final=None, ws=FAKE,
+                wsb=need if need else 1 << 20,
+                ind=ssd.SSD_BF16, yd=ssd.SSD_F32)
+    args.update(over)
+    return lib.ssd_forward(args["x"], args["dt"], args["A"], args["B"],
+                           args["C"], args["D"], args["init"], args["y"],
+                           args["states"], args["final"], args["ws"],
+                           args["wsb"], args["ind"], args["yd"],
+                           ctypes.byref(d) if d is not None else None, None)
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("batch", 0, INV), ("seqlen", 0, INV), ("nheads", -1, INV),
+    ("ngroups", 3, INV),                     # 4 % 3 != 0
+    ("headdim", 32, UNS), ("headdim", 128, UNS),
+    ("dstate", 256, UNS), ("dstate", 16, UNS),
+    ("chunk_size", 32, UNS), ("chunk_size", 100, UNS),
+    ("seqlen", 1 << 40, INV),
+])
+def test_forward_rejects_bad_dims(field, value, expect):
+    assert _fwd(dims(**{field: value})) == expect
+
+
+def test_forward_rejects_null_and_misaligned_pointers():
+    d = dims()
+    assert _fwd(None) == INV
+    for name in ("x", "dt", "A", "B", "C", "D", "y", "states"):
+        assert _fwd(d, **{name: None}) == INV, name
+        assert _fwd(d, **{name: MISALIGNED}) == INV, name
+    assert _fwd(d, init=MISALIGNED) == INV
+    assert _fwd(d, final=MISALIGNED) == INV
+    assert _fwd(d, ind=2) == INV
+    assert _fwd(d, yd=-1) == INV
+
+
+def test_forward_rejects_small_workspace():
+    d = dims()
+    need = ssd.workspace_bytes(d)
+    assert _fwd(d, wsb=need - 1) == WS
+    assert _fwd(d, ws=None) == WS
+    assert _fwd(d, ws=MISALIGNED) == WS
+
+
+def test_stage_entry_points_validate():
+    d = dims()
+    assert lib.ssd_chunk_cumsum(None, FAKE, FAKE, ctypes.byref(d), None) == INV
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, FAKE, None, None) == INV
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, FAKE,
+                                ctypes.byref(dims(chunk_size=48)), None) == UNS
+    # stage 1 ignores P, N and G
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, MISALIGNED,
+                                ctypes.byref(dims(headdim=7)), None) == INV
+    assert lib.ssd_fwd_pass_state(FAKE, FAKE, FAKE, FAKE, None, None, None,
+                                  ssd.SSD_BF16, ctypes.byref(d), None) == INV
+    assert lib.ssd_fwd_pass_state(FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 5,
+                                  ctypes.byref(d), None) == INV
+    assert lib.ssd_fwd_pass_state(FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                  ssd.SSD_F32, ctypes.byref(dims(dstate=96)),
+                                  None) == UNS
+    assert lib.ssd_compute_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               ssd.SSD_BF16, ssd.SSD_F32, ctypes.byref(d),
+                               None) == INV
+    assert lib.ssd_compute_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               ssd.SSD_BF16, 3, ctypes.byref(d), None) == INV
+    assert lib.ssd_compute_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               ssd.SSD_BF16, ssd.SSD_F32,
+                               ctypes.byref(dims(nheads=6, ngroups=4)), None) == INV
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 64, 2, 64)
+    B = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError):
+        ssd.forward(x, torch.zeros(1, 64, 2), torch.zeros(2), B, B,
+                    torch.zeros(2), chunk_size=64)

@@ -1,0 +1,309 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small cases compare every output element; they span several tiles, a ragged
+last chunk, grouped B/C and both input types.  The named workloads run at
+full size, in the same launch configuration the benchmark times, and compare
+sampled (batch, head) pairs that the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (assert_close, device_inputs, g_tolerance, log)
+from ssd_workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ssd():
+    import mamba_ssd_chunked_fwd_amd as m
+    return m
+
+
+def _wl(name, dtype, b, L, H, G, N, T, init, dt_shift=-2.0, a=(0.0, 1.5)):
+    return Workload(name, b, L, H, 64, N, G, T, dtype, dt_shift, a[0], a[1],
+                    0.1 if init else None)
+
+
+SMALL = [
+    _wl("bf16_T64_N128_ragged_grouped", "bf16", 2, 300, 4, 2, 128, 64, True),
+    _wl("bf16_T256_N64_ragged", "bf16", 1, 700, 3, 1, 64, 256, False),
+    _wl("bf16_T128_N128_init", "bf16", 2, 333, 2, 1, 128, 128, True),
+    _wl("bf16_T256_N128_two_chunks", "bf16", 1, 512, 2, 1, 128, 256, True),
+    _wl("fp32_T64_N64_grouped", "fp32", 2, 200, 6, 3, 64, 64, True, -1.0, (-1.0, 2.0)),
+    _wl("fp32_T128_N128", "fp32", 1, 520, 2, 2, 128, 128, False),
+    _wl("fp32_T256_N128_ragged", "fp32", 1, 600, 2, 1, 128, 256, True),
+    _wl("fp32_T64_N128_wide_batch", "fp32", 5, 130, 3, 1, 128, 64, False),
+    _wl("bf16_T64_N64_shorter_than_chunk", "bf16", 3, 37, 2, 1, 64, 64, False),
+    _wl("bf16_T128_N128_single_token", "bf16", 1, 1, 1, 1, 128, 128, True),
+    _wl("fp32_T256_N64_single_token", "fp32", 2, 1, 2, 2, 64, 256, True),
+]
+
+
+def _run_forward(ssd, dev, T, y_dtype=torch.float32):
+    y, states, final = ssd.forward(dev["x"], dev["dt"], dev["A"], dev["B"],
+                                   dev["C"], dev["D"], dev["init_state"],
+                                   chunk_size=T, y_dtype=y_dtype)
+    torch.cuda.synchronize()
+    return y, states, final
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_end_to_end(ssd, w):
+    log(f"[parity] {w.name}: b={w.batch} L={w.seqlen} H={w.nheads} "
+        f"G={w.ngroups} N={w.dstate} T={w.chunk_size} {w.dtype}")
+    inp = make_inputs(w, seed=11)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=w.chunk_size)
+    dev = device_inputs(inp, w.dtype)
+    y, states, final = _run_forward(ssd, dev, w.chunk_size)
+    assert_close(_np(states), ref["states"], w.dtype, "states")
+    assert_close(_np(final), ref["final"], w.dtype, "final")
+    assert_close(_np(y), ref["y"], w.dtype, "y")
+
+
+@pytest.mark.parametrize("w", SMALL[:8], ids=lambda w: w.name)
+def test_small_stages(ssd, w):
+    log(f"[stages] {w.name}")
+    T = w.chunk_size
+    inp = make_inputs(w, seed=12)
+    dev = device_inputs(inp, w.dtype)
+    b, L, H = w.batch, w.seqlen, w.nheads
+    nc = w.nchunks
+    # stage 1 against the oracle's cumsum, within the fp32 rounding bound
+    g = torch.empty(b, H, L, device=DEV)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, T)
+    torch.cuda.synchronize()
+    g_ref = oracle.chunk_cumsum(inp["dt"], inp["A"], T)
+    err = np.abs(_np(g) - g_ref)
+    assert np.all(err <= g_tolerance(g_ref, T)), float(err.max())
+    # stage 2 (fed the GPU g) against the recurrence's chunk states
+    states = torch.empty(b, H, nc, 64, w.dstate, device=DEV)
+    final = torch.empty(b, H, 64, w.dstate, device=DEV)
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dev["dt"], g, dev["init_state"],
+                           states, final, T)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=T)
+    assert_close(_np(states), ref["states"], w.dtype, "stage-2 states")
+    assert_close(_np(final), ref["final"], w.dtype, "stage-2 final")
+    # stage 3 fed the oracle's states (rounded to fp32), against the oracle's
+    # chunk outputs from those same fp32 states
+    st32 = ref["states"].astype(np.float32)
+    y = torch.empty(tuple(dev["x"].shape), dtype=torch.float32, device=DEV)
+    ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dev["dt"], g,
+                        torch.from_numpy(st32).to(DEV), dev["D"], y, T)
+    torch.cuda.synchronize()
+    y_ref = oracle.chunk_out(inp["x"], inp["dt"], inp["A"], inp["B"],
+                             inp["C"], inp["D"], st32, chunk_size=T)
+    assert_close(_np(y), y_ref, w.dtype, "stage-3 y")
+
+
+def test_cumsum_exact_inputs(ssd):
+    # A = -1 and dt powers of two: products and partial sums are exact in
+    # fp32, so g differs from the oracle only by the final log2(e) scaling.
+    b, L, H, T = 2, 300, 5, 64
+    rng = np.random.default_rng(3)
+    dt = (2.0 ** rng.integers(-6, 2, size=(b, L, H))).astype(np.float32)
+    A = -np.ones(H, np.float32)
+    g = torch.empty(b, H, L, device=DEV)
+    ssd.ssd_chunk_cumsum(torch.from_numpy(dt).to(DEV), torch.from_numpy(A).to(DEV), g, T)
+    torch.cuda.synchronize()
+    g_ref = oracle.chunk_cumsum(dt, A, T)
+    err = np.abs(_np(g) - g_ref)
+    assert np.all(err <= 2.0 ** -22 * np.abs(g_ref)), float((err / np.abs(g_ref)).max())
+
+
+# ------------------------------------------------------ named full workloads
+NAMED = ["tiny_fp32", "small_bf16", "large_bf16", "wide_fp32", "long_bf16"]
+
+
+def _sample_pairs(w, k, seed):
+    n = w.batch * w.nheads
+    rng = np.random.default_rng(seed)
+    picks = {0, n - 1} | set(int(v) for v in rng.integers(0, n, size=k))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_named_workload_full_size(ssd, name):
+    w = WORKLOADS[name]
+    log(f"[full] {name}: b={w.batch} L={w.seqlen} H={w.nheads} N={w.dstate} "
+        f"G={w.ngroups} T={w.chunk_size} {w.dtype}")
+    inp = make_inputs(w)
+    dev = device_inputs(inp, w.dtype)
+    y, states, final = _run_forward(ssd, dev, w.chunk_size)
+    if name == "tiny_fp32":
+        ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"],
+                             inp["C"], inp["D"], inp["init_state"],
+                             chunk_size=w.chunk_size)
+        assert_close(_np(y), ref["y"], w.dtype, "y")
+        assert_close(_np(states), ref["states"], w.dtype, "states")
+        assert_close(_np(final), ref["final"], w.dtype, "final")
+        return
+    pairs = _sample_pairs(w, 3, seed=len(name))
+    log(f"  sampled (b*H + h) pairs: {pairs}")
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=w.chunk_size,
+                         pairs=pairs)
+    H = w.nheads
+    ys = np.stack([_np(y[p // H, :, p % H]) for p in pairs])
+    ss = np.stack([_np(states[p // H, p % H]) for p in pairs])
+    fs = np.stack([_np(final[p // H, p % H]) for p in pairs])
+    assert_close(ss, ref["states"], w.dtype, "states (sampled pairs)")
+    assert_close(fs, ref["final"], w.dtype, "final (sampled pairs)")
+    assert_close(ys, ref["y"], w.dtype, "y (sampled pairs)")
+    # properties that hold over every element
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(states).all())
+    if inp["init_state"] is None:
+        assert bool((states[:, :, 0] == 0).all())
+    else:
+        assert torch.equal(states[:, :, 0], dev["init_state"])
+
+
+def test_long_sequence_split_in_halves_is_bitwise_equal(ssd):
+    w = WORKLOADS["long_bf16"]
+    log(f"[split] {w.name}: whole vs two halves of {w.seqlen // 2}")
+    inp = make_inputs(w)
+    dev = device_inputs(inp, w.dtype)
+    T = w.chunk_size
+    y, states, final = _run_forward(ssd, dev, T)
+    half = w.seqlen // 2
+    first = {k: (v[:, :half].contiguous() if k in ("x", "B", "C", "dt") else v)
+             for k, v in dev.items()}
+    y1, s1, f1 = _run_forward(ssd, first, T)
+    second = {k: (v[:, half:].contiguous() if k in ("x", "B", "C", "dt") else v)
+              for k, v in dev.items()}
+    second["init_state"] = f1
+    y2, s2, f2 = _run_forward(ssd, second, T)
+    assert torch.equal(f2, final)
+    assert torch.equal(torch.cat([s1, s2], 2), states)
+    assert torch.equal(torch.cat([y1, y2], 1), y)
+
+
+# ----------------------------------------------------------- special cases
+def _small_inputs(seed=21, dtype="bf16", b=2, L=200, H=4, G=2, N=128, T=64,
+                  init=True):
+    w = _wl("special", dtype, b, L, H, G, N, T, init)
+    return w, make_inputs(w, seed=seed)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_zero_dt_passes_state_through_exactly(ssd, dtype):
+    w, inp = _small_inputs(dtype=dtype)
+    inp["dt"] = np.zeros_like(inp["dt"])
+    dev = device_inputs(inp, dtype)
+    y, states, final = _run_forward(ssd, dev, w.chunk_size)
+    init = dev["init_state"]
+    for c in range(w.nchunks):
+        assert torch.equal(states[:, :, c], init)
+    assert torch.equal(final, init)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=w.chunk_size)
+    assert_close(_np(y), ref["y"], dtype, "y = C h0 + D x")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_no_decay_matches_oracle(ssd, dtype):
+    w, inp = _small_inputs(dtype=dtype, seed=22)
+    inp["A"] = np.zeros_like(inp["A"])
+    dev = device_inputs(inp, dtype)
+    y, states, final = _run_forward(ssd, dev, w.chunk_size)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=w.chunk_size)
+    assert_close(_np(y), ref["y"], dtype, "y")
+    assert_close(_np(final), ref["final"], dtype, "final")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_extreme_decay_is_finite_and_matches(ssd, dtype):
+    w, inp = _small_inputs(dtype=dtype, seed=23, T=256, L=600)
+    inp["A"] = (inp["A"] * 1e4).astype(np.float32)     # a_t << -100
+    dev = device_inputs(inp, dtype)
+    y, states, final = _run_forward(ssd, dev, w.chunk_size)
+    assert bool(torch.isfinite(y).all())
+    assert bool(torch.isfinite(states).all()) and bool(torch.isfinite(final).all())
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=w.chunk_size)
+    assert_close(_np(y), ref["y"], dtype, "y")
+    assert_close(_np(final), ref["final"], dtype, "final")
+
+
+def test_zero_inputs_give_zero_outputs(ssd):
+    w, inp = _small_inputs(seed=24, init=False)
+    inp["x"] = np.zeros_like(inp["x"])
+    dev = device_inputs(inp, "bf16")
+    y, states, final = _run_forward(ssd, dev, w.chunk_size)
+    assert bool((y == 0).all()) and bool((states == 0).all())
+    assert bool((final == 0).all())
+
+
+def test_deterministic_and_fully_written(ssd):
+    w, inp = _small_inputs(seed=25, L=333)
+    dev = device_inputs(inp, "bf16")
+    d = ssd.make_dims(dev["x"], dev["B"], w.chunk_size)
+    outs = []
+    for _ in range(2):
+        y = torch.full(tuple(dev["x"].shape), float("nan"), device=DEV)
+        st = torch.full((w.batch, w.nheads, w.nchunks, 64, w.dstate),
+                        float("nan"), device=DEV)
+        fin = torch.full((w.batch, w.nheads, 64, w.dstate), float("nan"), device=DEV)
+        ws = torch.full((ssd.workspace_bytes(d) // 4,), float("nan"), device=DEV)
+        ssd.ssd_forward(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"],
+                        dev["D"], dev["init_state"], y, st, fin, ws, w.chunk_size)
+        torch.cuda.synchronize()
+        assert not bool(torch.isnan(y).any())
+        assert not bool(torch.isnan(st).any()) and not bool(torch.isnan(fin).any())
+        outs.append((y, st, fin))
+    for a, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a, b_)
+
+
+def test_forward_equals_stage_calls(ssd):
+    w, inp = _small_inputs(seed=26, L=257, T=128)
+    dev = device_inputs(inp, "bf16")
+    T = w.chunk_size
+    y, states, final = _run_forward(ssd, dev, T)
+    b, L, H = w.batch, w.seqlen, w.nheads
+    g = torch.empty(b, H, L, device=DEV)
+    s2 = torch.empty_like(states)
+    f2 = torch.empty_like(final)
+    y2 = torch.empty_like(y)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, T)
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dev["dt"], g, dev["init_state"], s2, f2, T)
+    ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dev["dt"], g, s2, dev["D"], y2, T)
+    torch.cuda.synchronize()
+    assert torch.equal(s2, states) and torch.equal(f2, final) and torch.equal(y2, y)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bf16_output(ssd, dtype):
+    w, inp = _small_inputs(seed=27, dtype=dtype)
+    dev = device_inputs(inp, dtype)
+    y, _, _ = _run_forward(ssd, dev, w.chunk_size, y_dtype=torch.bfloat16)
+    assert y.dtype == torch.bfloat16
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=w.chunk_size)
+    assert_close(_np(y), ref["y"], dtype, "bf16 y", y_bf16=True)
+
+
+def test_binding_rejects_bad_arguments(ssd):
+    w, inp = _small_inputs(seed=28)
+    dev = device_inputs(inp, "bf16")
+    with pytest.raises(ValueError):     # wrong dt shape
+        ssd.forward(dev["x"], dev["dt"][:, :-1].contiguous(), dev["A"], dev["B"],
+                    dev["C"], dev["D"], chunk_size=64)
+    with pytest.raises(TypeError):      # B dtype differs from x
+        ssd.forward(dev["x"], dev["dt"], dev["A"], dev["B"].float(), dev["C"],
+                    dev["D"], chunk_size=64)
+    with pytest.raises(ssd.SsdError) as e:   # chunk size not built
+        ssd.forward(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"],
+                    dev["D"], chunk_size=32)
+    assert e.value.status == ssd.SSD_ERR_UNSUPPORTED
