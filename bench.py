@@ -1,0 +1,262 @@
+"""Benchmark of the Mamba-2 SSD chunked forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path -- stage 1 (chunk cumsum), stage 2
+(state pass), stage 3 (fused output) -- over one batch of synthetic input of
+the named workload (default: the small-model bf16 layer, batch 4 x 2048
+tokens, 24 heads of 64, state 128, chunk 64).  The step calls the three C-ABI
+stage entry points in order, which is exactly what ssd_forward launches, with
+HIP events between them on the launch stream so every stage's duration is
+measured inside the timed region.
+
+Inputs are resident in HBM before timing.  Steps rotate over several
+independent input/output sets whose total footprint is >= 1 GiB, so no step
+finds its operands in the 256 MB last-level cache from the previous step.
+
+Prints ONE JSON line: tokens/s (whole job), the roofline of the dominant
+kernel from algorithmic bytes and its event-measured duration, and the fp64
+CPU oracle timed on this host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD forward tokens/sec + % of HBM/MFMA roofline, 1×MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_TFLOPS = 2500.0      # dense
+FP32_MFMA_TFLOPS = 157.3
+STAGE_SOURCES = {"chunk_cumsum": "ssd_chunk_cumsum.hip",
+                 "fwd_pass_state": "ssd_fwd_pass_state.hip",
+                 "compute_out": "ssd_compute_out.hip"}
+
+
+def algorithmic(w, y_bytes: int):
+    """Bytes each stage must move and FLOPs it must do (no redundancy, no
+    masked upper triangle), per launch over the whole workload."""
+    b, L, H, P, N, G, T = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                           w.ngroups, w.chunk_size)
+    e = 2 if w.dtype == "bf16" else 4
+    nc = w.nchunks
+    init = 1 if w.init_std is not None else 0
+    by = {
+        "chunk_cumsum": 8 * b * L * H,
+        "fwd_pass_state": (e * b * L * H * P + e * b * L * G * N + 8 * b * L * H
+                           + 4 * b * H * P * N * init + 4 * b * H * nc * P * N
+                           + 4 * b * H * P * N),
+        "compute_out": (e * b * L * H * P + 2 * e * b * L * G * N + 8 * b * L * H
+                        + 4 * b * H * nc * P * N + 4 * H + y_bytes * b * L * H * P),
+    }
+    fl = {
+        "chunk_cumsum": 2 * b * L * H,
+        "fwd_pass_state": 2 * b * L * H * P * N,
+        "compute_out": (2 * b * L * H * P * N + b * nc * H * T * (T + 1) * P
+                        + b * nc * G * T * (T + 1) * N),
+    }
+    return by, fl
+
+
+def source_sha(stage: str) -> str:
+    path = os.path.join(ROOT, "mamba_ssd_chunked_fwd_amd", "csrc",
+                        STAGE_SOURCES[stage])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha(stage):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp):
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    if threads <= 0:
+        threads = len(os.sched_getaffinity(0))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                       inp["D"], inp["init_state"], chunk_size=w.chunk_size,
+                       nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": w.tokens / med, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"the full {w.name} workload ({w.batch * w.nheads} "
+                       f"(batch, head) pairs x {w.seqlen} tokens), fp64 "
+                       f"token recurrence, OpenMP over pairs; median of 3 "
+                       f"runs of {', '.join('%.2f' % t for t in times)} s")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="small_bf16")
+    ap.add_argument("--y-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (HBM counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
+              "is not supported (the path shards over (batch, head) with no "
+              "communication between GPUs).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mamba_ssd_chunked_fwd_amd as ssd
+    from ssd_workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w)
+    tin = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    ty = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
+    b, L, H, P, N, G, T = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                           w.ngroups, w.chunk_size)
+    nc = w.nchunks
+    y_bytes = 2 if ty == torch.bfloat16 else 4
+    by, fl = algorithmic(w, y_bytes)
+    step_bytes = sum(by.values())
+    nsets = max(1, min(16, -(-(1 << 30) // step_bytes)))
+
+    def make_set():
+        s = {k: torch.from_numpy(inp[k]).to(dev, tin) for k in ("x", "B", "C")}
+        for k in ("dt", "A", "D"):
+            s[k] = torch.from_numpy(inp[k]).to(dev)
+        s["init"] = (None if inp["init_state"] is None
+                     else torch.from_numpy(inp["init_state"]).to(dev))
+        s["g"] = torch.empty(b, H, L, device=dev)
+        s["states"] = torch.empty(b, H, nc, P, N, device=dev)
+        s["final"] = torch.empty(b, H, P, N, device=dev)
+        s["y"] = torch.empty(b, L, H, P, device=dev, dtype=ty)
+        return s
+
+    sets = [make_set() for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ssd.ssd_chunk_cumsum(s["dt"], s["A"], s["g"], T)
+        if ev is not None:
+            ev[1].record(stream)
+        ssd.ssd_fwd_pass_state(s["x"], s["B"], s["dt"], s["g"], s["init"],
+                               s["states"], s["final"], T)
+        if ev is not None:
+            ev[2].record(stream)
+        ssd.ssd_compute_out(s["x"], s["B"], s["C"], s["dt"], s["g"],
+                            s["states"], s["D"], s["y"], T)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % nsets], events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_names = ["chunk_cumsum", "fwd_pass_state", "compute_out"]
+    dur = {n: statistics.mean(e[k].elapsed_time(e[k + 1]) for e in events)
+           for k, n in enumerate(stage_names)}
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = w.tokens / (wall / args.steps)
+
+    # ssd_forward on the same sets, for transparency (same three launches)
+    for i in range(5):
+        s = sets[i % nsets]
+        ssd.ssd_forward(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
+                        s["init"], s["y"], s["states"], s["final"], s["g"], T)
+    torch.cuda.synchronize()
+    tf = time.perf_counter()
+    nfwd = max(20, args.steps // 2)
+    for i in range(nfwd):
+        s = sets[i % nsets]
+        ssd.ssd_forward(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
+                        s["init"], s["y"], s["states"], s["final"], s["g"], T)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - tf) * 1e3 / nfwd
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    stages = {}
+    for n in stage_names:
+        ms = dur[n]
+        gbs = by[n] / (ms * 1e-3) / 1e9
+        peak_tf = BF16_MFMA_TFLOPS if w.dtype == "bf16" else FP32_MFMA_TFLOPS
+        stages[n] = {"ms": round(ms, 5), "alg_bytes": by[n], "alg_flop": fl[n],
+                     "GB_per_s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "TFLOP_per_s": round(fl[n] / (ms * 1e-3) / 1e12, 2),
+                     "mfma_frac_of_peak": round(fl[n] / (ms * 1e-3) / 1e12 / peak_tf, 4)}
+    dom = max(stage_names, key=lambda n: dur[n])
+    achieved = by[dom] / (dur[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(w.name, dom)
+    total_flop = sum(fl.values())
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "batch": b, "seqlen": L, "nheads": H,
+                   "headdim": P, "dstate": N, "ngroups": G, "chunk_size": T,
+                   "x_dtype": w.dtype, "y_dtype": args.y_dtype,
+                   "state_dtype": "fp32", "input_sets_rotated": nsets},
+        "roofline": {"bound": "hbm", "kernel": dom,
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "stages": stages,
+        "effective_TFLOP_per_s": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "ssd_forward_ms": round(fwd_ms, 5),
+        "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
