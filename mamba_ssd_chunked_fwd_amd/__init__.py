@@ -51,7 +51,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"libssd.so not found at {LIB_PATH}; build it with "
-            "`python -m mamba_ssd_chunked_fwd_amd.build`")
+            "`python mamba_ssd_chunked_fwd_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     dims = ctypes.POINTER(SsdDims)

@@ -1,6 +1,8 @@
 """Build libssd.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m mamba_ssd_chunked_fwd_amd.build
+    python mamba_ssd_chunked_fwd_amd/build.py
+
+(run by path: importing the package loads the library this script builds)
 
 Sources compile in parallel into objects under _build/ at the repository
 root, then link into mamba_ssd_chunked_fwd_amd/libssd.so.  All device code

@@ -31,6 +31,34 @@ constexpr int kHeadDim = 64;  // P: the only head size built
 // log2(e): exp(v) = exp2(v * log2(e)).
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ---- raw buffer loads
+// A buffer descriptor (base, byte range) lives in scalar registers; each lane
+// passes a 32-bit byte offset.  Reads at or beyond the range return zero
+// without touching memory, which is how token tiles that run past the end
+// of a sequence are masked.  Offsets must stay below 2^31.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufferConfig = 0x00020000;  // raw 32-bit dwords (gfx9 family)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                           kBufferConfig);
+}
+__device__ __forceinline__ uint32_t load_b32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 load_b64(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x4 load_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float load_f32(rsrc_t r, uint32_t off) {
+  return __uint_as_float(load_b32(r, off));
+}
+__device__ __forceinline__ f32x4 load_f32x4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, load_b128(r, off));
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
       __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -70,6 +98,19 @@ __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi,
 
 __device__ __forceinline__ u32x4 make_u32x4(const uint32_t (&a)[4]) {
   return (u32x4){a[0], a[1], a[2], a[3]};
+}
+
+// ---- LDS transpose read (ds_read_b64_tr_b16)
+// Within each 16-lane group, if lane i points at row R0 + i/4, column
+// C0 + 4*(i%4) of a row-major bf16 tile in LDS, lane j receives the four
+// elements (R0 + k, C0 + j), k = 0..3: one column, four consecutive rows --
+// the layout of a matrix-instruction operand whose k index runs along rows.
+// `p` must point into LDS.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)const_cast<uint16_t*>(p)));
 }
 
 // Low / high bf16 halves of two words, packed: (lo16(a), lo16(b)) and

@@ -17,6 +17,14 @@
 // * The slice is computed transposed, S^T[n][p], so each lane's four
 //   accumulator registers are four consecutive n at one p: the per-chunk state
 //   store and the final store are 16-byte writes straight from registers.
+// * A chunk's contribution P_c = X_c^T (w o B_c) does not depend on the
+//   carried state, so it is accumulated in fresh registers and the only
+//   sequential step is S = 2^{g_last} S + P_c.  Everything else is streamed:
+//   the global loads of chunk c + D are issued while chunk c is processed
+//   (a D-deep register ring; the chunk loop is unrolled D times so every ring
+//   slot is a fixed set of registers), the LDS operand tiles are double
+//   buffered, and the per-token weights w of chunk c + 1 are formed while
+//   chunk c is processed, so one barrier per chunk suffices.
 // * The contraction runs over tokens, which are the slow axis of both x and
 //   B in memory.  Each chunk's X and w o B tiles are therefore written to LDS
 //   token-contiguous ([p][t] and [n][t]) by the threads that load them, so
@@ -25,8 +33,6 @@
 //   split into bf16 hi + lo (two MFMAs) so the product keeps ~16 mantissa bits
 //   under fp32 accumulation; a single bf16 rounding of it loses the output
 //   tolerance.  fp32 inputs use the fp32 matrix instruction directly.
-// * The next chunk's global loads are issued before the current chunk's
-//   matrix work so their latency overlaps it (register double-buffering).
 // * Block ids are remapped so the n-tiles of one (b, h) land on one XCD and
 //   share its L2 for the X chunk they all read.
 // HBM traffic per (b, h, chunk): x (e*T*64) + B (e*T*N, shared by the heads
@@ -38,6 +44,9 @@
 namespace ssd {
 namespace {
 
+// A byte offset past every buffer range used here (reads return zero).
+constexpr uint32_t kPastRange = 0x7FFFFFF0u;
+
 // Map the hardware block id so consecutive logical tiles run on one XCD
 // (blocks are dealt to the 8 XCDs round-robin).
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
@@ -46,20 +55,38 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // ---------------------------------------------------------------- bf16 path
-template <int T, int N, int BN>
+// The chunk is streamed in token tiles of TK = min(T, 128); P accumulates over
+// the T / TK tiles of a chunk.  Both operand tiles sit in LDS row-major
+// (token rows): X exactly as loaded, w o B as computed, and the matrix
+// operands are read with the LDS transpose read.  k-slot map of one 32-token
+// step kk for lane group lq: slots 0..3 <-> tokens 32kk + 4lq + 0..3, slots
+// 4..7 <-> tokens 32kk + 16 + 4lq + 0..3 (both operands alike).  Row strides
+// are chosen so each 32-lane pass of a transpose read (8 consecutive rows x
+// 32 bytes) touches every LDS bank once.
+template <int N>
+struct BfTileStride {
+  static constexpr int value = N == 16 ? 16 : N + 16;
+};
+
+template <int T, int N, int BN, int D>
 __global__ __launch_bounds__(256) void state_pass_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt, const float* __restrict__ g,
     const float* __restrict__ init, float* __restrict__ states,
     float* __restrict__ final_state, int L, int H, int G, int nc) {
-  constexpr int NB = BN / 16;           // 16-column blocks per wave
-  constexpr int XS = T + 8;             // LDS row stride (bf16 elements)
-  constexpr int IX = T / 64;            // X staging passes
-  constexpr int kUnits = (BN / 2) * (T / 8);   // B staging units
-  constexpr int UB = (kUnits + 255) / 256;     // per thread
-  __shared__ __attribute__((aligned(16))) uint16_t xT[64 * XS];
-  __shared__ __attribute__((aligned(16))) uint16_t bh[BN * XS];
-  __shared__ __attribute__((aligned(16))) uint16_t bl[BN * XS];
+  static_assert(D >= 2, "the weights of tile k+1 come from another ring slot");
+  constexpr int TK = T < 128 ? T : 128;        // tokens per tile
+  constexpr int R = T / TK;                    // tiles per chunk
+  constexpr int NB = BN / 16;                  // 16-column blocks per wave
+  constexpr int XS = BfTileStride<kHeadDim>::value;  // X row stride (bf16)
+  constexpr int BS = BfTileStride<BN>::value;        // w o B row stride (bf16)
+  constexpr int XU = TK * (kHeadDim / 8) / 256;      // X units (token x 8 p) per thread
+  constexpr int kBUnits = TK * (BN / 8);             // B units (token x 8 n)
+  constexpr int BU = (kBUnits + 255) / 256;          // B units per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][TK * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t bhs[2][TK * BS];
+  __shared__ __attribute__((aligned(16))) uint16_t bls[2][TK * BS];
+  __shared__ __attribute__((aligned(16))) float ws[2][TK];
 
   constexpr int NT = N / BN;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -70,116 +97,155 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   const int p = 16 * wave + lr;
+  const int ntiles = nc * R;
 
-  // State slice in registers: acc[nb] holds S[p][n0 + 16nb + 4lq + 0..3].
+  // Buffer descriptors: reads past the sequence's last token return zero.
+  const float* gh = g + (size_t)bh_idx * L;
+  const uint32_t xrow = (uint32_t)(H * kHeadDim), brow = (uint32_t)(G * N);
+  const rsrc_t xr = make_rsrc(x + ((size_t)b * L * H + h) * kHeadDim,
+                              ((uint32_t)(L - 1) * xrow + kHeadDim) * 2u);
+  const rsrc_t br = make_rsrc(Bm + ((size_t)b * L * G + grp) * N,
+                              ((uint32_t)(L - 1) * brow + N) * 2u);
+  const rsrc_t gr = make_rsrc(gh, (uint32_t)L * 4u);
+  const rsrc_t dr = make_rsrc(dt + (size_t)b * L * H + h, ((uint32_t)(L - 1) * H + 1) * 4u);
+
+  // State slice: acc[nb] holds S[p][n0 + 16nb + 4lq + 0..3].
   f32x4 acc[NB];
   const size_t sbase = (size_t)bh_idx * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
     acc[nb] = init ? *(const f32x4*)(init + sbase + 16 * nb) : (f32x4){0, 0, 0, 0};
+  // Let the initial state land before the tile ring starts, so waits inside
+  // the loop only ever concern ring loads.
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // Staging registers for one chunk.
-  const int pp = tid & 31, xtb = tid >> 5;   // X: p pair, 8-token block
-  uint32_t xr[IX][8];
-  uint32_t br[UB][8];
-  float gr[UB][8], dr[UB][8];
-  float glast = 0.0f;
-  int nvalid = 0;
+  // Per-thread byte offsets (within a tile) of each staging unit; idle B
+  // units point past the range, so every thread issues the same loads
+  // (straight-line code keeps the compiler's memory-wait counts exact).
+  uint32_t xoff[XU], boff[BU];
+  int xlds[XU], blds[BU];
+#pragma unroll
+  for (int i = 0; i < XU; ++i) {
+    const int u = tid + 256 * i;
+    const int t = u >> 3, c8 = u & 7;
+    xoff[i] = ((uint32_t)t * xrow + 8 * c8) * 2u;
+    xlds[i] = t * XS + 8 * c8;
+  }
+#pragma unroll
+  for (int i = 0; i < BU; ++i) {
+    const int u = tid + 256 * i;
+    const int t = u / (BN / 8), c8 = u % (BN / 8);
+    boff[i] = u < kBUnits ? ((uint32_t)t * brow + n0 + 8 * c8) * 2u : kPastRange;
+    blds[i] = t * BS + 8 * c8;
+  }
+  const uint32_t xstep = xrow * 2u, bstep = brow * 2u;   // bytes per token
 
-  const float* gh = g + (size_t)bh_idx * L;
+  struct Slot {
+    u32x4 x[XU];           // one token x 8 p's
+    u32x4 b[BU];           // one token x 8 n's
+    float g, dt, glast;
+  };
+  Slot ring[D];
 
-  auto load = [&](int c) {
-    const int t0 = c * T;
-    nvalid = min(T, L - t0);
+  // Global loads of tile k (tokens [k*TK, k*TK + TK) of the sequence).
+  auto issue = [&](int k, Slot& sl) {
+    const int c = k / R;
+    const uint32_t t0 = (uint32_t)(k * TK);
 #pragma unroll
-    for (int it = 0; it < IX; ++it) {
+    for (int i = 0; i < XU; ++i) sl.x[i] = load_b128(xr, xoff[i] + t0 * xstep);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int t = 8 * (xtb + 8 * it) + r;
-        xr[it][r] = t < nvalid
-            ? *(const uint32_t*)(x + (((size_t)b * L + t0 + t) * H + h) * kHeadDim + 2 * pp)
-            : 0u;
-      }
-    }
-#pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
-      const int u = tid + 256 * ub;
-      const int np = u % (BN / 2), tb = u / (BN / 2);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int t = 8 * tb + r;
-        const bool ok = (u < kUnits) && t < nvalid;
-        br[ub][r] = ok ? *(const uint32_t*)(Bm + (((size_t)b * L + t0 + t) * G + grp) * N + n0 + 2 * np) : 0u;
-        gr[ub][r] = ok ? gh[t0 + t] : 0.0f;
-        dr[ub][r] = ok ? dt[((size_t)b * L + t0 + t) * H + h] : 0.0f;
-      }
-    }
-    glast = gh[t0 + nvalid - 1];
+    for (int i = 0; i < BU; ++i) sl.b[i] = load_b128(br, boff[i] + t0 * bstep);
+    sl.g = load_f32(gr, (t0 + tid) * 4u);
+    sl.dt = load_f32(dr, (t0 + tid) * (uint32_t)H * 4u);
+    // g at the chunk's last token: a vector load, so nothing waits for it here
+    sl.glast = load_f32(gr, (uint32_t)(min(c * T + T, L) - 1) * 4u);
   };
 
-  auto commit = [&]() {
+  // Per-token weights of tile k and its chunk's total decay 2^{g_last}.
+  // Tokens past the end read dt = g = 0, so their weight is exactly 0.
+  auto commit_w = [&](int k, const Slot& sl, float& decay) {
+    if (tid < TK) ws[k & 1][tid] = sl.dt * exp2_hw(sl.glast - sl.g);
+    decay = exp2_hw(sl.glast);
+  };
+
+  // X (as loaded) and the split w o B of tile k into LDS buffer k & 1.
+  auto commit_xb = [&](int k, const Slot& sl) {
+    const int buf = k & 1;
 #pragma unroll
-    for (int it = 0; it < IX; ++it) {
-      u32x4 lo, hi;
+    for (int i = 0; i < XU; ++i) *(u32x4*)(xs[buf] + xlds[i]) = sl.x[i];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lo[k] = lo_halves(xr[it][2 * k], xr[it][2 * k + 1]);
-        hi[k] = hi_halves(xr[it][2 * k], xr[it][2 * k + 1]);
-      }
-      const int tcol = 8 * (xtb + 8 * it);
-      *(u32x4*)(xT + (2 * pp) * XS + tcol) = lo;
-      *(u32x4*)(xT + (2 * pp + 1) * XS + tcol) = hi;
-    }
+    for (int i = 0; i < BU; ++i) {
+      const int u = tid + 256 * i;
+      if (u < kBUnits) {
+        const float w = ws[buf][u / (BN / 8)];
+        uint32_t hv[4], lv[4];
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
-      const int u = tid + 256 * ub;
-      if (u < kUnits) {
-        const int np = u % (BN / 2), tb = u / (BN / 2);
-        float f0[8], f1[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float w = (8 * tb + r < nvalid) ? dr[ub][r] * exp2_hw(glast - gr[ub][r]) : 0.0f;
-          f0[r] = bf16_lo(br[ub][r]) * w;
-          f1[r] = bf16_hi(br[ub][r]) * w;
-        }
-        uint32_t h0[4], l0[4], h1[4], l1[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          split_bf16(f0[2 * k], f0[2 * k + 1], h0[k], l0[k]);
-          split_bf16(f1[2 * k], f1[2 * k + 1], h1[k], l1[k]);
-        }
-        *(u32x4*)(bh + (2 * np) * XS + 8 * tb) = make_u32x4(h0);
-        *(u32x4*)(bh + (2 * np + 1) * XS + 8 * tb) = make_u32x4(h1);
-        *(u32x4*)(bl + (2 * np) * XS + 8 * tb) = make_u32x4(l0);
-        *(u32x4*)(bl + (2 * np + 1) * XS + 8 * tb) = make_u32x4(l1);
+        for (int e = 0; e < 4; ++e)
+          split_bf16(bf16_lo(sl.b[i][e]) * w, bf16_hi(sl.b[i][e]) * w, hv[e], lv[e]);
+        *(u32x4*)(bhs[buf] + blds[i]) = make_u32x4(hv);
+        *(u32x4*)(bls[buf] + blds[i]) = make_u32x4(lv);
       }
     }
   };
 
-  load(0);
-  for (int c = 0; c < nc; ++c) {
-    // The state entering chunk c.
-    float* dst = states + ((size_t)bh_idx * nc + c) * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) *(f32x4*)(dst + 16 * nb) = acc[nb];
+  // Transpose-read addresses of this lane (element offsets within a tile).
+  const int rsel = 4 * lq + (lr >> 2), csel = 4 * (lr & 3);
+  const int xrd = rsel * XS + 16 * wave + csel;
+  const int brd = rsel * BS + csel;
 
-    __syncthreads();  // every wave is done reading the previous chunk's tiles
-    commit();
-    const float decay = exp2_hw(glast);
-    if (c + 1 < nc) load(c + 1);
-    __syncthreads();
+  // Tiles past the end are issued too: their loads fall outside every
+  // buffer range, cost no memory traffic and keep the wait counts exact.
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(s, ring[s]);
+  float decay_cur = 1.0f, decay_next = 1.0f;
+  commit_w(0, ring[0], decay_cur);
+  __syncthreads();
 
+  f32x4 ph[NB], pl[NB];
+  for (int k0 = 0; k0 < ntiles; k0 += D) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] *= decay;
+    for (int s = 0; s < D; ++s) {
+      const int k = k0 + s;
+      if (k >= ntiles) break;
+      const int sub = k % R;
+      if (sub == 0) {
+        // The state entering chunk k / R.
+        float* dst = states + ((size_t)bh_idx * nc + k / R) * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
 #pragma unroll
-    for (int s = 0; s < T / 32; ++s) {
-      const u32x4 xv = *(const u32x4*)(xT + p * XS + 32 * s + 8 * lq);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int row = (16 * nb + lr) * XS + 32 * s + 8 * lq;
-        acc[nb] = mfma_bf16(*(const u32x4*)(bh + row), xv, acc[nb]);
-        acc[nb] = mfma_bf16(*(const u32x4*)(bl + row), xv, acc[nb]);
+        for (int nb = 0; nb < NB; ++nb) {
+          *(f32x4*)(dst + 16 * nb) = acc[nb];
+          ph[nb] = pl[nb] = (f32x4){0, 0, 0, 0};
+        }
       }
+      commit_xb(k, ring[s]);
+      float dnext = decay_next;
+      if (k + 1 < ntiles) commit_w(k + 1, ring[(s + 1) % D], dnext);
+      issue(k + D, ring[s]);
+      __syncthreads();
+
+      const uint16_t* xt = xs[k & 1];
+      const uint16_t* bht = bhs[k & 1];
+      const uint16_t* blt = bls[k & 1];
+#pragma unroll
+      for (int kk = 0; kk < TK / 32; ++kk) {
+        const u32x2 x0 = lds_read_tr16(xt + xrd + 32 * kk * XS);
+        const u32x2 x1 = lds_read_tr16(xt + xrd + (32 * kk + 16) * XS);
+        const u32x4 xv = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int o0 = brd + 32 * kk * BS + 16 * nb, o1 = o0 + 16 * BS;
+          const u32x2 h0 = lds_read_tr16(bht + o0), h1 = lds_read_tr16(bht + o1);
+          const u32x2 l0 = lds_read_tr16(blt + o0), l1 = lds_read_tr16(blt + o1);
+          ph[nb] = mfma_bf16((u32x4){h0[0], h0[1], h1[0], h1[1]}, xv, ph[nb]);
+          pl[nb] = mfma_bf16((u32x4){l0[0], l0[1], l1[0], l1[1]}, xv, pl[nb]);
+        }
+      }
+      if (sub == R - 1) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = decay_cur * acc[nb] + (ph[nb] + pl[nb]);
+      }
+      if (k + 1 < ntiles && (k + 1) % R == 0) decay_cur = dnext;
+      decay_next = dnext;
     }
   }
   if (final_state) {
@@ -189,21 +255,26 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
 }
 
 // ---------------------------------------------------------------- fp32 path
-// Token k-map for v_mfma_f32_16x16x4_f32: step (u, v) gives lane group lq the
-// token 16u + 4lq + v, so each lane reads four steps' operands at once.
-template <int T, int N, int BN>
+// Token tiles of TK = 64.  k-map for v_mfma_f32_16x16x4_f32: step (u, v)
+// gives lane group lq the token 16u + 4lq + v of the tile, so each lane reads
+// four steps' operands at once.  Staging units are (4 columns x 4 tokens).
+template <int T, int N, int BN, int D>
 __global__ __launch_bounds__(256) void state_pass_f32(
     const float* __restrict__ x, const float* __restrict__ Bm,
     const float* __restrict__ dt, const float* __restrict__ g,
     const float* __restrict__ init, float* __restrict__ states,
     float* __restrict__ final_state, int L, int H, int G, int nc) {
+  static_assert(D >= 2, "the weights of tile k+1 come from another ring slot");
+  constexpr int TK = 64;
+  constexpr int R = T / TK;
   constexpr int NB = BN / 16;
-  constexpr int XS = T + 4;             // LDS row stride (floats)
-  constexpr int IX = T / 64;            // X staging passes (4 tokens x 4 p each)
-  constexpr int kUnits = (BN / 4) * (T / 4);
-  constexpr int UB = (kUnits + 255) / 256;
-  __shared__ __attribute__((aligned(16))) float xT[64 * XS];
-  __shared__ __attribute__((aligned(16))) float bT[BN * XS];
+  constexpr int XS = TK + 4;                   // LDS row stride (floats)
+  constexpr int XU = TK / 64;                  // X units per thread
+  constexpr int kBUnits = (BN / 4) * (TK / 4);
+  constexpr int BU = (kBUnits + 255) / 256;
+  __shared__ __attribute__((aligned(16))) float xs[2][64 * XS];
+  __shared__ __attribute__((aligned(16))) float bs[2][BN * XS];
+  __shared__ __attribute__((aligned(16))) float ws[2][TK];
 
   constexpr int NT = N / BN;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -214,101 +285,143 @@ __global__ __launch_bounds__(256) void state_pass_f32(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   const int p = 16 * wave + lr;
+  const int ntiles = nc * R;
+
+  const float* gh = g + (size_t)bh_idx * L;
+  const uint32_t xrow = (uint32_t)(H * kHeadDim), brow = (uint32_t)(G * N);
+  const rsrc_t xr = make_rsrc(x + ((size_t)b * L * H + h) * kHeadDim,
+                              ((uint32_t)(L - 1) * xrow + kHeadDim) * 4u);
+  const rsrc_t br = make_rsrc(Bm + ((size_t)b * L * G + grp) * N,
+                              ((uint32_t)(L - 1) * brow + N) * 4u);
+  const rsrc_t gr = make_rsrc(gh, (uint32_t)L * 4u);
+  const rsrc_t dr = make_rsrc(dt + (size_t)b * L * H + h, ((uint32_t)(L - 1) * H + 1) * 4u);
 
   f32x4 acc[NB];
   const size_t sbase = (size_t)bh_idx * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
     acc[nb] = init ? *(const f32x4*)(init + sbase + 16 * nb) : (f32x4){0, 0, 0, 0};
+  // Let the initial state land before the tile ring starts, so waits inside
+  // the loop only ever concern ring loads.
+  __builtin_amdgcn_s_waitcnt(0);
 
-  const int pq = tid & 15, xtb = tid >> 4;   // X: 4 p's, 4-token block
-  f32x4 xr[IX][4];
-  f32x4 br[UB][4];
-  float gr[UB][4], dr[UB][4];
-  float glast = 0.0f;
-  int nvalid = 0;
-  const float* gh = g + (size_t)bh_idx * L;
+  struct Slot {
+    f32x4 x[XU][4];
+    f32x4 b[BU][4];
+    float g, dt, glast;
+  };
+  Slot ring[D];
 
-  auto load = [&](int c) {
-    const int t0 = c * T;
-    nvalid = min(T, L - t0);
+  uint32_t xoff[XU], boff[BU];
 #pragma unroll
-    for (int it = 0; it < IX; ++it) {
+  for (int i = 0; i < XU; ++i) {
+    const int u = tid + 256 * i;
+    xoff[i] = ((uint32_t)(4 * (u >> 4)) * xrow + 4 * (u & 15)) * 4u;
+  }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * (xtb + 16 * it) + r;
-        xr[it][r] = t < nvalid
-            ? *(const f32x4*)(x + (((size_t)b * L + t0 + t) * H + h) * kHeadDim + 4 * pq)
-            : (f32x4){0, 0, 0, 0};
-      }
+  for (int i = 0; i < BU; ++i) {
+    const int u = tid + 256 * i;
+    boff[i] = u < kBUnits
+        ? ((uint32_t)(4 * (u / (BN / 4))) * brow + n0 + 4 * (u % (BN / 4))) * 4u
+        : kPastRange;
+  }
+  const uint32_t xstep = xrow * 4u, bstep = brow * 4u;
+
+  auto issue = [&](int k, Slot& sl) {
+    const int c = k / R;
+    const uint32_t t0 = (uint32_t)(k * TK);
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sl.x[i][r] = load_f32x4(xr, xoff[i] + (t0 + r) * xstep);
     }
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
-      const int u = tid + 256 * ub;
-      const int nq = u % (BN / 4), tb = u / (BN / 4);
+    for (int i = 0; i < BU; ++i) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * tb + r;
-        const bool ok = (u < kUnits) && t < nvalid;
-        br[ub][r] = ok ? *(const f32x4*)(Bm + (((size_t)b * L + t0 + t) * G + grp) * N + n0 + 4 * nq)
-                       : (f32x4){0, 0, 0, 0};
-        gr[ub][r] = ok ? gh[t0 + t] : 0.0f;
-        dr[ub][r] = ok ? dt[((size_t)b * L + t0 + t) * H + h] : 0.0f;
-      }
+      for (int r = 0; r < 4; ++r) sl.b[i][r] = load_f32x4(br, boff[i] + (t0 + r) * bstep);
     }
-    glast = gh[t0 + nvalid - 1];
+    sl.g = load_f32(gr, (t0 + tid) * 4u);
+    sl.dt = load_f32(dr, (t0 + tid) * (uint32_t)H * 4u);
+    sl.glast = load_f32(gr, (uint32_t)(min(c * T + T, L) - 1) * 4u);
   };
 
-  auto commit = [&]() {
+  auto commit_w = [&](int k, const Slot& sl, float& decay) {
+    if (tid < TK) ws[k & 1][tid] = sl.dt * exp2_hw(sl.glast - sl.g);
+    decay = exp2_hw(sl.glast);
+  };
+
+  auto commit_xb = [&](int k, const Slot& sl) {
+    const int buf = k & 1;
 #pragma unroll
-    for (int it = 0; it < IX; ++it) {
-      const int tcol = 4 * (xtb + 16 * it);
+    for (int i = 0; i < XU; ++i) {
+      const int u = tid + 256 * i;
+      const int pq = u & 15, tq = u >> 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *(f32x4*)(xT + (4 * pq + i) * XS + tcol) =
-            (f32x4){xr[it][0][i], xr[it][1][i], xr[it][2][i], xr[it][3][i]};
+      for (int e = 0; e < 4; ++e)
+        *(f32x4*)(xs[buf] + (4 * pq + e) * XS + 4 * tq) =
+            (f32x4){sl.x[i][0][e], sl.x[i][1][e], sl.x[i][2][e], sl.x[i][3][e]};
     }
 #pragma unroll
-    for (int ub = 0; ub < UB; ++ub) {
-      const int u = tid + 256 * ub;
-      if (u < kUnits) {
-        const int nq = u % (BN / 4), tb = u / (BN / 4);
-        float w[4];
+    for (int i = 0; i < BU; ++i) {
+      const int u = tid + 256 * i;
+      if (u < kBUnits) {
+        const int nq = u % (BN / 4), tq = u / (BN / 4);
+        const f32x4 w = *(const f32x4*)(ws[buf] + 4 * tq);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          w[r] = (4 * tb + r < nvalid) ? dr[ub][r] * exp2_hw(glast - gr[ub][r]) : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *(f32x4*)(bT + (4 * nq + i) * XS + 4 * tb) =
-              (f32x4){br[ub][0][i] * w[0], br[ub][1][i] * w[1], br[ub][2][i] * w[2],
-                      br[ub][3][i] * w[3]};
+        for (int e = 0; e < 4; ++e)
+          *(f32x4*)(bs[buf] + (4 * nq + e) * XS + 4 * tq) =
+              (f32x4){sl.b[i][0][e] * w[0], sl.b[i][1][e] * w[1],
+                      sl.b[i][2][e] * w[2], sl.b[i][3][e] * w[3]};
       }
     }
   };
 
-  load(0);
-  for (int c = 0; c < nc; ++c) {
-    float* dst = states + ((size_t)bh_idx * nc + c) * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
+  // Tiles past the end are issued too: their loads fall outside every
+  // buffer range, cost no memory traffic and keep the wait counts exact.
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) *(f32x4*)(dst + 16 * nb) = acc[nb];
+  for (int s = 0; s < D; ++s) issue(s, ring[s]);
+  float decay_cur = 1.0f, decay_next = 1.0f;
+  commit_w(0, ring[0], decay_cur);
+  __syncthreads();
 
-    __syncthreads();
-    commit();
-    const float decay = exp2_hw(glast);
-    if (c + 1 < nc) load(c + 1);
-    __syncthreads();
-
+  f32x4 pc[NB];
+  for (int k0 = 0; k0 < ntiles; k0 += D) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] *= decay;
+    for (int s = 0; s < D; ++s) {
+      const int k = k0 + s;
+      if (k >= ntiles) break;
+      const int sub = k % R;
+      if (sub == 0) {
+        float* dst = states + ((size_t)bh_idx * nc + k / R) * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
 #pragma unroll
-    for (int u = 0; u < T / 16; ++u) {
-      const f32x4 xv = *(const f32x4*)(xT + p * XS + 16 * u + 4 * lq);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const f32x4 bv = *(const f32x4*)(bT + (16 * nb + lr) * XS + 16 * u + 4 * lq);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[nb] = mfma_f32(bv[v], xv[v], acc[nb]);
+        for (int nb = 0; nb < NB; ++nb) {
+          *(f32x4*)(dst + 16 * nb) = acc[nb];
+          pc[nb] = (f32x4){0, 0, 0, 0};
+        }
       }
+      commit_xb(k, ring[s]);
+      float dnext = decay_next;
+      if (k + 1 < ntiles) commit_w(k + 1, ring[(s + 1) % D], dnext);
+      issue(k + D, ring[s]);
+      __syncthreads();
+
+      const int buf = k & 1;
+#pragma unroll
+      for (int u = 0; u < TK / 16; ++u) {
+        const f32x4 xv = *(const f32x4*)(xs[buf] + p * XS + 16 * u + 4 * lq);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const f32x4 bv = *(const f32x4*)(bs[buf] + (16 * nb + lr) * XS + 16 * u + 4 * lq);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) pc[nb] = mfma_f32(bv[v], xv[v], pc[nb]);
+        }
+      }
+      if (sub == R - 1) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = decay_cur * acc[nb] + pc[nb];
+      }
+      if (k + 1 < ntiles && (k + 1) % R == 0) decay_cur = dnext;
+      decay_next = dnext;
     }
   }
   if (final_state) {
@@ -319,8 +432,7 @@ __global__ __launch_bounds__(256) void state_pass_f32(
 
 // ------------------------------------------------------------- launching
 // n-tile width: the widest tile that still gives >= 1024 workgroups (four
-// per CU), else the narrowest; a (b, h) pair's slice is split at most N/16
-// ways.
+// per CU), else the narrowest.
 int choose_bn(const Shape& s) {
   const int64_t pairs = s.batch * s.nheads;
   for (int bn : {64, 32}) {
@@ -329,19 +441,27 @@ int choose_bn(const Shape& s) {
   return 16;
 }
 
+// Ring depth: token tiles in flight per workgroup, bounded by register use.
+template <bool BF16, int T, int BN>
+constexpr int ring_depth() {
+  if constexpr (BF16) return (T >= 128 && BN >= 32) ? 2 : 4;
+  else return BN >= 32 ? 2 : 4;
+}
+
 template <bool BF16, int T, int N, int BN>
 int launch_t(const void* x, const void* B, const float* dt, const float* g,
              const float* init, float* states, float* fin, const Shape& s,
              hipStream_t st) {
+  constexpr int D = ring_depth<BF16, T, BN>();
   const unsigned blocks = (unsigned)(s.batch * s.nheads * (N / BN));
   const int L = (int)s.seqlen, H = (int)s.nheads, G = (int)s.ngroups,
             nc = (int)s.nchunks();
   if constexpr (BF16) {
-    hipLaunchKernelGGL((state_pass_bf16<T, N, BN>), dim3(blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL((state_pass_bf16<T, N, BN, D>), dim3(blocks), dim3(256), 0, st,
                        (const uint16_t*)x, (const uint16_t*)B, dt, g, init, states,
                        fin, L, H, G, nc);
   } else {
-    hipLaunchKernelGGL((state_pass_f32<T, N, BN>), dim3(blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL((state_pass_f32<T, N, BN, D>), dim3(blocks), dim3(256), 0, st,
                        (const float*)x, (const float*)B, dt, g, init, states, fin,
                        L, H, G, nc);
   }
