@@ -50,7 +50,7 @@ def algorithmic(w, y_bytes: int):
     nc = w.nchunks
     init = 1 if w.init_std is not None else 0
     by = {
-        "chunk_cumsum": 8 * b * L * H,
+        "chunk_cumsum": 12 * b * L * H,
         "fwd_pass_state": (e * b * L * H * P + e * b * L * G * N + 8 * b * L * H
                            + 4 * b * H * P * N * init + 4 * b * H * nc * P * N
                            + 4 * b * H * P * N),
@@ -150,7 +150,8 @@ def main() -> int:
             s[k] = torch.from_numpy(inp[k]).to(dev)
         s["init"] = (None if inp["init_state"] is None
                      else torch.from_numpy(inp["init_state"]).to(dev))
-        s["g"] = torch.empty(b, H, L, device=dev)
+        s["ws"] = torch.empty(2, b, H, L, device=dev)   # ssd_forward's workspace
+        s["g"], s["dt_t"] = s["ws"][0], s["ws"][1]
         s["states"] = torch.empty(b, H, nc, P, N, device=dev)
         s["final"] = torch.empty(b, H, P, N, device=dev)
         s["y"] = torch.empty(b, L, H, P, device=dev, dtype=ty)
@@ -162,14 +163,14 @@ def main() -> int:
     def step(s, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        ssd.ssd_chunk_cumsum(s["dt"], s["A"], s["g"], T)
+        ssd.ssd_chunk_cumsum(s["dt"], s["A"], s["g"], s["dt_t"], T)
         if ev is not None:
             ev[1].record(stream)
-        ssd.ssd_fwd_pass_state(s["x"], s["B"], s["dt"], s["g"], s["init"],
+        ssd.ssd_fwd_pass_state(s["x"], s["B"], s["dt_t"], s["g"], s["init"],
                                s["states"], s["final"], T)
         if ev is not None:
             ev[2].record(stream)
-        ssd.ssd_compute_out(s["x"], s["B"], s["C"], s["dt"], s["g"],
+        ssd.ssd_compute_out(s["x"], s["B"], s["C"], s["dt_t"], s["g"],
                             s["states"], s["D"], s["y"], T)
         if ev is not None:
             ev[3].record(stream)
@@ -195,14 +196,14 @@ def main() -> int:
     for i in range(5):
         s = sets[i % nsets]
         ssd.ssd_forward(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
-                        s["init"], s["y"], s["states"], s["final"], s["g"], T)
+                        s["init"], s["y"], s["states"], s["final"], s["ws"], T)
     torch.cuda.synchronize()
     tf = time.perf_counter()
     nfwd = max(20, args.steps // 2)
     for i in range(nfwd):
         s = sets[i % nsets]
         ssd.ssd_forward(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
-                        s["init"], s["y"], s["states"], s["final"], s["g"], T)
+                        s["init"], s["y"], s["states"], s["final"], s["ws"], T)
     torch.cuda.synchronize()
     fwd_ms = (time.perf_counter() - tf) * 1e3 / nfwd
 

@@ -38,8 +38,13 @@
  *   defines it.  Supported: P = 64; N in {64, 128}; T in {64, 128, 256};
  *   x/B/C in fp32 or bf16.  Anything else returns SSD_ERR_UNSUPPORTED.
  * - nc = ceil(seqlen / chunk_size) is the number of chunks.
- * - Element types: x, B, C share `in_dtype`; y has `y_dtype`; dt, A, D, g,
- *   states, final_state and init_state are always fp32.
+ * - Element types: x, B, C share `in_dtype`; y has `y_dtype`; dt, dt_t, A,
+ *   D, g, states, final_state and init_state are always fp32.
+ * - Stage 1 also writes dt_t, dt transposed to [b, H, L]: with g it is what
+ *   stages 2 and 3 read, so every per-head token run they load is contiguous.
+ * - Per-sequence byte extents must stay below 2 GiB:
+ *   (seqlen + chunk_size) * nheads * headdim * 4 and the same with
+ *   ngroups * dstate, else SSD_ERR_UNSUPPORTED.
  */
 #ifndef SSD_H_
 #define SSD_H_
@@ -78,22 +83,25 @@ typedef struct {
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *ssd_status_string(int status);
 
-/* Bytes of device workspace ssd_forward needs: the stage-1 output g,
- * 4 * batch * nheads * seqlen.  Returns 0 when dims is NULL or invalid. */
+/* Bytes of device workspace ssd_forward needs: the stage-1 outputs g and
+ * dt_t, 8 * batch * nheads * seqlen.  Returns 0 when dims is NULL or
+ * invalid. */
 size_t ssd_forward_workspace_bytes(const ssd_dims *dims);
 
 /*
  * Stage 1 [P1 "Kernel 1: chunk_cumsum, the Cumulative Decay Sums"]:
  *   g[b,h,t] = log2(e) * sum_{s = T*floor(t/T)}^{t} A[h] * dt[b,s,h]
  * the within-chunk inclusive cumsum of a = A dt, scaled so later stages use
- * exp2.  g is stored head-major so per-head token runs are contiguous, the
- * layout change the pages list among their optimizations [P1 "Mamba-2
- * Performance Optimizations in cuTile"; P2 "Mamba-2性能优化"].
- *   dt [b, L, H] fp32 (read)     A [H] fp32 (read)     g [b, H, L] fp32 (written)
+ * exp2.  g and a transposed copy of dt are stored head-major, [b, H, L], so
+ * per-head token runs are contiguous: the layout change the pages apply to
+ * both decay_cumsum and dt [P2 "Mamba-2性能优化", the global-memory layout
+ * item; P1 "Mamba-2 Performance Optimizations in cuTile"].
+ *   dt [b, L, H] fp32 (read)     A [H] fp32 (read)
+ *   g [b, H, L] fp32 (written)   dt_t [b, H, L] fp32 (written; dt_t[b,h,t] = dt[b,t,h])
  * Only batch, seqlen, nheads and chunk_size of `dims` are read.
  */
 ssd_status ssd_chunk_cumsum(const float *dt, const float *A, float *g,
-                            const ssd_dims *dims, void *stream);
+                            float *dt_t, const ssd_dims *dims, void *stream);
 
 /*
  * Stage 2 [P1 "Kernel 2: fwd_pass_state, Carrying the State Between Chunks";
@@ -104,11 +112,11 @@ ssd_status ssd_chunk_cumsum(const float *dt, const float *A, float *g,
  * with g_last the value of g at the chunk's last token.  final_state = S
  * after the last chunk.
  *   x [b, L, H, P] in_dtype      B [b, L, G, N] in_dtype
- *   dt [b, L, H] fp32            g [b, H, L] fp32 (from ssd_chunk_cumsum)
+ *   dt_t, g [b, H, L] fp32 (from ssd_chunk_cumsum)
  *   init_state [b, H, P, N] fp32 or NULL
  *   states [b, H, nc, P, N] fp32 (written)   final_state [b, H, P, N] or NULL
  */
-ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt,
+ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt_t,
                               const float *g, const float *init_state,
                               float *states, float *final_state, int in_dtype,
                               const ssd_dims *dims, void *stream);
@@ -122,18 +130,19 @@ ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt,
  * The masked entries are selected away, never multiplied by zero, so the
  * positive exponents above the diagonal cannot turn into NaN [P1 "Step 3"].
  * The chunk x chunk matrix never reaches memory.
- *   x, B, C as above; dt, g as above; states [b, H, nc, P, N] fp32 (read)
+ *   x, B, C as above; dt_t, g as above; states [b, H, nc, P, N] fp32 (read)
  *   D [H] fp32; y [b, L, H, P] in y_dtype (written)
  */
 ssd_status ssd_compute_out(const void *x, const void *B, const void *C,
-                           const float *dt, const float *g,
+                           const float *dt_t, const float *g,
                            const float *states, const float *D, void *y,
                            int in_dtype, int y_dtype, const ssd_dims *dims,
                            void *stream);
 
 /*
- * The whole forward [P1 "From the Math to Three Kernels"]: stage 1 into the
- * caller's workspace (at least ssd_forward_workspace_bytes(dims) bytes, else
+ * The whole forward [P1 "From the Math to Three Kernels"]: stage 1 (g, dt_t)
+ * into the caller's workspace (at least ssd_forward_workspace_bytes(dims)
+ * bytes, else
  * SSD_ERR_WORKSPACE), then stages 2 and 3, all on `stream`.  Returns y, the
  * per-chunk starting states and (if final_state != NULL) the final state,
  * which a later call can take back as init_state to continue the sequence.

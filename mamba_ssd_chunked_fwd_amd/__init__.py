@@ -59,7 +59,7 @@ def _load() -> ctypes.CDLL:
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_forward_workspace_bytes.argtypes = [dims]
     lib.ssd_forward_workspace_bytes.restype = sz
-    lib.ssd_chunk_cumsum.argtypes = [vp, vp, vp, dims, vp]
+    lib.ssd_chunk_cumsum.argtypes = [vp, vp, vp, vp, dims, vp]
     lib.ssd_chunk_cumsum.restype = i
     lib.ssd_fwd_pass_state.argtypes = [vp] * 7 + [i, dims, vp]
     lib.ssd_fwd_pass_state.restype = i
@@ -151,8 +151,9 @@ def _raise(st: int, where: str) -> None:
 
 # ------------------------------------------------------------- C-ABI entries
 def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, g: torch.Tensor,
-                     chunk_size: int) -> None:
-    """Stage 1: g [b, H, L] = log2(e) * per-chunk inclusive cumsum of A dt."""
+                     dt_t: torch.Tensor, chunk_size: int) -> None:
+    """Stage 1: g [b, H, L] = log2(e) * per-chunk inclusive cumsum of A dt,
+    and dt_t [b, H, L], dt transposed to head-major."""
     if dt.dim() != 3:
         raise ValueError("dt must be [batch, seqlen, nheads]")
     b, L, H = dt.shape
@@ -160,13 +161,15 @@ def ssd_chunk_cumsum(dt: torch.Tensor, A: torch.Tensor, g: torch.Tensor,
     _check(dt, "dt", None, f32)
     _check(A, "A", (H,), f32, dt.device)
     _check(g, "g", (b, H, L), f32, dt.device)
+    _check(dt_t, "dt_t", (b, H, L), f32, dt.device)
     # stage 1 reads only batch, seqlen, nheads and chunk_size
     d = SsdDims(b, L, H, 64, 64, 1, int(chunk_size))
-    _raise(_lib.ssd_chunk_cumsum(_ptr(dt), _ptr(A), _ptr(g), ctypes.byref(d),
-                                 _stream(dt.device)), "ssd_chunk_cumsum")
+    _raise(_lib.ssd_chunk_cumsum(_ptr(dt), _ptr(A), _ptr(g), _ptr(dt_t),
+                                 ctypes.byref(d), _stream(dt.device)),
+           "ssd_chunk_cumsum")
 
 
-def ssd_fwd_pass_state(x: torch.Tensor, B: torch.Tensor, dt: torch.Tensor,
+def ssd_fwd_pass_state(x: torch.Tensor, B: torch.Tensor, dt_t: torch.Tensor,
                        g: torch.Tensor, init_state: Optional[torch.Tensor],
                        states: torch.Tensor,
                        final_state: Optional[torch.Tensor],
@@ -178,7 +181,7 @@ def ssd_fwd_pass_state(x: torch.Tensor, B: torch.Tensor, dt: torch.Tensor,
     f32 = (torch.float32,)
     _check(x, "x", None, ins)
     _check(B, "B", (d.batch, d.seqlen, d.ngroups, d.dstate), (x.dtype,), dev)
-    _check(dt, "dt", (d.batch, d.seqlen, d.nheads), f32, dev)
+    _check(dt_t, "dt_t", (d.batch, d.nheads, d.seqlen), f32, dev)
     _check(g, "g", (d.batch, d.nheads, d.seqlen), f32, dev)
     st_shape = (d.batch, d.nheads, d.headdim, d.dstate)
     _check(init_state, "init_state", st_shape, f32, dev, optional=True)
@@ -186,13 +189,13 @@ def ssd_fwd_pass_state(x: torch.Tensor, B: torch.Tensor, dt: torch.Tensor,
                               d.dstate), f32, dev)
     _check(final_state, "final_state", st_shape, f32, dev, optional=True)
     _raise(_lib.ssd_fwd_pass_state(
-        _ptr(x), _ptr(B), _ptr(dt), _ptr(g), _ptr(init_state), _ptr(states),
+        _ptr(x), _ptr(B), _ptr(dt_t), _ptr(g), _ptr(init_state), _ptr(states),
         _ptr(final_state), _dtype_code(x.dtype), ctypes.byref(d),
         _stream(dev)), "ssd_fwd_pass_state")
 
 
 def ssd_compute_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
-                    dt: torch.Tensor, g: torch.Tensor, states: torch.Tensor,
+                    dt_t: torch.Tensor, g: torch.Tensor, states: torch.Tensor,
                     D: torch.Tensor, y: torch.Tensor, chunk_size: int) -> None:
     """Stage 3: y [b, L, H, P] from the per-chunk starting states."""
     d = make_dims(x, B, chunk_size)
@@ -203,14 +206,14 @@ def ssd_compute_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
     bc = (d.batch, d.seqlen, d.ngroups, d.dstate)
     _check(B, "B", bc, (x.dtype,), dev)
     _check(C, "C", bc, (x.dtype,), dev)
-    _check(dt, "dt", (d.batch, d.seqlen, d.nheads), f32, dev)
+    _check(dt_t, "dt_t", (d.batch, d.nheads, d.seqlen), f32, dev)
     _check(g, "g", (d.batch, d.nheads, d.seqlen), f32, dev)
     _check(states, "states", (d.batch, d.nheads, nchunks(d), d.headdim,
                               d.dstate), f32, dev)
     _check(D, "D", (d.nheads,), f32, dev)
     _check(y, "y", tuple(x.shape), ins, dev)
     _raise(_lib.ssd_compute_out(
-        _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(g), _ptr(states), _ptr(D),
+        _ptr(x), _ptr(B), _ptr(C), _ptr(dt_t), _ptr(g), _ptr(states), _ptr(D),
         _ptr(y), _dtype_code(x.dtype), _dtype_code(y.dtype), ctypes.byref(d),
         _stream(dev)), "ssd_compute_out")
 
@@ -220,7 +223,8 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
                 init_state: Optional[torch.Tensor], y: torch.Tensor,
                 states: torch.Tensor, final_state: Optional[torch.Tensor],
                 workspace: torch.Tensor, chunk_size: int) -> None:
-    """All three stages on the current stream; g lives in ``workspace``."""
+    """All three stages on the current stream; g and dt_t live in
+    ``workspace`` (``workspace_bytes`` bytes)."""
     d = make_dims(x, B, chunk_size)
     dev = x.device
     ins = (torch.float32, torch.bfloat16)

@@ -32,6 +32,12 @@ ssd_status check_dims(const ssd_dims* d, ssd::Shape* out) {
   const int64_t per_head_blocks = nc * 4 > 8 ? nc * 4 : 8;
   if (d->batch * d->nheads * per_head_blocks > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
   if (d->headdim != 64) return SSD_ERR_UNSUPPORTED;
+  // Kernels address each sequence with 32-bit byte offsets (up to one chunk
+  // past its end).
+  const int64_t span = d->seqlen + d->chunk_size;
+  if (span * d->nheads * d->headdim * 4 >= INT32_MAX ||
+      span * d->ngroups * d->dstate * 4 >= INT32_MAX)
+    return SSD_ERR_UNSUPPORTED;
   if (d->dstate != 64 && d->dstate != 128) return SSD_ERR_UNSUPPORTED;
   if (d->chunk_size != 64 && d->chunk_size != 128 && d->chunk_size != 256)
     return SSD_ERR_UNSUPPORTED;
@@ -63,12 +69,12 @@ const char* ssd_status_string(int status) {
 
 size_t ssd_forward_workspace_bytes(const ssd_dims* dims) {
   if (check_dims(dims, nullptr) != SSD_OK) return 0;
-  return sizeof(float) * (size_t)dims->batch * (size_t)dims->nheads *
+  return 2 * sizeof(float) * (size_t)dims->batch * (size_t)dims->nheads *
          (size_t)dims->seqlen;
 }
 
 ssd_status ssd_chunk_cumsum(const float* dt, const float* A, float* g,
-                            const ssd_dims* dims, void* stream) {
+                            float* dt_t, const ssd_dims* dims, void* stream) {
   if (dims == nullptr) return SSD_ERR_INVALID_ARGUMENT;
   // Stage 1 reads only batch, seqlen, nheads and chunk_size; check those with
   // a shape whose other fields are fixed to a supported value.
@@ -79,11 +85,12 @@ ssd_status ssd_chunk_cumsum(const float* dt, const float* A, float* g,
   ssd::Shape s;
   const ssd_status st = check_dims(&d1, &s);
   if (st != SSD_OK) return st;
-  if (!ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(g)) return SSD_ERR_INVALID_ARGUMENT;
-  return from_hip(ssd::launch_chunk_cumsum(dt, A, g, s, stream));
+  if (!ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(g) || !ok_ptr(dt_t))
+    return SSD_ERR_INVALID_ARGUMENT;
+  return from_hip(ssd::launch_chunk_cumsum(dt, A, g, dt_t, s, stream));
 }
 
-ssd_status ssd_fwd_pass_state(const void* x, const void* B, const float* dt,
+ssd_status ssd_fwd_pass_state(const void* x, const void* B, const float* dt_t,
                               const float* g, const float* init_state,
                               float* states, float* final_state, int in_dtype,
                               const ssd_dims* dims, void* stream) {
@@ -91,16 +98,16 @@ ssd_status ssd_fwd_pass_state(const void* x, const void* B, const float* dt,
   const ssd_status st = check_dims(dims, &s);
   if (st != SSD_OK) return st;
   if (!ok_dtype(in_dtype)) return SSD_ERR_INVALID_ARGUMENT;
-  if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(dt) || !ok_ptr(g) || !ok_ptr(states) ||
+  if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(dt_t) || !ok_ptr(g) || !ok_ptr(states) ||
       !ok_opt(init_state) || !ok_opt(final_state))
     return SSD_ERR_INVALID_ARGUMENT;
-  return from_hip(ssd::launch_fwd_pass_state(x, B, dt, g, init_state, states,
+  return from_hip(ssd::launch_fwd_pass_state(x, B, dt_t, g, init_state, states,
                                              final_state, in_dtype == SSD_BF16,
                                              s, stream));
 }
 
 ssd_status ssd_compute_out(const void* x, const void* B, const void* C,
-                           const float* dt, const float* g,
+                           const float* dt_t, const float* g,
                            const float* states, const float* D, void* y,
                            int in_dtype, int y_dtype, const ssd_dims* dims,
                            void* stream) {
@@ -108,10 +115,10 @@ ssd_status ssd_compute_out(const void* x, const void* B, const void* C,
   const ssd_status st = check_dims(dims, &s);
   if (st != SSD_OK) return st;
   if (!ok_dtype(in_dtype) || !ok_dtype(y_dtype)) return SSD_ERR_INVALID_ARGUMENT;
-  if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt) || !ok_ptr(g) ||
+  if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt_t) || !ok_ptr(g) ||
       !ok_ptr(states) || !ok_ptr(D) || !ok_ptr(y))
     return SSD_ERR_INVALID_ARGUMENT;
-  return from_hip(ssd::launch_compute_out(x, B, C, dt, g, states, D, y,
+  return from_hip(ssd::launch_compute_out(x, B, C, dt_t, g, states, D, y,
                                           in_dtype == SSD_BF16,
                                           y_dtype == SSD_BF16, s, stream));
 }
@@ -134,13 +141,14 @@ ssd_status ssd_forward(const void* x, const float* dt, const float* A,
       workspace_bytes < ssd_forward_workspace_bytes(dims))
     return SSD_ERR_WORKSPACE;
   float* g = static_cast<float*>(workspace);
+  float* dt_t = g + (size_t)s.batch * s.nheads * s.seqlen;
   const bool bf16 = in_dtype == SSD_BF16;
-  int err = ssd::launch_chunk_cumsum(dt, A, g, s, stream);
+  int err = ssd::launch_chunk_cumsum(dt, A, g, dt_t, s, stream);
   if (err == 0)
-    err = ssd::launch_fwd_pass_state(x, B, dt, g, init_state, states,
+    err = ssd::launch_fwd_pass_state(x, B, dt_t, g, init_state, states,
                                      final_state, bf16, s, stream);
   if (err == 0)
-    err = ssd::launch_compute_out(x, B, C, dt, g, states, D, y, bf16,
+    err = ssd::launch_compute_out(x, B, C, dt_t, g, states, D, y, bf16,
                                   y_dtype == SSD_BF16, s, stream);
   return from_hip(err);
 }

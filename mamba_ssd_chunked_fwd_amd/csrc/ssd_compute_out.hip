@@ -74,7 +74,7 @@ __device__ __forceinline__ OutTile decode_tile(int bid, int H, int NQ, int nc) {
 template <int T, int N, bool YBF16>
 __global__ __launch_bounds__(256) void compute_out_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
-    const uint16_t* __restrict__ Cm, const float* __restrict__ dt,
+    const uint16_t* __restrict__ Cm, const float* __restrict__ dt_t,
     const float* __restrict__ g, const float* __restrict__ states,
     const float* __restrict__ Dv, void* __restrict__ y, int L, int H, int G,
     int nc) {
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void compute_out_bf16(
     for (int t = tid; t < T; t += 256) {
       const bool ok = t < nvalid;
       gs[t] = ok ? g[(size_t)bh_idx * L + t0 + t] : 0.0f;
-      ds[t] = ok ? dt[((size_t)b * L + t0 + t) * H + h] : 0.0f;
+      ds[t] = ok ? dt_t[(size_t)bh_idx * L + t0 + t] : 0.0f;
     }
   }
 
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void compute_out_bf16(
 template <int T, int N, bool YBF16>
 __global__ __launch_bounds__(256) void compute_out_f32(
     const float* __restrict__ x, const float* __restrict__ Bm,
-    const float* __restrict__ Cm, const float* __restrict__ dt,
+    const float* __restrict__ Cm, const float* __restrict__ dt_t,
     const float* __restrict__ g, const float* __restrict__ states,
     const float* __restrict__ Dv, void* __restrict__ y, int L, int H, int G,
     int nc) {
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void compute_out_f32(
     for (int t = tid; t < T; t += 256) {
       const bool ok = t < nvalid;
       gs[t] = ok ? g[(size_t)bh_idx * L + t0 + t] : 0.0f;
-      ds[t] = ok ? dt[((size_t)b * L + t0 + t) * H + h] : 0.0f;
+      ds[t] = ok ? dt_t[(size_t)bh_idx * L + t0 + t] : 0.0f;
     }
   }
 
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void compute_out_f32(
 
 // ------------------------------------------------------------- launching
 template <bool BF16, int T, int N, bool YBF16>
-int launch_t(const void* x, const void* B, const void* C, const float* dt,
+int launch_t(const void* x, const void* B, const void* C, const float* dt_t,
              const float* g, const float* states, const float* D, void* y,
              const Shape& s, hipStream_t st) {
   const int nc = (int)s.nchunks();
@@ -366,52 +366,52 @@ int launch_t(const void* x, const void* B, const void* C, const float* dt,
   using E = typename In<BF16>::T;
   if constexpr (BF16) {
     hipLaunchKernelGGL((compute_out_bf16<T, N, YBF16>), dim3(blocks), dim3(256), 0, st,
-                       (const E*)x, (const E*)B, (const E*)C, dt, g, states, D, y, L,
+                       (const E*)x, (const E*)B, (const E*)C, dt_t, g, states, D, y, L,
                        H, G, nc);
   } else {
     hipLaunchKernelGGL((compute_out_f32<T, N, YBF16>), dim3(blocks), dim3(256), 0, st,
-                       (const E*)x, (const E*)B, (const E*)C, dt, g, states, D, y, L,
+                       (const E*)x, (const E*)B, (const E*)C, dt_t, g, states, D, y, L,
                        H, G, nc);
   }
   return (int)hipGetLastError();
 }
 
 template <bool BF16, int T, int N>
-int launch_y(const void* x, const void* B, const void* C, const float* dt,
+int launch_y(const void* x, const void* B, const void* C, const float* dt_t,
              const float* g, const float* states, const float* D, void* y,
              bool ybf16, const Shape& s, hipStream_t st) {
-  if (ybf16) return launch_t<BF16, T, N, true>(x, B, C, dt, g, states, D, y, s, st);
-  return launch_t<BF16, T, N, false>(x, B, C, dt, g, states, D, y, s, st);
+  if (ybf16) return launch_t<BF16, T, N, true>(x, B, C, dt_t, g, states, D, y, s, st);
+  return launch_t<BF16, T, N, false>(x, B, C, dt_t, g, states, D, y, s, st);
 }
 
 template <bool BF16, int T>
-int launch_n(const void* x, const void* B, const void* C, const float* dt,
+int launch_n(const void* x, const void* B, const void* C, const float* dt_t,
              const float* g, const float* states, const float* D, void* y,
              bool ybf16, const Shape& s, hipStream_t st) {
-  if (s.dstate == 64) return launch_y<BF16, T, 64>(x, B, C, dt, g, states, D, y, ybf16, s, st);
-  return launch_y<BF16, T, 128>(x, B, C, dt, g, states, D, y, ybf16, s, st);
+  if (s.dstate == 64) return launch_y<BF16, T, 64>(x, B, C, dt_t, g, states, D, y, ybf16, s, st);
+  return launch_y<BF16, T, 128>(x, B, C, dt_t, g, states, D, y, ybf16, s, st);
 }
 
 template <bool BF16>
-int launch_chunk(const void* x, const void* B, const void* C, const float* dt,
+int launch_chunk(const void* x, const void* B, const void* C, const float* dt_t,
                  const float* g, const float* states, const float* D, void* y,
                  bool ybf16, const Shape& s, hipStream_t st) {
   switch (s.chunk) {
-    case 64: return launch_n<BF16, 64>(x, B, C, dt, g, states, D, y, ybf16, s, st);
-    case 128: return launch_n<BF16, 128>(x, B, C, dt, g, states, D, y, ybf16, s, st);
-    default: return launch_n<BF16, 256>(x, B, C, dt, g, states, D, y, ybf16, s, st);
+    case 64: return launch_n<BF16, 64>(x, B, C, dt_t, g, states, D, y, ybf16, s, st);
+    case 128: return launch_n<BF16, 128>(x, B, C, dt_t, g, states, D, y, ybf16, s, st);
+    default: return launch_n<BF16, 256>(x, B, C, dt_t, g, states, D, y, ybf16, s, st);
   }
 }
 
 }  // namespace
 
 int launch_compute_out(const void* x, const void* B, const void* C,
-                       const float* dt, const float* g, const float* states,
+                       const float* dt_t, const float* g, const float* states,
                        const float* D, void* y, bool bf16_in, bool bf16_out,
                        const Shape& s, void* stream) {
   hipStream_t st = (hipStream_t)stream;
-  if (bf16_in) return launch_chunk<true>(x, B, C, dt, g, states, D, y, bf16_out, s, st);
-  return launch_chunk<false>(x, B, C, dt, g, states, D, y, bf16_out, s, st);
+  if (bf16_in) return launch_chunk<true>(x, B, C, dt_t, g, states, D, y, bf16_out, s, st);
+  return launch_chunk<false>(x, B, C, dt_t, g, states, D, y, bf16_out, s, st);
 }
 
 }  // namespace ssd

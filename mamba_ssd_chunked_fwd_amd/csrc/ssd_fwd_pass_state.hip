@@ -68,13 +68,12 @@ struct BfTileStride {
   static constexpr int value = N == 16 ? 16 : N + 16;
 };
 
-template <int T, int N, int BN, int D>
+template <int T, int N, int BN, int Q>
 __global__ __launch_bounds__(256) void state_pass_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
-    const float* __restrict__ dt, const float* __restrict__ g,
+    const float* __restrict__ dt_t, const float* __restrict__ g,
     const float* __restrict__ init, float* __restrict__ states,
     float* __restrict__ final_state, int L, int H, int G, int nc) {
-  static_assert(D >= 2, "the weights of tile k+1 come from another ring slot");
   constexpr int TK = T < 128 ? T : 128;        // tokens per tile
   constexpr int R = T / TK;                    // tiles per chunk
   constexpr int NB = BN / 16;                  // 16-column blocks per wave
@@ -86,7 +85,6 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TK * XS];
   __shared__ __attribute__((aligned(16))) uint16_t bhs[2][TK * BS];
   __shared__ __attribute__((aligned(16))) uint16_t bls[2][TK * BS];
-  __shared__ __attribute__((aligned(16))) float ws[2][TK];
 
   constexpr int NT = N / BN;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -100,14 +98,13 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
   const int ntiles = nc * R;
 
   // Buffer descriptors: reads past the sequence's last token return zero.
-  const float* gh = g + (size_t)bh_idx * L;
   const uint32_t xrow = (uint32_t)(H * kHeadDim), brow = (uint32_t)(G * N);
   const rsrc_t xr = make_rsrc(x + ((size_t)b * L * H + h) * kHeadDim,
                               ((uint32_t)(L - 1) * xrow + kHeadDim) * 2u);
   const rsrc_t br = make_rsrc(Bm + ((size_t)b * L * G + grp) * N,
                               ((uint32_t)(L - 1) * brow + N) * 2u);
-  const rsrc_t gr = make_rsrc(gh, (uint32_t)L * 4u);
-  const rsrc_t dr = make_rsrc(dt + (size_t)b * L * H + h, ((uint32_t)(L - 1) * H + 1) * 4u);
+  const rsrc_t gr = make_rsrc(g + (size_t)bh_idx * L, (uint32_t)L * 4u);
+  const rsrc_t dr = make_rsrc(dt_t + (size_t)bh_idx * L, (uint32_t)L * 4u);
 
   // State slice: acc[nb] holds S[p][n0 + 16nb + 4lq + 0..3].
   f32x4 acc[NB];
@@ -115,14 +112,13 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
     acc[nb] = init ? *(const f32x4*)(init + sbase + 16 * nb) : (f32x4){0, 0, 0, 0};
-  // Let the initial state land before the tile ring starts, so waits inside
-  // the loop only ever concern ring loads.
+  // Let the initial state land before the pipeline starts, so waits inside
+  // the loop only ever concern tile loads.
   __builtin_amdgcn_s_waitcnt(0);
 
   // Per-thread byte offsets (within a tile) of each staging unit; idle B
-  // units point past the range, so every thread issues the same loads
-  // (straight-line code keeps the compiler's memory-wait counts exact).
-  uint32_t xoff[XU], boff[BU];
+  // units point past the range, so every thread issues the same loads.
+  uint32_t xoff[XU], boff[BU], toff[BU];
   int xlds[XU], blds[BU];
 #pragma unroll
   for (int i = 0; i < XU; ++i) {
@@ -135,53 +131,49 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
   for (int i = 0; i < BU; ++i) {
     const int u = tid + 256 * i;
     const int t = u / (BN / 8), c8 = u % (BN / 8);
-    boff[i] = u < kBUnits ? ((uint32_t)t * brow + n0 + 8 * c8) * 2u : kPastRange;
+    const bool on = u < kBUnits;
+    boff[i] = on ? ((uint32_t)t * brow + n0 + 8 * c8) * 2u : kPastRange;
+    toff[i] = on ? (uint32_t)t : kPastRange / 4;   // token of the unit
     blds[i] = t * BS + 8 * c8;
   }
   const uint32_t xstep = xrow * 2u, bstep = brow * 2u;   // bytes per token
 
-  struct Slot {
-    u32x4 x[XU];           // one token x 8 p's
-    u32x4 b[BU];           // one token x 8 n's
-    float g, dt, glast;
+  // Raw global data of one tile: X rows, B rows, and each B unit's token's
+  // g and dt together with g at the chunk's last token.
+  struct Tile {
+    u32x4 x[XU];
+    u32x4 b[BU];
+    float g[BU], dt[BU];
+    float glast;
   };
-  Slot ring[D];
 
-  // Global loads of tile k (tokens [k*TK, k*TK + TK) of the sequence).
-  auto issue = [&](int k, Slot& sl) {
+  auto issue = [&](int k, Tile& tl) {
     const int c = k / R;
     const uint32_t t0 = (uint32_t)(k * TK);
 #pragma unroll
-    for (int i = 0; i < XU; ++i) sl.x[i] = load_b128(xr, xoff[i] + t0 * xstep);
-#pragma unroll
-    for (int i = 0; i < BU; ++i) sl.b[i] = load_b128(br, boff[i] + t0 * bstep);
-    sl.g = load_f32(gr, (t0 + tid) * 4u);
-    sl.dt = load_f32(dr, (t0 + tid) * (uint32_t)H * 4u);
-    // g at the chunk's last token: a vector load, so nothing waits for it here
-    sl.glast = load_f32(gr, (uint32_t)(min(c * T + T, L) - 1) * 4u);
-  };
-
-  // Per-token weights of tile k and its chunk's total decay 2^{g_last}.
-  // Tokens past the end read dt = g = 0, so their weight is exactly 0.
-  auto commit_w = [&](int k, const Slot& sl, float& decay) {
-    if (tid < TK) ws[k & 1][tid] = sl.dt * exp2_hw(sl.glast - sl.g);
-    decay = exp2_hw(sl.glast);
-  };
-
-  // X (as loaded) and the split w o B of tile k into LDS buffer k & 1.
-  auto commit_xb = [&](int k, const Slot& sl) {
-    const int buf = k & 1;
-#pragma unroll
-    for (int i = 0; i < XU; ++i) *(u32x4*)(xs[buf] + xlds[i]) = sl.x[i];
+    for (int i = 0; i < XU; ++i) tl.x[i] = load_b128(xr, xoff[i] + t0 * xstep);
 #pragma unroll
     for (int i = 0; i < BU; ++i) {
-      const int u = tid + 256 * i;
-      if (u < kBUnits) {
-        const float w = ws[buf][u / (BN / 8)];
+      tl.b[i] = load_b128(br, boff[i] + t0 * bstep);
+      tl.g[i] = load_f32(gr, (t0 + toff[i]) * 4u);
+      tl.dt[i] = load_f32(dr, (t0 + toff[i]) * 4u);
+    }
+    tl.glast = load_f32(gr, (uint32_t)(min(c * T + T, L) - 1) * 4u);
+  };
+
+  // X (as loaded) and the split w o B of a tile into LDS buffer `buf`.
+  // w_t = dt_t 2^{g_last - g_t}; tokens past the end read dt = g = 0 -> 0.
+  auto commit = [&](int buf, const Tile& tl) {
+#pragma unroll
+    for (int i = 0; i < XU; ++i) *(u32x4*)(xs[buf] + xlds[i]) = tl.x[i];
+#pragma unroll
+    for (int i = 0; i < BU; ++i) {
+      if (tid + 256 * i < kBUnits) {
+        const float w = tl.dt[i] * exp2_hw(tl.glast - tl.g[i]);
         uint32_t hv[4], lv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          split_bf16(bf16_lo(sl.b[i][e]) * w, bf16_hi(sl.b[i][e]) * w, hv[e], lv[e]);
+          split_bf16(bf16_lo(tl.b[i][e]) * w, bf16_hi(tl.b[i][e]) * w, hv[e], lv[e]);
         *(u32x4*)(bhs[buf] + blds[i]) = make_u32x4(hv);
         *(u32x4*)(bls[buf] + blds[i]) = make_u32x4(lv);
       }
@@ -193,60 +185,80 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
   const int xrd = rsel * XS + 16 * wave + csel;
   const int brd = rsel * BS + csel;
 
-  // Tiles past the end are issued too: their loads fall outside every
-  // buffer range, cost no memory traffic and keep the wait counts exact.
-#pragma unroll
-  for (int s = 0; s < D; ++s) issue(s, ring[s]);
-  float decay_cur = 1.0f, decay_next = 1.0f;
-  commit_w(0, ring[0], decay_cur);
-  __syncthreads();
-
   f32x4 ph[NB], pl[NB];
-  for (int k0 = 0; k0 < ntiles; k0 += D) {
+  // One step of the sequential pass for tile k: the state store at a chunk
+  // start, tile k's matrix products from LDS buffer k & 1, the staging of
+  // tile k + 1 into the other buffer (independent of the products, so the
+  // two overlap), the state update S = 2^{g_last} S + P at a chunk end, and
+  // one barrier.
+  auto step = [&](int k, const Tile& cur, const Tile& next) {
+    const int sub = k % R;
+    if (sub == 0) {
+      float* dst = states + ((size_t)bh_idx * nc + k / R) * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
-      const int k = k0 + s;
-      if (k >= ntiles) break;
-      const int sub = k % R;
-      if (sub == 0) {
-        // The state entering chunk k / R.
-        float* dst = states + ((size_t)bh_idx * nc + k / R) * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          *(f32x4*)(dst + 16 * nb) = acc[nb];
-          ph[nb] = pl[nb] = (f32x4){0, 0, 0, 0};
-        }
+      for (int nb = 0; nb < NB; ++nb) {
+        *(f32x4*)(dst + 16 * nb) = acc[nb];
+        ph[nb] = pl[nb] = (f32x4){0, 0, 0, 0};
       }
-      commit_xb(k, ring[s]);
-      float dnext = decay_next;
-      if (k + 1 < ntiles) commit_w(k + 1, ring[(s + 1) % D], dnext);
-      issue(k + D, ring[s]);
-      __syncthreads();
-
-      const uint16_t* xt = xs[k & 1];
-      const uint16_t* bht = bhs[k & 1];
-      const uint16_t* blt = bls[k & 1];
-#pragma unroll
-      for (int kk = 0; kk < TK / 32; ++kk) {
-        const u32x2 x0 = lds_read_tr16(xt + xrd + 32 * kk * XS);
-        const u32x2 x1 = lds_read_tr16(xt + xrd + (32 * kk + 16) * XS);
-        const u32x4 xv = {x0[0], x0[1], x1[0], x1[1]};
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int o0 = brd + 32 * kk * BS + 16 * nb, o1 = o0 + 16 * BS;
-          const u32x2 h0 = lds_read_tr16(bht + o0), h1 = lds_read_tr16(bht + o1);
-          const u32x2 l0 = lds_read_tr16(blt + o0), l1 = lds_read_tr16(blt + o1);
-          ph[nb] = mfma_bf16((u32x4){h0[0], h0[1], h1[0], h1[1]}, xv, ph[nb]);
-          pl[nb] = mfma_bf16((u32x4){l0[0], l0[1], l1[0], l1[1]}, xv, pl[nb]);
-        }
-      }
-      if (sub == R - 1) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = decay_cur * acc[nb] + (ph[nb] + pl[nb]);
-      }
-      if (k + 1 < ntiles && (k + 1) % R == 0) decay_cur = dnext;
-      decay_next = dnext;
     }
+    const int buf = k & 1;
+    const uint16_t* xt = xs[buf];
+    const uint16_t* bht = bhs[buf];
+    const uint16_t* blt = bls[buf];
+#pragma unroll
+    for (int kk = 0; kk < TK / 32; ++kk) {
+      const u32x2 x0 = lds_read_tr16(xt + xrd + 32 * kk * XS);
+      const u32x2 x1 = lds_read_tr16(xt + xrd + (32 * kk + 16) * XS);
+      const u32x4 xv = {x0[0], x0[1], x1[0], x1[1]};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int o0 = brd + 32 * kk * BS + 16 * nb, o1 = o0 + 16 * BS;
+        const u32x2 h0 = lds_read_tr16(bht + o0), h1 = lds_read_tr16(bht + o1);
+        const u32x2 l0 = lds_read_tr16(blt + o0), l1 = lds_read_tr16(blt + o1);
+        ph[nb] = mfma_bf16((u32x4){h0[0], h0[1], h1[0], h1[1]}, xv, ph[nb]);
+        pl[nb] = mfma_bf16((u32x4){l0[0], l0[1], l1[0], l1[1]}, xv, pl[nb]);
+      }
+    }
+    if (k + 1 < ntiles) commit(buf ^ 1, next);
+    if (sub == R - 1) {
+      const float decay = exp2_hw(cur.glast);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = decay * acc[nb] + (ph[nb] + pl[nb]);
+    }
+    __syncthreads();
+  };
+
+  // Two groups of Q tiles: one group is consumed while the other group's
+  // loads are in flight, then the roles swap.  Within one pass of the loop
+  // body the code is straight-line, so the compiler's memory-wait counts let
+  // the other group's loads stay outstanding; scheduling barriers pin each
+  // group's loads in place so they are issued in the same order on every
+  // path into the loop.  Tiles past the end are issued too (their loads fall
+  // outside every range and cost nothing).
+  Tile ga[Q], gb[Q];
+#pragma unroll
+  for (int q = 0; q < Q; ++q) issue(q, ga[q]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < Q; ++q) issue(Q + q, gb[q]);
+  __builtin_amdgcn_sched_barrier(0);
+  commit(0, ga[0]);
+  __syncthreads();
+  for (int k0 = 0; k0 < ntiles; k0 += 2 * Q) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (k0 + q < ntiles) step(k0 + q, ga[q], q + 1 < Q ? ga[q + 1] : gb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) issue(k0 + 2 * Q + q, ga[q]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (k0 + Q + q < ntiles) step(k0 + Q + q, gb[q], q + 1 < Q ? gb[q + 1] : ga[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) issue(k0 + 3 * Q + q, gb[q]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (final_state) {
 #pragma unroll
@@ -261,7 +273,7 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
 template <int T, int N, int BN, int D>
 __global__ __launch_bounds__(256) void state_pass_f32(
     const float* __restrict__ x, const float* __restrict__ Bm,
-    const float* __restrict__ dt, const float* __restrict__ g,
+    const float* __restrict__ dt_t, const float* __restrict__ g,
     const float* __restrict__ init, float* __restrict__ states,
     float* __restrict__ final_state, int L, int H, int G, int nc) {
   static_assert(D >= 2, "the weights of tile k+1 come from another ring slot");
@@ -294,7 +306,7 @@ __global__ __launch_bounds__(256) void state_pass_f32(
   const rsrc_t br = make_rsrc(Bm + ((size_t)b * L * G + grp) * N,
                               ((uint32_t)(L - 1) * brow + N) * 4u);
   const rsrc_t gr = make_rsrc(gh, (uint32_t)L * 4u);
-  const rsrc_t dr = make_rsrc(dt + (size_t)b * L * H + h, ((uint32_t)(L - 1) * H + 1) * 4u);
+  const rsrc_t dr = make_rsrc(dt_t + (size_t)bh_idx * L, (uint32_t)L * 4u);
 
   f32x4 acc[NB];
   const size_t sbase = (size_t)bh_idx * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
@@ -341,7 +353,7 @@ __global__ __launch_bounds__(256) void state_pass_f32(
       for (int r = 0; r < 4; ++r) sl.b[i][r] = load_f32x4(br, boff[i] + (t0 + r) * bstep);
     }
     sl.g = load_f32(gr, (t0 + tid) * 4u);
-    sl.dt = load_f32(dr, (t0 + tid) * (uint32_t)H * 4u);
+    sl.dt = load_f32(dr, (t0 + tid) * 4u);
     sl.glast = load_f32(gr, (uint32_t)(min(c * T + T, L) - 1) * 4u);
   };
 
@@ -441,15 +453,16 @@ int choose_bn(const Shape& s) {
   return 16;
 }
 
-// Ring depth: token tiles in flight per workgroup, bounded by register use.
+// Pipeline depth: for bf16, tiles per group (two groups in flight); for fp32,
+// the register ring depth.  Bounded by register use.
 template <bool BF16, int T, int BN>
 constexpr int ring_depth() {
-  if constexpr (BF16) return (T >= 128 && BN >= 32) ? 2 : 4;
+  if constexpr (BF16) return (T >= 128 && BN >= 32) ? 1 : 2;
   else return BN >= 32 ? 2 : 4;
 }
 
 template <bool BF16, int T, int N, int BN>
-int launch_t(const void* x, const void* B, const float* dt, const float* g,
+int launch_t(const void* x, const void* B, const float* dt_t, const float* g,
              const float* init, float* states, float* fin, const Shape& s,
              hipStream_t st) {
   constexpr int D = ring_depth<BF16, T, BN>();
@@ -458,56 +471,56 @@ int launch_t(const void* x, const void* B, const float* dt, const float* g,
             nc = (int)s.nchunks();
   if constexpr (BF16) {
     hipLaunchKernelGGL((state_pass_bf16<T, N, BN, D>), dim3(blocks), dim3(256), 0, st,
-                       (const uint16_t*)x, (const uint16_t*)B, dt, g, init, states,
+                       (const uint16_t*)x, (const uint16_t*)B, dt_t, g, init, states,
                        fin, L, H, G, nc);
   } else {
     hipLaunchKernelGGL((state_pass_f32<T, N, BN, D>), dim3(blocks), dim3(256), 0, st,
-                       (const float*)x, (const float*)B, dt, g, init, states, fin,
+                       (const float*)x, (const float*)B, dt_t, g, init, states, fin,
                        L, H, G, nc);
   }
   return (int)hipGetLastError();
 }
 
 template <bool BF16, int T, int N>
-int launch_bn(const void* x, const void* B, const float* dt, const float* g,
+int launch_bn(const void* x, const void* B, const float* dt_t, const float* g,
               const float* init, float* states, float* fin, const Shape& s,
               hipStream_t st) {
   switch (choose_bn(s)) {
-    case 64: return launch_t<BF16, T, N, 64>(x, B, dt, g, init, states, fin, s, st);
-    case 32: return launch_t<BF16, T, N, 32>(x, B, dt, g, init, states, fin, s, st);
-    default: return launch_t<BF16, T, N, 16>(x, B, dt, g, init, states, fin, s, st);
+    case 64: return launch_t<BF16, T, N, 64>(x, B, dt_t, g, init, states, fin, s, st);
+    case 32: return launch_t<BF16, T, N, 32>(x, B, dt_t, g, init, states, fin, s, st);
+    default: return launch_t<BF16, T, N, 16>(x, B, dt_t, g, init, states, fin, s, st);
   }
 }
 
 template <bool BF16, int T>
-int launch_n(const void* x, const void* B, const float* dt, const float* g,
+int launch_n(const void* x, const void* B, const float* dt_t, const float* g,
              const float* init, float* states, float* fin, const Shape& s,
              hipStream_t st) {
-  if (s.dstate == 64) return launch_bn<BF16, T, 64>(x, B, dt, g, init, states, fin, s, st);
-  return launch_bn<BF16, T, 128>(x, B, dt, g, init, states, fin, s, st);
+  if (s.dstate == 64) return launch_bn<BF16, T, 64>(x, B, dt_t, g, init, states, fin, s, st);
+  return launch_bn<BF16, T, 128>(x, B, dt_t, g, init, states, fin, s, st);
 }
 
 template <bool BF16>
-int launch_chunk(const void* x, const void* B, const float* dt, const float* g,
+int launch_chunk(const void* x, const void* B, const float* dt_t, const float* g,
                  const float* init, float* states, float* fin, const Shape& s,
                  hipStream_t st) {
   switch (s.chunk) {
-    case 64: return launch_n<BF16, 64>(x, B, dt, g, init, states, fin, s, st);
-    case 128: return launch_n<BF16, 128>(x, B, dt, g, init, states, fin, s, st);
-    default: return launch_n<BF16, 256>(x, B, dt, g, init, states, fin, s, st);
+    case 64: return launch_n<BF16, 64>(x, B, dt_t, g, init, states, fin, s, st);
+    case 128: return launch_n<BF16, 128>(x, B, dt_t, g, init, states, fin, s, st);
+    default: return launch_n<BF16, 256>(x, B, dt_t, g, init, states, fin, s, st);
   }
 }
 
 }  // namespace
 
-int launch_fwd_pass_state(const void* x, const void* B, const float* dt,
+int launch_fwd_pass_state(const void* x, const void* B, const float* dt_t,
                           const float* g, const float* init_state,
                           float* states, float* final_state, bool bf16_in,
                           const Shape& s, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (bf16_in)
-    return launch_chunk<true>(x, B, dt, g, init_state, states, final_state, s, st);
-  return launch_chunk<false>(x, B, dt, g, init_state, states, final_state, s, st);
+    return launch_chunk<true>(x, B, dt_t, g, init_state, states, final_state, s, st);
+  return launch_chunk<false>(x, B, dt_t, g, init_state, states, final_state, s, st);
 }
 
 }  // namespace ssd

@@ -14,15 +14,15 @@ struct Shape {
 };
 
 int launch_chunk_cumsum(const float* dt, const float* A, float* g,
-                        const Shape& s, void* stream);
+                        float* dt_t, const Shape& s, void* stream);
 
-int launch_fwd_pass_state(const void* x, const void* B, const float* dt,
+int launch_fwd_pass_state(const void* x, const void* B, const float* dt_t,
                           const float* g, const float* init_state,
                           float* states, float* final_state, bool bf16_in,
                           const Shape& s, void* stream);
 
 int launch_compute_out(const void* x, const void* B, const void* C,
-                       const float* dt, const float* g, const float* states,
+                       const float* dt_t, const float* g, const float* states,
                        const float* D, void* y, bool bf16_in, bool bf16_out,
                        const Shape& s, void* stream);
 

@@ -2,11 +2,21 @@
 
 Every call below fails argument validation, which the library performs on the
 host before any HIP call, so nothing is launched and no pointer is touched.
+The calls pass fake device addresses, so the module refuses to run where a
+GPU is visible: a mistaken case there could launch a kernel on them.
 """
 import ctypes
 import subprocess
 
 import pytest
+
+try:
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only validation tests use fake device pointers; "
+                    "not run where a GPU is visible", allow_module_level=True)
+except ImportError:  # pragma: no cover
+    pass
 
 import mamba_ssd_chunked_fwd_amd as ssd
 from mamba_ssd_chunked_fwd_amd import SsdDims
@@ -49,8 +59,8 @@ def test_status_strings():
 
 def test_workspace_bytes():
     d = dims()
-    assert ssd.workspace_bytes(d) == 4 * 2 * 4 * 256
-    assert ssd.workspace_bytes(dims(seqlen=1000, chunk_size=256)) == 4 * 2 * 4 * 1000
+    assert ssd.workspace_bytes(d) == 8 * 2 * 4 * 256
+    assert ssd.workspace_bytes(dims(seqlen=1000, chunk_size=256)) == 8 * 2 * 4 * 1000
     assert ssd.workspace_bytes(dims(headdim=32)) == 0
     assert ssd.workspace_bytes(dims(nheads=5)) == 0
     assert lib.ssd_forward_workspace_bytes(None) == 0
@@ -77,6 +87,7 @@ def _fwd(d, **over):
     ("dstate", 256, UNS), ("dstate", 16, UNS),
     ("chunk_size", 32, UNS), ("chunk_size", 100, UNS),
     ("seqlen", 1 << 40, INV),
+    ("seqlen", 1 << 22, UNS),                # per-sequence extent >= 2 GiB
 ])
 def test_forward_rejects_bad_dims(field, value, expect):
     assert _fwd(dims(**{field: value})) == expect
@@ -104,12 +115,13 @@ def test_forward_rejects_small_workspace():
 
 def test_stage_entry_points_validate():
     d = dims()
-    assert lib.ssd_chunk_cumsum(None, FAKE, FAKE, ctypes.byref(d), None) == INV
-    assert lib.ssd_chunk_cumsum(FAKE, FAKE, FAKE, None, None) == INV
-    assert lib.ssd_chunk_cumsum(FAKE, FAKE, FAKE,
+    assert lib.ssd_chunk_cumsum(None, FAKE, FAKE, FAKE, ctypes.byref(d), None) == INV
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, FAKE, None, ctypes.byref(d), None) == INV
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, FAKE, FAKE, None, None) == INV
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, FAKE, FAKE,
                                 ctypes.byref(dims(chunk_size=48)), None) == UNS
     # stage 1 ignores P, N and G
-    assert lib.ssd_chunk_cumsum(FAKE, FAKE, MISALIGNED,
+    assert lib.ssd_chunk_cumsum(FAKE, FAKE, MISALIGNED, FAKE,
                                 ctypes.byref(dims(headdim=7)), None) == INV
     assert lib.ssd_fwd_pass_state(FAKE, FAKE, FAKE, FAKE, None, None, None,
                                   ssd.SSD_BF16, ctypes.byref(d), None) == INV

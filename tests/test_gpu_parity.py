@@ -77,17 +77,20 @@ def test_small_stages(ssd, w):
     dev = device_inputs(inp, w.dtype)
     b, L, H = w.batch, w.seqlen, w.nheads
     nc = w.nchunks
-    # stage 1 against the oracle's cumsum, within the fp32 rounding bound
+    # stage 1 against the oracle's cumsum, within the fp32 rounding bound;
+    # its transposed dt copy is exact
     g = torch.empty(b, H, L, device=DEV)
-    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, T)
+    dt_t = torch.empty(b, H, L, device=DEV)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, dt_t, T)
     torch.cuda.synchronize()
     g_ref = oracle.chunk_cumsum(inp["dt"], inp["A"], T)
     err = np.abs(_np(g) - g_ref)
     assert np.all(err <= g_tolerance(g_ref, T)), float(err.max())
+    assert np.array_equal(_np(dt_t), inp["dt"].transpose(0, 2, 1))
     # stage 2 (fed the GPU g) against the recurrence's chunk states
     states = torch.empty(b, H, nc, 64, w.dstate, device=DEV)
     final = torch.empty(b, H, 64, w.dstate, device=DEV)
-    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dev["dt"], g, dev["init_state"],
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dt_t, g, dev["init_state"],
                            states, final, T)
     torch.cuda.synchronize()
     ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
@@ -98,7 +101,7 @@ def test_small_stages(ssd, w):
     # chunk outputs from those same fp32 states
     st32 = ref["states"].astype(np.float32)
     y = torch.empty(tuple(dev["x"].shape), dtype=torch.float32, device=DEV)
-    ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dev["dt"], g,
+    ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dt_t, g,
                         torch.from_numpy(st32).to(DEV), dev["D"], y, T)
     torch.cuda.synchronize()
     y_ref = oracle.chunk_out(inp["x"], inp["dt"], inp["A"], inp["B"],
@@ -114,7 +117,8 @@ def test_cumsum_exact_inputs(ssd):
     dt = (2.0 ** rng.integers(-6, 2, size=(b, L, H))).astype(np.float32)
     A = -np.ones(H, np.float32)
     g = torch.empty(b, H, L, device=DEV)
-    ssd.ssd_chunk_cumsum(torch.from_numpy(dt).to(DEV), torch.from_numpy(A).to(DEV), g, T)
+    dt_t = torch.empty(b, H, L, device=DEV)
+    ssd.ssd_chunk_cumsum(torch.from_numpy(dt).to(DEV), torch.from_numpy(A).to(DEV), g, dt_t, T)
     torch.cuda.synchronize()
     g_ref = oracle.chunk_cumsum(dt, A, T)
     err = np.abs(_np(g) - g_ref)
@@ -273,12 +277,13 @@ def test_forward_equals_stage_calls(ssd):
     y, states, final = _run_forward(ssd, dev, T)
     b, L, H = w.batch, w.seqlen, w.nheads
     g = torch.empty(b, H, L, device=DEV)
+    dt_t = torch.empty(b, H, L, device=DEV)
     s2 = torch.empty_like(states)
     f2 = torch.empty_like(final)
     y2 = torch.empty_like(y)
-    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, T)
-    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dev["dt"], g, dev["init_state"], s2, f2, T)
-    ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dev["dt"], g, s2, dev["D"], y2, T)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, dt_t, T)
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dt_t, g, dev["init_state"], s2, f2, T)
+    ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dt_t, g, s2, dev["D"], y2, T)
     torch.cuda.synchronize()
     assert torch.equal(s2, states) and torch.equal(f2, final) and torch.equal(y2, y)
 
