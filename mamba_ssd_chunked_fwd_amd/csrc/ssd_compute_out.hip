@@ -13,38 +13,41 @@
 // positive exponents there cannot produce Inf * 0 = NaN.
 //
 // MI355X design.
-// * One workgroup (4 waves) per (b, c, 64-row tile q of the chunk, h); wave
-//   w owns the 16 query rows i in block ib = 4q + w and all 64 columns p of
-//   y, computed transposed (Y^T[p][i]) so each lane's accumulators are four
-//   consecutive p of one token: 16-byte stores of y.
-// * C B^T is computed transposed as well (B C^T, rows j, columns i), only for
-//   16x16 blocks on or below the diagonal.  In that accumulator layout a lane
-//   holds, for its query column i, exactly the eight j values the next
-//   product's operand needs, so L'^T goes from accumulator to matrix operand
-//   with no data movement: the decay, dt_j, the causal select and the D_h
-//   skip term (folded onto the diagonal, L'[i,i] += D_h) are applied in
-//   registers.
-// * X is staged in LDS token-contiguous ([p][j]) for the L' X product; the
-//   state S_c is staged in LDS row-major.  The C fragments of a wave's rows
-//   are the B operand of both C S^T and B C^T and are loaded once.
+// * Persistent workgroups.  The work items are the (b, c, h) triples, h
+//   fastest; the grid holds as many workgroups as fit on the chip at once
+//   and each takes one contiguous run of items, so every workgroup does the
+//   same amount of work and runs of heads share one chunk.  Consecutive runs
+//   are placed on the same XCD (blocks are dealt to the 8 XCDs round-robin).
+// * Software pipeline across items: while item k is computed from LDS, the
+//   x tile, state, g and dt of item k+1 are already in flight into
+//   registers.  C B^T and the C fragments depend only on (b, c, group), so
+//   they are formed once and reused for every head of the group in the run
+//   (the pages compute C B^T once per group as well).
+// * One workgroup covers the whole chunk.  Wave w owns query-row blocks
+//   (16 rows each) w and, for chunks of 128 and 256 tokens, NIB-1-w, so
+//   every wave has the same share of the causal triangle.  Y is computed
+//   transposed (Y^T[p][i]) so each lane's accumulators are four consecutive
+//   p of one token: 16-byte stores of y.
+// * C B^T is computed transposed (B C^T, rows j, columns i), only for 16x16
+//   blocks on or below the diagonal.  In that accumulator layout a lane
+//   holds, for its query column i, exactly the j values the next product's
+//   operand needs, so L'^T goes from accumulator to matrix operand with no
+//   data movement: the decay, dt_j, the causal select and the D_h skip term
+//   (folded onto the diagonal, L'[i,i] += D_h) are applied in registers.
 // * bf16 inputs: C, B and X are exact bf16 operands; S_c and L' are computed
-//   fp32 values and are split into bf16 hi + lo (two MFMAs each).  fp32
-//   inputs use the fp32 matrix instruction.
-// HBM traffic per (b, h, chunk): x, C and B tiles, dt and g, the state
-// S_c (4*64*N) and y; the stage is HBM-bound at every supported shape by
-// algorithmic count.
+//   fp32 values, split into bf16 hi + lo (two matrix instructions each).
+//   X is staged row-major in LDS and read with the LDS transpose read.
+//   fp32 inputs use the fp32 matrix instruction with X staged transposed.
+// HBM traffic per item: the x tile, the state S_c (4*64*N bytes), dt, g and
+// y; B and C once per (b, c, group) run.  The stage is HBM-bound at every
+// supported shape by algorithmic count.
+#include <atomic>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 namespace {
-
-template <bool BF16>
-struct In;
-template <>
-struct In<true> { using T = uint16_t; };
-template <>
-struct In<false> { using T = float; };
 
 template <bool YBF16>
 __device__ __forceinline__ void store_y(void* y, size_t off, f32x4 v) {
@@ -55,323 +58,483 @@ __device__ __forceinline__ void store_y(void* y, size_t off, f32x4 v) {
   }
 }
 
-// Decode the flat block id: h fastest, then the row tile, chunk and batch.
-struct OutTile {
-  int h, q, c, b;
+// Geometry shared by both element types.
+template <int T>
+struct Geo {
+  static constexpr int NIB = T / 16;             // 16-token blocks per chunk
+  static constexpr int NW = T == 256 ? 8 : 4;    // waves per workgroup
+  static constexpr int NTHR = 64 * NW;
+  static constexpr int MB = NIB / NW;            // query-row blocks per wave
+  static_assert(MB == 1 || MB == 2, "one or two row blocks per wave");
 };
-__device__ __forceinline__ OutTile decode_tile(int bid, int H, int NQ, int nc) {
-  OutTile t;
-  t.h = bid % H;
-  bid /= H;
-  t.q = bid % NQ;
-  bid /= NQ;
-  t.c = bid % nc;
-  t.b = bid / nc;
-  return t;
+
+// Row block of slot m (0 or 1) of wave w: w and NIB-1-w.
+template <int T>
+__device__ __forceinline__ int row_block(int w, int m) {
+  return m == 0 ? w : Geo<T>::NIB - 1 - w;
+}
+
+struct Item {
+  int b, c, h, grp;
+};
+__device__ __forceinline__ Item decode_item(int k, int H, int nc, int hpg) {
+  Item it;
+  it.h = k % H;
+  k /= H;
+  it.c = k % nc;
+  it.b = k / nc;
+  it.grp = it.h / hpg;
+  return it;
+}
+
+// This workgroup's contiguous run of items [k0, k1).
+__device__ __forceinline__ void item_range(int items, int& k0, int& k1) {
+  const int nwg = gridDim.x;
+  int wg = blockIdx.x;
+  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  k0 = (int)((int64_t)wg * items / nwg);
+  k1 = (int)((int64_t)(wg + 1) * items / nwg);
 }
 
 // ---------------------------------------------------------------- bf16 path
+// cb entries: row slot 0 keeps its blocks 0..ib0 at entries 0..ib0; row slot
+// 1 keeps block k at entry NE-1-k.  Each row's block count is padded to
+// even (the 32-token k-step covers two blocks), padding entries stay zero;
+// with ib0 + ib1 = NIB - 1 the two padded counts add up to NIB + 2.
 template <int T, int N, bool YBF16>
-__global__ __launch_bounds__(256) void compute_out_bf16(
+__global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const uint16_t* __restrict__ Cm, const float* __restrict__ dt_t,
     const float* __restrict__ g, const float* __restrict__ states,
     const float* __restrict__ Dv, void* __restrict__ y, int L, int H, int G,
-    int nc) {
-  constexpr int NQ = T / 64;
-  constexpr int XS = T + 8;   // xT row stride (bf16)
-  constexpr int SS = N + 8;   // state row stride (bf16)
-  constexpr int KN = N / 32;  // k-steps over the state index
-  constexpr int NJB = T / 16; // 16-token blocks per chunk
-  __shared__ __attribute__((aligned(16))) uint16_t xT[64 * XS];
+    int nc, int items) {
+  using Gm = Geo<T>;
+  constexpr int NTHR = Gm::NTHR, MB = Gm::MB, NIB = Gm::NIB;
+  constexpr int KN = N / 32;            // k-steps over the state index
+  constexpr int XS = 80;                // X tile row stride (bf16), 64 + 16
+  constexpr int SS = N + 8;             // state-half row stride (bf16)
+  constexpr int XU = T * 8 / NTHR;      // 16-byte x units per thread
+  constexpr int SU = 16 * N / NTHR;     // 16-byte state units per thread
+  constexpr int NE = MB == 1 ? NIB : NIB + 2;
+  static_assert(XU >= 1 && SU >= 1 && 2 * T <= NTHR, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[T * XS];
   __shared__ __attribute__((aligned(16))) uint16_t sh[64 * SS];
   __shared__ __attribute__((aligned(16))) uint16_t sl[64 * SS];
   __shared__ float gs[T], ds[T];
 
-  const OutTile tile = decode_tile(blockIdx.x, H, NQ, nc);
-  const int h = tile.h, q = tile.q, c = tile.c, b = tile.b;
-  const int grp = h / (H / G);
-  const int t0 = c * T;
-  const int nvalid = min(T, L - t0);
-  const int bh_idx = b * H + h;
+  int k0, k1;
+  item_range(items, k0, k1);
+  if (k0 >= k1) return;
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
-  const int ib = 4 * q + wave;
-  const int i = 16 * ib + lr;          // this lane's query token in the chunk
+  const int hpg = H / G;
+  const uint32_t xbytes = (uint32_t)L * H * kHeadDim * 2;
+  const uint32_t bcbytes = (uint32_t)L * G * N * 2;
+  const rsrc_t drs = make_rsrc(Dv, (uint32_t)H * 4);
 
-  // ---- stage X^T (tokens [0, 64(q+1))), the state split, g and dt in LDS
-  {
-    const int pp = tid & 31, xtb = tid >> 5;
-    for (int it = 0; it <= q; ++it) {
-      uint32_t xr[8];
+  // ---- per-item operands, prefetched into registers
+  struct Regs {
+    u32x4 x[XU];
+    f32x4 s[SU];
+    float gd, dh;
+  } r;
+  auto issue = [&](int k) {
+    const Item it = decode_item(k, H, nc, hpg);
+    const rsrc_t xr = make_rsrc(x + (size_t)it.b * L * H * kHeadDim, xbytes);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int t = 8 * (xtb + 8 * it) + r;
-        xr[r] = t < nvalid
-            ? *(const uint32_t*)(x + (((size_t)b * L + t0 + t) * H + h) * kHeadDim + 2 * pp)
-            : 0u;
-      }
-      u32x4 lo, hi;
+    for (int u = 0; u < XU; ++u) {
+      const int e = tid + NTHR * u, row = e >> 3, c8 = e & 7;
+      r.x[u] = load_b128(xr, ((uint32_t)(it.c * T + row) * H + it.h) * (kHeadDim * 2) + 16 * c8);
+    }
+    const rsrc_t sr = make_rsrc(
+        states + (((size_t)it.b * H + it.h) * nc + it.c) * kHeadDim * N, kHeadDim * N * 4);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        lo[k] = lo_halves(xr[2 * k], xr[2 * k + 1]);
-        hi[k] = hi_halves(xr[2 * k], xr[2 * k + 1]);
-      }
-      const int tcol = 8 * (xtb + 8 * it);
-      *(u32x4*)(xT + (2 * pp) * XS + tcol) = lo;
-      *(u32x4*)(xT + (2 * pp + 1) * XS + tcol) = hi;
+    for (int u = 0; u < SU; ++u) r.s[u] = load_f32x4(sr, 16 * (tid + NTHR * u));
+    const size_t row = ((size_t)it.b * H + it.h) * L;
+    const uint32_t toff = 4 * (uint32_t)(it.c * T + (tid % T));
+    if (tid < T) {
+      r.gd = load_f32(make_rsrc(g + row, (uint32_t)L * 4), toff);
+    } else if (tid < 2 * T) {
+      r.gd = load_f32(make_rsrc(dt_t + row, (uint32_t)L * 4), toff);
     }
-    const float* S = states + ((size_t)bh_idx * nc + c) * kHeadDim * N;
+    r.dh = load_f32(drs, 4 * it.h);
+  };
+  auto commit = [&]() {
 #pragma unroll
-    for (int u = tid; u < kHeadDim * N / 8; u += 256) {
-      const int row = u / (N / 8), col = 8 * (u % (N / 8));
-      const f32x4 a = *(const f32x4*)(S + (size_t)row * N + col);
-      const f32x4 a2 = *(const f32x4*)(S + (size_t)row * N + col + 4);
-      uint32_t hv[4], lv[4];
-      split_bf16(a[0], a[1], hv[0], lv[0]);
-      split_bf16(a[2], a[3], hv[1], lv[1]);
-      split_bf16(a2[0], a2[1], hv[2], lv[2]);
-      split_bf16(a2[2], a2[3], hv[3], lv[3]);
-      *(u32x4*)(sh + row * SS + col) = make_u32x4(hv);
-      *(u32x4*)(sl + row * SS + col) = make_u32x4(lv);
+    for (int u = 0; u < XU; ++u) {
+      const int e = tid + NTHR * u, row = e >> 3, c8 = e & 7;
+      *(u32x4*)(xs + row * XS + 8 * c8) = r.x[u];
     }
-    for (int t = tid; t < T; t += 256) {
-      const bool ok = t < nvalid;
-      gs[t] = ok ? g[(size_t)bh_idx * L + t0 + t] : 0.0f;
-      ds[t] = ok ? dt_t[(size_t)bh_idx * L + t0 + t] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int e = tid + NTHR * u, row = e / (N / 4), col = 4 * (e % (N / 4));
+      uint32_t h0, l0, h1, l1;
+      split_bf16(r.s[u][0], r.s[u][1], h0, l0);
+      split_bf16(r.s[u][2], r.s[u][3], h1, l1);
+      *(u32x2*)(sh + row * SS + col) = (u32x2){h0, h1};
+      *(u32x2*)(sl + row * SS + col) = (u32x2){l0, l1};
     }
-  }
+    if (tid < T) {
+      gs[tid] = r.gd;
+    } else if (tid < 2 * T) {
+      ds[tid - T] = r.gd;
+    }
+  };
 
-  // ---- C fragments of this lane's query token (k = state index 32kk+8lq+e)
-  u32x4 cf[KN];
-  {
-    const bool ok = i < nvalid;
-    const uint16_t* crow = Cm + (((size_t)b * L + t0 + i) * G + grp) * N + 8 * lq;
+  // ---- C fragments (k = state index 32kk + 8lq + e) and C B^T blocks,
+  //      cb[entry][rr] = (C B^T)[i][16 jb + 4 lq + rr]
+  u32x4 cf[MB][KN];
+  f32x4 cb[NE];
 #pragma unroll
-    for (int kk = 0; kk < KN; ++kk)
-      cf[kk] = ok ? *(const u32x4*)(crow + 32 * kk) : (u32x4){0, 0, 0, 0};
-  }
-
-  // ---- (B C^T) blocks on or below the diagonal: cb[jb][r] = (C B^T)[i][j],
-  //      j = 16 jb + 4 lq + r
-  f32x4 cb[NJB];
+  for (int e = 0; e < NE; ++e) cb[e] = (f32x4){0, 0, 0, 0};
+  auto form_cb = [&](const Item& it) {
+    const rsrc_t cr = make_rsrc(Cm + (size_t)it.b * L * G * N, bcbytes);
+    const rsrc_t br = make_rsrc(Bm + (size_t)it.b * L * G * N, bcbytes);
 #pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    cb[jb] = (f32x4){0, 0, 0, 0};
-    if (jb <= ib) {
-      const int j = 16 * jb + lr;
-      const bool ok = j < nvalid;
-      const uint16_t* brow = Bm + (((size_t)b * L + t0 + j) * G + grp) * N + 8 * lq;
+    for (int m = 0; m < MB; ++m) {
+      const int i = 16 * row_block<T>(wave, m) + lr;
+      const uint32_t off = ((uint32_t)(it.c * T + i) * G + it.grp) * (N * 2) + 16 * lq;
 #pragma unroll
-      for (int kk = 0; kk < KN; ++kk) {
-        const u32x4 bv = ok ? *(const u32x4*)(brow + 32 * kk) : (u32x4){0, 0, 0, 0};
-        cb[jb] = mfma_bf16(bv, cf[kk], cb[jb]);
-      }
+      for (int kk = 0; kk < KN; ++kk) cf[m][kk] = load_b128(cr, off + 64 * kk);
     }
-  }
-  __syncthreads();
-
-  // ---- Y^T = S C^T (state split hi + lo), then scale column i by 2^{g_i}
-  f32x4 yacc[4];
 #pragma unroll
-  for (int pb = 0; pb < 4; ++pb) yacc[pb] = (f32x4){0, 0, 0, 0};
+    for (int m = 0; m < MB; ++m) {
+      const int ib = row_block<T>(wave, m);
 #pragma unroll
-  for (int kk = 0; kk < KN; ++kk) {
+      for (int k = 0; k < NIB; ++k) {
+        if (k <= ib) {
+          const uint32_t off =
+              ((uint32_t)(it.c * T + 16 * k + lr) * G + it.grp) * (N * 2) + 16 * lq;
+          f32x4 acc = (f32x4){0, 0, 0, 0};
 #pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      const int off = (16 * pb + lr) * SS + 32 * kk + 8 * lq;
-      yacc[pb] = mfma_bf16(*(const u32x4*)(sh + off), cf[kk], yacc[pb]);
-      yacc[pb] = mfma_bf16(*(const u32x4*)(sl + off), cf[kk], yacc[pb]);
-    }
-  }
-  const float gi = gs[i];
-  const float ei = exp2_hw(gi);
-#pragma unroll
-  for (int pb = 0; pb < 4; ++pb) yacc[pb] *= ei;
-
-  // ---- Y^T += X^T L'^T over 32-token k-steps; slots 0..3 carry tokens
-  //      32kj + 4lq + r and slots 4..7 tokens 32kj + 16 + 4lq + r.
-  const float Dh = Dv[h];
-#pragma unroll
-  for (int kj = 0; kj < T / 32; ++kj) {
-    if (2 * kj <= ib) {
-      float v[8];
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int jb = 2 * kj + half;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jb + 4 * lq + r;
-          float w = cb[jb][r] * exp2_hw(gi - gs[j]) * ds[j];
-          if (j == i) w += Dh;
-          v[4 * half + r] = (jb <= ib && j <= i) ? w : 0.0f;
+          for (int kk = 0; kk < KN; ++kk) acc = mfma_bf16(load_b128(br, off + 64 * kk), cf[m][kk], acc);
+          if (m == 0) {
+            if (k < NE) cb[k] = acc;
+          } else {
+            if (NE - 1 - k >= 0) cb[NE - 1 - k] = acc;
+          }
         }
       }
-      uint32_t lh4[4], ll4[4];
+    }
+  };
+
+  issue(k0);
+  int key = -1;
+  for (int k = k0; k < k1; ++k) {
+    const Item it = decode_item(k, H, nc, hpg);
+    const int nkey = (it.b * nc + it.c) * G + it.grp;
+    if (nkey != key) {
+      form_cb(it);
+      key = nkey;
+    }
+    __syncthreads();  // the previous item's LDS reads are done
+    commit();
+    const float Dh = r.dh;
+    if (k + 1 < k1) issue(k + 1);
+    __syncthreads();
+
+    const int t0 = it.c * T;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) split_bf16(v[2 * k], v[2 * k + 1], lh4[k], ll4[k]);
-      const u32x4 lh = make_u32x4(lh4), ll = make_u32x4(ll4);
+    for (int m = 0; m < MB; ++m) {
+      const int ib = row_block<T>(wave, m);
+      const int i = 16 * ib + lr;
+      // Y^T = S C^T (state split hi + lo), then column i scaled by 2^{g_i}
+      f32x4 yacc[4];
 #pragma unroll
-      for (int pb = 0; pb < 4; ++pb) {
-        const int off = (16 * pb + lr) * XS + 32 * kj + 4 * lq;
-        const u32x2 a0 = *(const u32x2*)(xT + off);
-        const u32x2 a1 = *(const u32x2*)(xT + off + 16);
-        const u32x4 xa = (u32x4){a0[0], a0[1], a1[0], a1[1]};
-        yacc[pb] = mfma_bf16(xa, lh, yacc[pb]);
-        yacc[pb] = mfma_bf16(xa, ll, yacc[pb]);
+      for (int pb = 0; pb < 4; ++pb) yacc[pb] = (f32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk) {
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+          const int off = (16 * pb + lr) * SS + 32 * kk + 8 * lq;
+          yacc[pb] = mfma_bf16(*(const u32x4*)(sh + off), cf[m][kk], yacc[pb]);
+          yacc[pb] = mfma_bf16(*(const u32x4*)(sl + off), cf[m][kk], yacc[pb]);
+        }
+      }
+      const float gi = gs[i];
+      const float ei = exp2_hw(gi);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) yacc[pb] *= ei;
+
+      // Y^T += X^T L'^T over 32-token k-steps s: slots 0..3 carry tokens
+      // 32s + 4lq + rr and slots 4..7 tokens 32s + 16 + 4lq + rr.
+#pragma unroll
+      for (int s = 0; s < NE / 2; ++s) {
+        if (2 * s <= ib) {
+          const int e0 = m == 0 ? 2 * s : NE - 1 - 2 * s;
+          const int e1 = m == 0 ? 2 * s + 1 : NE - 2 - 2 * s;
+          float v[8];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const f32x4 cbv = half ? cb[e1] : cb[e0];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int j = 32 * s + 16 * half + 4 * lq + rr;
+              float w = cbv[rr] * exp2_hw(gi - gs[j]) * ds[j];
+              if (j == i) w += Dh;
+              v[4 * half + rr] = j <= i ? w : 0.0f;
+            }
+          }
+          uint32_t lh4[4], ll4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) split_bf16(v[2 * q], v[2 * q + 1], lh4[q], ll4[q]);
+          const u32x4 lh = make_u32x4(lh4), ll = make_u32x4(ll4);
+          const uint16_t* xp = xs + (32 * s + 4 * lq + (lr >> 2)) * XS + 4 * (lr & 3);
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb) {
+            const u32x2 a0 = lds_read_tr16(xp + 16 * pb);
+            const u32x2 a1 = lds_read_tr16(xp + 16 * XS + 16 * pb);
+            const u32x4 xa = (u32x4){a0[0], a0[1], a1[0], a1[1]};
+            yacc[pb] = mfma_bf16(xa, lh, yacc[pb]);
+            yacc[pb] = mfma_bf16(xa, ll, yacc[pb]);
+          }
+        }
+      }
+      if (t0 + i < L) {
+        const size_t off = (((size_t)it.b * L + t0 + i) * H + it.h) * kHeadDim + 4 * lq;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) store_y<YBF16>(y, off + 16 * pb, yacc[pb]);
       }
     }
-  }
-
-  if (i < nvalid) {
-    const size_t off = (((size_t)b * L + t0 + i) * H + h) * kHeadDim + 4 * lq;
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) store_y<YBF16>(y, off + 16 * pb, yacc[pb]);
   }
 }
 
 // ---------------------------------------------------------------- fp32 path
 // k-map over the state index n for v_mfma_f32_16x16x4_f32: step (u, v)
-// gives lane group lq the index 16u + 4lq + v; over tokens j: step (jb, r)
-// gives 16jb + 4lq + r, which is exactly the j of accumulator element r.
+// gives lane group lq the index 16u + 4lq + v; over tokens j: step (jb, rr)
+// gives 16jb + 4lq + rr, which is exactly the j of accumulator element rr.
+// cb entries: row slot 0 block k at entry k, row slot 1 block k at entry
+// NE-1-k; the two rows have NIB + 1 blocks together.
 template <int T, int N, bool YBF16>
-__global__ __launch_bounds__(256) void compute_out_f32(
+__global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_f32(
     const float* __restrict__ x, const float* __restrict__ Bm,
     const float* __restrict__ Cm, const float* __restrict__ dt_t,
     const float* __restrict__ g, const float* __restrict__ states,
     const float* __restrict__ Dv, void* __restrict__ y, int L, int H, int G,
-    int nc) {
-  constexpr int NQ = T / 64;
-  constexpr int XS = T + 4;   // xT row stride (floats)
-  constexpr int KU = N / 16;  // groups of four k-steps over n
-  constexpr int NJB = T / 16;
+    int nc, int items) {
+  using Gm = Geo<T>;
+  constexpr int NTHR = Gm::NTHR, MB = Gm::MB, NIB = Gm::NIB;
+  constexpr int KU = N / 16;            // groups of four k-steps over n
+  constexpr int XS = T + 4;             // X^T row stride (floats)
+  constexpr int SS = N + 4;             // state row stride (floats)
+  constexpr int XU = 4 * T / NTHR;      // (4 tokens x 4 p) x units per thread
+  constexpr int SU = 16 * N / NTHR;     // 16-byte state units per thread
+  constexpr int NE = MB == 1 ? NIB : NIB + 1;
+  static_assert(XU >= 1 && SU >= 1 && 2 * T <= NTHR, "tile split");
   __shared__ __attribute__((aligned(16))) float xT[64 * XS];
+  __shared__ __attribute__((aligned(16))) float ss[64 * SS];
   __shared__ float gs[T], ds[T];
 
-  const OutTile tile = decode_tile(blockIdx.x, H, NQ, nc);
-  const int h = tile.h, q = tile.q, c = tile.c, b = tile.b;
-  const int grp = h / (H / G);
-  const int t0 = c * T;
-  const int nvalid = min(T, L - t0);
-  const int bh_idx = b * H + h;
+  int k0, k1;
+  item_range(items, k0, k1);
+  if (k0 >= k1) return;
+
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
-  const int ib = 4 * q + wave;
-  const int i = 16 * ib + lr;
+  const int hpg = H / G;
+  const uint32_t xbytes = (uint32_t)L * H * kHeadDim * 4;
+  const uint32_t bcbytes = (uint32_t)L * G * N * 4;
+  const rsrc_t drs = make_rsrc(Dv, (uint32_t)H * 4);
 
-  {
-    const int pq = tid & 15, xtb = tid >> 4;
-    for (int it = 0; it <= q; ++it) {
-      f32x4 xr[4];
+  struct Regs {
+    f32x4 x[XU][4];
+    f32x4 s[SU];
+    float gd, dh;
+  } r;
+  auto issue = [&](int k) {
+    const Item it = decode_item(k, H, nc, hpg);
+    const rsrc_t xr = make_rsrc(x + (size_t)it.b * L * H * kHeadDim, xbytes);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * (xtb + 16 * it) + r;
-        xr[r] = t < nvalid
-            ? *(const f32x4*)(x + (((size_t)b * L + t0 + t) * H + h) * kHeadDim + 4 * pq)
-            : (f32x4){0, 0, 0, 0};
+    for (int u = 0; u < XU; ++u) {
+      const int e = tid + NTHR * u, pq = e & 15, tq = e >> 4;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        r.x[u][rr] = load_f32x4(
+            xr, ((uint32_t)(it.c * T + 4 * tq + rr) * H + it.h) * (kHeadDim * 4) + 16 * pq);
+    }
+    const rsrc_t sr = make_rsrc(
+        states + (((size_t)it.b * H + it.h) * nc + it.c) * kHeadDim * N, kHeadDim * N * 4);
+#pragma unroll
+    for (int u = 0; u < SU; ++u) r.s[u] = load_f32x4(sr, 16 * (tid + NTHR * u));
+    const size_t row = ((size_t)it.b * H + it.h) * L;
+    const uint32_t toff = 4 * (uint32_t)(it.c * T + (tid % T));
+    if (tid < T) {
+      r.gd = load_f32(make_rsrc(g + row, (uint32_t)L * 4), toff);
+    } else if (tid < 2 * T) {
+      r.gd = load_f32(make_rsrc(dt_t + row, (uint32_t)L * 4), toff);
+    }
+    r.dh = load_f32(drs, 4 * it.h);
+  };
+  auto commit = [&]() {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int e = tid + NTHR * u, pq = e & 15, tq = e >> 4;
+#pragma unroll
+      for (int ee = 0; ee < 4; ++ee)
+        *(f32x4*)(xT + (4 * pq + ee) * XS + 4 * tq) =
+            (f32x4){r.x[u][0][ee], r.x[u][1][ee], r.x[u][2][ee], r.x[u][3][ee]};
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int e = tid + NTHR * u, row = e / (N / 4), col = 4 * (e % (N / 4));
+      *(f32x4*)(ss + row * SS + col) = r.s[u];
+    }
+    if (tid < T) {
+      gs[tid] = r.gd;
+    } else if (tid < 2 * T) {
+      ds[tid - T] = r.gd;
+    }
+  };
+
+  f32x4 cf[MB][KU];
+  f32x4 cb[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) cb[e] = (f32x4){0, 0, 0, 0};
+  auto form_cb = [&](const Item& it) {
+    const rsrc_t cr = make_rsrc(Cm + (size_t)it.b * L * G * N, bcbytes);
+    const rsrc_t br = make_rsrc(Bm + (size_t)it.b * L * G * N, bcbytes);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int i = 16 * row_block<T>(wave, m) + lr;
+      const uint32_t off = ((uint32_t)(it.c * T + i) * G + it.grp) * (N * 4) + 16 * lq;
+#pragma unroll
+      for (int u = 0; u < KU; ++u) cf[m][u] = load_f32x4(cr, off + 64 * u);
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int ib = row_block<T>(wave, m);
+#pragma unroll
+      for (int k = 0; k < NIB; ++k) {
+        if (k <= ib) {
+          const uint32_t off =
+              ((uint32_t)(it.c * T + 16 * k + lr) * G + it.grp) * (N * 4) + 16 * lq;
+          f32x4 acc = (f32x4){0, 0, 0, 0};
+#pragma unroll
+          for (int u = 0; u < KU; ++u) {
+            const f32x4 bv = load_f32x4(br, off + 64 * u);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc = mfma_f32(bv[v], cf[m][u][v], acc);
+          }
+          if (m == 0) {
+            if (k < NE) cb[k] = acc;
+          } else {
+            if (NE - 1 - k >= 0) cb[NE - 1 - k] = acc;
+          }
+        }
       }
-      const int tcol = 4 * (xtb + 16 * it);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        *(f32x4*)(xT + (4 * pq + e) * XS + tcol) = (f32x4){xr[0][e], xr[1][e], xr[2][e], xr[3][e]};
     }
-    for (int t = tid; t < T; t += 256) {
-      const bool ok = t < nvalid;
-      gs[t] = ok ? g[(size_t)bh_idx * L + t0 + t] : 0.0f;
-      ds[t] = ok ? dt_t[(size_t)bh_idx * L + t0 + t] : 0.0f;
+  };
+
+  issue(k0);
+  int key = -1;
+  for (int k = k0; k < k1; ++k) {
+    const Item it = decode_item(k, H, nc, hpg);
+    const int nkey = (it.b * nc + it.c) * G + it.grp;
+    if (nkey != key) {
+      form_cb(it);
+      key = nkey;
     }
-  }
+    __syncthreads();
+    commit();
+    const float Dh = r.dh;
+    if (k + 1 < k1) issue(k + 1);
+    __syncthreads();
 
-  f32x4 cf[KU];
-  {
-    const bool ok = i < nvalid;
-    const float* crow = Cm + (((size_t)b * L + t0 + i) * G + grp) * N + 4 * lq;
+    const int t0 = it.c * T;
 #pragma unroll
-    for (int u = 0; u < KU; ++u) cf[u] = ok ? *(const f32x4*)(crow + 16 * u) : (f32x4){0, 0, 0, 0};
-  }
-
-  f32x4 cb[NJB];
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    cb[jb] = (f32x4){0, 0, 0, 0};
-    if (jb <= ib) {
-      const int j = 16 * jb + lr;
-      const bool ok = j < nvalid;
-      const float* brow = Bm + (((size_t)b * L + t0 + j) * G + grp) * N + 4 * lq;
-#pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        const f32x4 bv = ok ? *(const f32x4*)(brow + 16 * u) : (f32x4){0, 0, 0, 0};
-#pragma unroll
-        for (int v = 0; v < 4; ++v) cb[jb] = mfma_f32(bv[v], cf[u][v], cb[jb]);
-      }
-    }
-  }
-
-  f32x4 yacc[4];
-  const float* S = states + ((size_t)bh_idx * nc + c) * kHeadDim * N + 4 * lq;
-#pragma unroll
-  for (int pb = 0; pb < 4; ++pb) {
-    yacc[pb] = (f32x4){0, 0, 0, 0};
-    const float* srow = S + (size_t)(16 * pb + lr) * N;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const f32x4 sv = *(const f32x4*)(srow + 16 * u);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) yacc[pb] = mfma_f32(sv[v], cf[u][v], yacc[pb]);
-    }
-  }
-  __syncthreads();
-
-  const float gi = gs[i];
-  const float ei = exp2_hw(gi);
-#pragma unroll
-  for (int pb = 0; pb < 4; ++pb) yacc[pb] *= ei;
-
-  const float Dh = Dv[h];
-#pragma unroll
-  for (int jb = 0; jb < NJB; ++jb) {
-    if (jb <= ib) {
-      float w[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * jb + 4 * lq + r;
-        float v = cb[jb][r] * exp2_hw(gi - gs[j]) * ds[j];
-        if (j == i) v += Dh;
-        w[r] = (j <= i) ? v : 0.0f;
-      }
+    for (int m = 0; m < MB; ++m) {
+      const int ib = row_block<T>(wave, m);
+      const int i = 16 * ib + lr;
+      f32x4 yacc[4];
 #pragma unroll
       for (int pb = 0; pb < 4; ++pb) {
-        const f32x4 xv = *(const f32x4*)(xT + (16 * pb + lr) * XS + 16 * jb + 4 * lq);
+        yacc[pb] = (f32x4){0, 0, 0, 0};
+        const float* srow = ss + (16 * pb + lr) * SS + 4 * lq;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yacc[pb] = mfma_f32(xv[r], w[r], yacc[pb]);
+        for (int u = 0; u < KU; ++u) {
+          const f32x4 sv = *(const f32x4*)(srow + 16 * u);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) yacc[pb] = mfma_f32(sv[v], cf[m][u][v], yacc[pb]);
+        }
+      }
+      const float gi = gs[i];
+      const float ei = exp2_hw(gi);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) yacc[pb] *= ei;
+
+#pragma unroll
+      for (int kb = 0; kb < NIB; ++kb) {
+        if (kb <= ib) {
+          const int e = m == 0 ? kb : NE - 1 - kb;
+          if (e < 0 || e >= NE) continue;
+          float w[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int j = 16 * kb + 4 * lq + rr;
+            float v = cb[e][rr] * exp2_hw(gi - gs[j]) * ds[j];
+            if (j == i) v += Dh;
+            w[rr] = j <= i ? v : 0.0f;
+          }
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb) {
+            const f32x4 xv = *(const f32x4*)(xT + (16 * pb + lr) * XS + 16 * kb + 4 * lq);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) yacc[pb] = mfma_f32(xv[rr], w[rr], yacc[pb]);
+          }
+        }
+      }
+      if (t0 + i < L) {
+        const size_t off = (((size_t)it.b * L + t0 + i) * H + it.h) * kHeadDim + 4 * lq;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) store_y<YBF16>(y, off + 16 * pb, yacc[pb]);
       }
     }
-  }
-
-  if (i < nvalid) {
-    const size_t off = (((size_t)b * L + t0 + i) * H + h) * kHeadDim + 4 * lq;
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) store_y<YBF16>(y, off + 16 * pb, yacc[pb]);
   }
 }
 
 // ------------------------------------------------------------- launching
+// Workgroups resident on the whole device at once for `kernel`: the grid of
+// the persistent kernels.  Computed once per instantiation (a property of
+// the kernel and the device model, not mutable state); a multiple of 8 so
+// the XCD-aware placement applies.
+int resident_slots(const void* kernel, int threads) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
+    return 0;
+  const int slots = (per < 1 ? 1 : per) * cus;
+  return slots < 8 ? slots : slots / 8 * 8;
+}
+
 template <bool BF16, int T, int N, bool YBF16>
 int launch_t(const void* x, const void* B, const void* C, const float* dt_t,
              const float* g, const float* states, const float* D, void* y,
              const Shape& s, hipStream_t st) {
+  constexpr int NTHR = Geo<T>::NTHR;
   const int nc = (int)s.nchunks();
-  const unsigned blocks = (unsigned)(s.batch * nc * (T / 64) * s.nheads);
   const int L = (int)s.seqlen, H = (int)s.nheads, G = (int)s.ngroups;
-  using E = typename In<BF16>::T;
+  const int items = (int)(s.batch * nc * s.nheads);
+  const void* kern = BF16 ? (const void*)compute_out_bf16<T, N, YBF16>
+                          : (const void*)compute_out_f32<T, N, YBF16>;
+  static std::atomic<int> cached{0};
+  int slots = cached.load(std::memory_order_relaxed);
+  if (slots <= 0) {
+    slots = resident_slots(kern, NTHR);
+    if (slots <= 0) return (int)hipErrorInvalidDevice;
+    cached.store(slots, std::memory_order_relaxed);
+  }
+  const unsigned grid = (unsigned)(items < slots ? items : slots);
   if constexpr (BF16) {
-    hipLaunchKernelGGL((compute_out_bf16<T, N, YBF16>), dim3(blocks), dim3(256), 0, st,
-                       (const E*)x, (const E*)B, (const E*)C, dt_t, g, states, D, y, L,
-                       H, G, nc);
+    hipLaunchKernelGGL((compute_out_bf16<T, N, YBF16>), dim3(grid), dim3(NTHR), 0, st,
+                       (const uint16_t*)x, (const uint16_t*)B, (const uint16_t*)C, dt_t, g,
+                       states, D, y, L, H, G, nc, items);
   } else {
-    hipLaunchKernelGGL((compute_out_f32<T, N, YBF16>), dim3(blocks), dim3(256), 0, st,
-                       (const E*)x, (const E*)B, (const E*)C, dt_t, g, states, D, y, L,
-                       H, G, nc);
+    hipLaunchKernelGGL((compute_out_f32<T, N, YBF16>), dim3(grid), dim3(NTHR), 0, st,
+                       (const float*)x, (const float*)B, (const float*)C, dt_t, g, states,
+                       D, y, L, H, G, nc, items);
   }
   return (int)hipGetLastError();
 }
