@@ -38,6 +38,7 @@ SMALL = [
     _wl("fp32_T256_N128_ragged", "fp32", 1, 600, 2, 1, 128, 256, True),
     _wl("fp32_T64_N128_wide_batch", "fp32", 5, 130, 3, 1, 128, 64, False),
     _wl("bf16_T64_N64_shorter_than_chunk", "bf16", 3, 37, 2, 1, 64, 64, False),
+    _wl("bf16_T64_N64_grouped_init", "bf16", 2, 450, 6, 3, 64, 64, True),
     _wl("bf16_T128_N128_single_token", "bf16", 1, 1, 1, 1, 128, 128, True),
     _wl("fp32_T256_N64_single_token", "fp32", 2, 1, 2, 2, 64, 256, True),
 ]
