@@ -38,6 +38,8 @@
 // HBM traffic per (b, h, chunk): x (e*T*64) + B (e*T*N, shared by the heads
 // of a group) + dt, g (8*T) + the stored state (4*64*N); the stored states
 // dominate, so the stage is HBM-bound.
+#include <atomic>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -55,137 +57,172 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // ---------------------------------------------------------------- bf16 path
-// The chunk is streamed in token tiles of TK = min(T, 128); P accumulates over
-// the T / TK tiles of a chunk.  Both operand tiles sit in LDS row-major
-// (token rows): X exactly as loaded, w o B as computed, and the matrix
+// Workgroup tile: HB heads of one group x 16 state rows (p0..p0+15) x BN
+// state columns (n0..n0+BN-1); one wave per (head, NBW blocks of 16 columns).
+// The chunk is streamed in token tiles of TK = min(T, 128).  Per tile, the
+// B columns n0..n0+BN-1 are staged once, exact, and serve all HB heads; the
+// decay weight is folded into x instead:
+//   P^T[n][p] = sum_t B[t][n] (w_t x_t[p]),  w_t = dt_t 2^{g_last - g_t},
+// with w o x a computed fp32 value split into bf16 hi + lo (two MFMAs), so
+// the product keeps ~16 mantissa bits under fp32 accumulation.  Compared with
+// slicing only the state columns, a workgroup reads 16 columns of x per head
+// instead of all 64 and shares one B tile among its heads: about half the
+// bytes and a third of the load instructions per CU per chunk.
+// Both operand tiles sit in LDS token-major ([t][n], [t][p]) and the matrix
 // operands are read with the LDS transpose read.  k-slot map of one 32-token
 // step kk for lane group lq: slots 0..3 <-> tokens 32kk + 4lq + 0..3, slots
 // 4..7 <-> tokens 32kk + 16 + 4lq + 0..3 (both operands alike).  Row strides
-// are chosen so each 32-lane pass of a transpose read (8 consecutive rows x
-// 32 bytes) touches every LDS bank once.
+// are chosen so each 32-lane pass of a transpose read touches every LDS bank
+// once.
 template <int N>
 struct BfTileStride {
   static constexpr int value = N == 16 ? 16 : N + 16;
 };
 
-template <int T, int N, int BN, int Q>
-__global__ __launch_bounds__(256) void state_pass_bf16(
+template <int HB, int BN, int NBW>
+struct BfTile {
+  static constexpr int WPH = BN / (16 * NBW);   // waves per head
+  static constexpr int NTHR = 64 * HB * WPH;
+};
+
+template <int T, int N, int HB, int BN, int NBW, int Q>
+__global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt_t, const float* __restrict__ g,
     const float* __restrict__ init, float* __restrict__ states,
     float* __restrict__ final_state, int L, int H, int G, int nc) {
   constexpr int TK = T < 128 ? T : 128;        // tokens per tile
   constexpr int R = T / TK;                    // tiles per chunk
-  constexpr int NB = BN / 16;                  // 16-column blocks per wave
-  constexpr int XS = BfTileStride<kHeadDim>::value;  // X row stride (bf16)
-  constexpr int BS = BfTileStride<BN>::value;        // w o B row stride (bf16)
-  constexpr int XU = TK * (kHeadDim / 8) / 256;      // X units (token x 8 p) per thread
-  constexpr int kBUnits = TK * (BN / 8);             // B units (token x 8 n)
-  constexpr int BU = (kBUnits + 255) / 256;          // B units per thread
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][TK * XS];
-  __shared__ __attribute__((aligned(16))) uint16_t bhs[2][TK * BS];
-  __shared__ __attribute__((aligned(16))) uint16_t bls[2][TK * BS];
+  constexpr int WPH = BfTile<HB, BN, NBW>::WPH;
+  constexpr int NTHR = BfTile<HB, BN, NBW>::NTHR;
+  constexpr int XS = 16;                       // w o x row stride (bf16)
+  constexpr int BS = BfTileStride<BN>::value;  // B row stride (bf16)
+  constexpr int kXUnits = HB * TK * 2;         // (head, token, 8 of the 16 p)
+  constexpr int XU = (kXUnits + NTHR - 1) / NTHR;
+  constexpr int kBUnits = TK * (BN / 8);       // (token, 8 n)
+  constexpr int BU = (kBUnits + NTHR - 1) / NTHR;
+  __shared__ __attribute__((aligned(16))) uint16_t bts[2][TK * BS];
+  __shared__ __attribute__((aligned(16))) uint16_t whs[2][HB * TK * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t wls[2][HB * TK * XS];
 
   constexpr int NT = N / BN;
+  constexpr int NPS = kHeadDim / 16;           // 16-row slices of the state
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int ntile = logical % NT;
-  const int bh_idx = logical / NT;
-  const int b = bh_idx / H, h = bh_idx % H, grp = h / (H / G);
-  const int n0 = ntile * BN;
+  const int ps = (logical / NT) % NPS;
+  const int hblk = logical / (NT * NPS);
+  const int nhb = H / HB;
+  const int b = hblk / nhb, h0 = (hblk % nhb) * HB;
+  const int grp = h0 / (H / G);
+  const int n0 = ntile * BN, p0 = 16 * ps;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
-  const int p = 16 * wave + lr;
+  const int hh = wave / WPH;                   // this wave's head in the block
+  const int nb0 = (wave % WPH) * NBW;          // its first 16-column block
+  const int h = h0 + hh;
   const int ntiles = nc * R;
 
-  // Buffer descriptors: reads past the sequence's last token return zero.
+  // Buffer descriptors.  x and B: reads past the sequence's last token
+  // return zero.  g and dt_t: the HB heads' rows, [hh][L]; token indices at
+  // or past L are redirected past the range.
   const uint32_t xrow = (uint32_t)(H * kHeadDim), brow = (uint32_t)(G * N);
-  const rsrc_t xr = make_rsrc(x + ((size_t)b * L * H + h) * kHeadDim,
-                              ((uint32_t)(L - 1) * xrow + kHeadDim) * 2u);
+  const rsrc_t xr = make_rsrc(x + (size_t)b * L * H * kHeadDim, (uint32_t)L * xrow * 2u);
   const rsrc_t br = make_rsrc(Bm + ((size_t)b * L * G + grp) * N,
                               ((uint32_t)(L - 1) * brow + N) * 2u);
-  const rsrc_t gr = make_rsrc(g + (size_t)bh_idx * L, (uint32_t)L * 4u);
-  const rsrc_t dr = make_rsrc(dt_t + (size_t)bh_idx * L, (uint32_t)L * 4u);
+  const size_t grow = ((size_t)b * H + h0) * L;
+  const rsrc_t gr = make_rsrc(g + grow, (uint32_t)(HB * L) * 4u);
+  const rsrc_t dr = make_rsrc(dt_t + grow, (uint32_t)(HB * L) * 4u);
 
-  // State slice: acc[nb] holds S[p][n0 + 16nb + 4lq + 0..3].
-  f32x4 acc[NB];
-  const size_t sbase = (size_t)bh_idx * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
+  // State block of this wave: acc[j] holds S_h[p0 + lr][n0 + 16 (nb0 + j) + 4 lq + 0..3].
+  f32x4 acc[NBW];
+  const size_t sbase = ((size_t)b * H + h) * kHeadDim * N + (size_t)(p0 + lr) * N + n0 +
+                       16 * nb0 + 4 * lq;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-    acc[nb] = init ? *(const f32x4*)(init + sbase + 16 * nb) : (f32x4){0, 0, 0, 0};
+  for (int j = 0; j < NBW; ++j)
+    acc[j] = init ? *(const f32x4*)(init + sbase + 16 * j) : (f32x4){0, 0, 0, 0};
   // Let the initial state land before the pipeline starts, so waits inside
   // the loop only ever concern tile loads.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // Per-thread byte offsets (within a tile) of each staging unit; idle B
-  // units point past the range, so every thread issues the same loads.
-  uint32_t xoff[XU], boff[BU], toff[BU];
+  // Staging units of this thread.  x unit u: head u / (2 TK), token
+  // (u / 2) % TK, columns p0 + 8 (u % 2) .. + 7.  B unit u: token u / (BN/8),
+  // columns n0 + 8 (u % (BN/8)) .. + 7.  Idle units read past the range, so
+  // every thread issues the same loads.
+  uint32_t xoff[XU], gtok[XU], ghead[XU], boff[BU];
   int xlds[XU], blds[BU];
 #pragma unroll
   for (int i = 0; i < XU; ++i) {
-    const int u = tid + 256 * i;
-    const int t = u >> 3, c8 = u & 7;
-    xoff[i] = ((uint32_t)t * xrow + 8 * c8) * 2u;
-    xlds[i] = t * XS + 8 * c8;
+    const int u = tid + NTHR * i;
+    const bool on = u < kXUnits;
+    const int uh = on ? u / (2 * TK) : 0, t = (u / 2) % TK, half = u % 2;
+    xoff[i] = on ? (((uint32_t)t * H + h0 + uh) * kHeadDim + p0 + 8 * half) * 2u : kPastRange;
+    gtok[i] = on ? (uint32_t)t : (uint32_t)L;    // token within the tile (L: never valid)
+    ghead[i] = (uint32_t)uh * L;
+    xlds[i] = (uh * TK + t) * XS + 8 * half;
   }
 #pragma unroll
   for (int i = 0; i < BU; ++i) {
-    const int u = tid + 256 * i;
+    const int u = tid + NTHR * i;
     const int t = u / (BN / 8), c8 = u % (BN / 8);
-    const bool on = u < kBUnits;
-    boff[i] = on ? ((uint32_t)t * brow + n0 + 8 * c8) * 2u : kPastRange;
-    toff[i] = on ? (uint32_t)t : kPastRange / 4;   // token of the unit
+    boff[i] = u < kBUnits ? ((uint32_t)t * brow + n0 + 8 * c8) * 2u : kPastRange;
     blds[i] = t * BS + 8 * c8;
   }
   const uint32_t xstep = xrow * 2u, bstep = brow * 2u;   // bytes per token
 
-  // Raw global data of one tile: X rows, B rows, and each B unit's token's
-  // g and dt together with g at the chunk's last token.
+  // Raw global data of one tile: x units with their token's g and dt and
+  // their head's g at the chunk's last token; B units; and g at the chunk's
+  // last token for this wave's own head (its decay).
   struct Tile {
     u32x4 x[XU];
+    float g[XU], dt[XU], gl[XU];
     u32x4 b[BU];
-    float g[BU], dt[BU];
-    float glast;
+    float dl;
   };
 
   auto issue = [&](int k, Tile& tl) {
     const int c = k / R;
     const uint32_t t0 = (uint32_t)(k * TK);
+    const uint32_t tlast = (uint32_t)(min(c * T + T, L) - 1);
 #pragma unroll
-    for (int i = 0; i < XU; ++i) tl.x[i] = load_b128(xr, xoff[i] + t0 * xstep);
-#pragma unroll
-    for (int i = 0; i < BU; ++i) {
-      tl.b[i] = load_b128(br, boff[i] + t0 * bstep);
-      tl.g[i] = load_f32(gr, (t0 + toff[i]) * 4u);
-      tl.dt[i] = load_f32(dr, (t0 + toff[i]) * 4u);
+    for (int i = 0; i < XU; ++i) {
+      tl.x[i] = load_b128(xr, xoff[i] + t0 * xstep);
+      const uint32_t tt = t0 + gtok[i];
+      const uint32_t go = tt < (uint32_t)L ? (ghead[i] + tt) * 4u : kPastRange;
+      tl.g[i] = load_f32(gr, go);
+      tl.dt[i] = load_f32(dr, go);
+      tl.gl[i] = load_f32(gr, (ghead[i] + tlast) * 4u);
     }
-    tl.glast = load_f32(gr, (uint32_t)(min(c * T + T, L) - 1) * 4u);
+#pragma unroll
+    for (int i = 0; i < BU; ++i) tl.b[i] = load_b128(br, boff[i] + t0 * bstep);
+    tl.dl = load_f32(gr, ((uint32_t)hh * L + tlast) * 4u);
   };
 
-  // X (as loaded) and the split w o B of a tile into LDS buffer `buf`.
-  // w_t = dt_t 2^{g_last - g_t}; tokens past the end read dt = g = 0 -> 0.
+  // B (as loaded) and the split w o x of a tile into LDS buffer `buf`.
+  // Tokens past the end read dt = g = 0 and x = 0, so w o x = 0.
   auto commit = [&](int buf, const Tile& tl) {
 #pragma unroll
-    for (int i = 0; i < XU; ++i) *(u32x4*)(xs[buf] + xlds[i]) = tl.x[i];
-#pragma unroll
-    for (int i = 0; i < BU; ++i) {
-      if (tid + 256 * i < kBUnits) {
-        const float w = tl.dt[i] * exp2_hw(tl.glast - tl.g[i]);
+    for (int i = 0; i < XU; ++i) {
+      if (tid + NTHR * i < kXUnits) {
+        const float w = tl.dt[i] * exp2_hw(tl.gl[i] - tl.g[i]);
         uint32_t hv[4], lv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          split_bf16(bf16_lo(tl.b[i][e]) * w, bf16_hi(tl.b[i][e]) * w, hv[e], lv[e]);
-        *(u32x4*)(bhs[buf] + blds[i]) = make_u32x4(hv);
-        *(u32x4*)(bls[buf] + blds[i]) = make_u32x4(lv);
+          split_bf16(bf16_lo(tl.x[i][e]) * w, bf16_hi(tl.x[i][e]) * w, hv[e], lv[e]);
+        *(u32x4*)(whs[buf] + xlds[i]) = make_u32x4(hv);
+        *(u32x4*)(wls[buf] + xlds[i]) = make_u32x4(lv);
       }
     }
+#pragma unroll
+    for (int i = 0; i < BU; ++i)
+      if (tid + NTHR * i < kBUnits) *(u32x4*)(bts[buf] + blds[i]) = tl.b[i];
   };
 
   // Transpose-read addresses of this lane (element offsets within a tile).
   const int rsel = 4 * lq + (lr >> 2), csel = 4 * (lr & 3);
-  const int xrd = rsel * XS + 16 * wave + csel;
-  const int brd = rsel * BS + csel;
+  const int wrd = (hh * TK + rsel) * XS + csel;
+  const int brd = rsel * BS + 16 * nb0 + csel;
 
-  f32x4 ph[NB], pl[NB];
+  f32x4 ph[NBW], pl[NBW];
   // One step of the sequential pass for tile k: the state store at a chunk
   // start, tile k's matrix products from LDS buffer k & 1, the staging of
   // tile k + 1 into the other buffer (independent of the products, so the
@@ -194,36 +231,38 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
   auto step = [&](int k, const Tile& cur, const Tile& next) {
     const int sub = k % R;
     if (sub == 0) {
-      float* dst = states + ((size_t)bh_idx * nc + k / R) * kHeadDim * N + (size_t)p * N + n0 + 4 * lq;
+      float* dst = states + (((size_t)b * H + h) * nc + k / R) * kHeadDim * N +
+                   (size_t)(p0 + lr) * N + n0 + 16 * nb0 + 4 * lq;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        *(f32x4*)(dst + 16 * nb) = acc[nb];
-        ph[nb] = pl[nb] = (f32x4){0, 0, 0, 0};
+      for (int j = 0; j < NBW; ++j) {
+        *(f32x4*)(dst + 16 * j) = acc[j];
+        ph[j] = pl[j] = (f32x4){0, 0, 0, 0};
       }
     }
     const int buf = k & 1;
-    const uint16_t* xt = xs[buf];
-    const uint16_t* bht = bhs[buf];
-    const uint16_t* blt = bls[buf];
 #pragma unroll
     for (int kk = 0; kk < TK / 32; ++kk) {
-      const u32x2 x0 = lds_read_tr16(xt + xrd + 32 * kk * XS);
-      const u32x2 x1 = lds_read_tr16(xt + xrd + (32 * kk + 16) * XS);
-      const u32x4 xv = {x0[0], x0[1], x1[0], x1[1]};
+      const u32x2 a0 = lds_read_tr16(whs[buf] + wrd + 32 * kk * XS);
+      const u32x2 a1 = lds_read_tr16(whs[buf] + wrd + (32 * kk + 16) * XS);
+      const u32x2 c0 = lds_read_tr16(wls[buf] + wrd + 32 * kk * XS);
+      const u32x2 c1 = lds_read_tr16(wls[buf] + wrd + (32 * kk + 16) * XS);
+      const u32x4 wxh = {a0[0], a0[1], a1[0], a1[1]};
+      const u32x4 wxl = {c0[0], c0[1], c1[0], c1[1]};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int o0 = brd + 32 * kk * BS + 16 * nb, o1 = o0 + 16 * BS;
-        const u32x2 h0 = lds_read_tr16(bht + o0), h1 = lds_read_tr16(bht + o1);
-        const u32x2 l0 = lds_read_tr16(blt + o0), l1 = lds_read_tr16(blt + o1);
-        ph[nb] = mfma_bf16((u32x4){h0[0], h0[1], h1[0], h1[1]}, xv, ph[nb]);
-        pl[nb] = mfma_bf16((u32x4){l0[0], l0[1], l1[0], l1[1]}, xv, pl[nb]);
+      for (int j = 0; j < NBW; ++j) {
+        const int o0 = brd + 32 * kk * BS + 16 * j;
+        const u32x2 e0 = lds_read_tr16(bts[buf] + o0);
+        const u32x2 e1 = lds_read_tr16(bts[buf] + o0 + 16 * BS);
+        const u32x4 bv = {e0[0], e0[1], e1[0], e1[1]};
+        ph[j] = mfma_bf16(bv, wxh, ph[j]);
+        pl[j] = mfma_bf16(bv, wxl, pl[j]);
       }
     }
     if (k + 1 < ntiles) commit(buf ^ 1, next);
     if (sub == R - 1) {
-      const float decay = exp2_hw(cur.glast);
+      const float decay = exp2_hw(cur.dl);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = decay * acc[nb] + (ph[nb] + pl[nb]);
+      for (int j = 0; j < NBW; ++j) acc[j] = decay * acc[j] + (ph[j] + pl[j]);
     }
     __syncthreads();
   };
@@ -262,7 +301,7 @@ __global__ __launch_bounds__(256) void state_pass_bf16(
   }
   if (final_state) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) *(f32x4*)(final_state + sbase + 16 * nb) = acc[nb];
+    for (int j = 0; j < NBW; ++j) *(f32x4*)(final_state + sbase + 16 * j) = acc[j];
   }
 }
 
@@ -443,8 +482,84 @@ __global__ __launch_bounds__(256) void state_pass_f32(
 }
 
 // ------------------------------------------------------------- launching
-// n-tile width: the widest tile that still gives >= 1024 workgroups (four
-// per CU), else the narrowest.
+// bf16 workgroup tiles (heads HB, state columns BN, 16-column blocks per
+// wave NBW), in order of preference: the first that divides the heads of a
+// group (so the heads of a tile share B) and still gives one workgroup per
+// CU is used, else the one with the most workgroups.  Measured on MI355X:
+// tiles with 64 columns (each B row one 128-byte line) beat narrower ones
+// with fewer bytes but more partial lines, and among those more heads per
+// tile (fewer x and B requests per state element) is faster.
+struct BfCfg {
+  int hb, bn, nbw;
+};
+constexpr BfCfg kBfCfgs[] = {{5, 64, 2}, {4, 64, 2}, {3, 64, 1}, {2, 64, 1},
+                             {1, 64, 1}, {2, 32, 1}, {1, 32, 1}, {1, 16, 1}};
+constexpr int kNumBfCfgs = sizeof(kBfCfgs) / sizeof(kBfCfgs[0]);
+
+int choose_bf_cfg(const Shape& s, int cus) {
+  const int64_t hpg = s.nheads / s.ngroups;
+  int most = -1;
+  int64_t most_wgs = -1;
+  for (int i = 0; i < kNumBfCfgs; ++i) {
+    const BfCfg c = kBfCfgs[i];
+    if (hpg % c.hb != 0 || c.bn > s.dstate) continue;
+    const int64_t wgs = s.batch * (s.nheads / c.hb) * (kHeadDim / 16) * (s.dstate / c.bn);
+    if (wgs >= cus) return i;
+    if (wgs > most_wgs) {
+      most = i;
+      most_wgs = wgs;
+    }
+  }
+  return most;
+}
+
+int device_cus() {
+  static std::atomic<int> cached{0};
+  int cus = cached.load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;  // the MI355X count; only the tile choice depends on it
+  cached.store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+template <int T, int N, int HB, int BN, int NBW>
+int launch_bf(const uint16_t* x, const uint16_t* B, const float* dt_t, const float* g,
+              const float* init, float* states, float* fin, const Shape& s,
+              hipStream_t st) {
+  constexpr int NTHR = BfTile<HB, BN, NBW>::NTHR;
+  constexpr int Q = 2;   // tiles per group (measured: deeper is no faster)
+  const unsigned blocks =
+      (unsigned)(s.batch * (s.nheads / HB) * (kHeadDim / 16) * (N / BN));
+  hipLaunchKernelGGL((state_pass_bf16<T, N, HB, BN, NBW, Q>), dim3(blocks), dim3(NTHR), 0,
+                     st, x, B, dt_t, g, init, states, fin, (int)s.seqlen, (int)s.nheads,
+                     (int)s.ngroups, (int)s.nchunks());
+  return (int)hipGetLastError();
+}
+
+template <int T, int N>
+int launch_bf_n(const void* x, const void* B, const float* dt_t, const float* g,
+                const float* init, float* states, float* fin, const Shape& s,
+                hipStream_t st) {
+  const uint16_t* xb = (const uint16_t*)x;
+  const uint16_t* bb = (const uint16_t*)B;
+  switch (choose_bf_cfg(s, device_cus())) {
+    case 0: return launch_bf<T, N, 5, 64, 2>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 1: return launch_bf<T, N, 4, 64, 2>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 2: return launch_bf<T, N, 3, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 3: return launch_bf<T, N, 2, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 4: return launch_bf<T, N, 1, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 5: return launch_bf<T, N, 2, 32, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 6: return launch_bf<T, N, 1, 32, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    default: return launch_bf<T, N, 1, 16, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+  }
+}
+
+// fp32 n-tile width: the widest tile that still gives >= 1024 workgroups
+// (four per CU), else the narrowest.
 int choose_bn(const Shape& s) {
   const int64_t pairs = s.batch * s.nheads;
   for (int bn : {64, 32}) {
@@ -453,42 +568,26 @@ int choose_bn(const Shape& s) {
   return 16;
 }
 
-// Pipeline depth: for bf16, tiles per group (two groups in flight); for fp32,
-// the register ring depth.  Bounded by register use.
-template <bool BF16, int T, int BN>
-constexpr int ring_depth() {
-  if constexpr (BF16) return (T >= 128 && BN >= 32) ? 1 : 2;
-  else return BN >= 32 ? 2 : 4;
-}
-
-template <bool BF16, int T, int N, int BN>
-int launch_t(const void* x, const void* B, const float* dt_t, const float* g,
-             const float* init, float* states, float* fin, const Shape& s,
-             hipStream_t st) {
-  constexpr int D = ring_depth<BF16, T, BN>();
+template <int T, int N, int BN>
+int launch_f32(const void* x, const void* B, const float* dt_t, const float* g,
+               const float* init, float* states, float* fin, const Shape& s,
+               hipStream_t st) {
+  constexpr int D = BN >= 32 ? 2 : 4;   // register ring depth
   const unsigned blocks = (unsigned)(s.batch * s.nheads * (N / BN));
-  const int L = (int)s.seqlen, H = (int)s.nheads, G = (int)s.ngroups,
-            nc = (int)s.nchunks();
-  if constexpr (BF16) {
-    hipLaunchKernelGGL((state_pass_bf16<T, N, BN, D>), dim3(blocks), dim3(256), 0, st,
-                       (const uint16_t*)x, (const uint16_t*)B, dt_t, g, init, states,
-                       fin, L, H, G, nc);
-  } else {
-    hipLaunchKernelGGL((state_pass_f32<T, N, BN, D>), dim3(blocks), dim3(256), 0, st,
-                       (const float*)x, (const float*)B, dt_t, g, init, states, fin,
-                       L, H, G, nc);
-  }
+  hipLaunchKernelGGL((state_pass_f32<T, N, BN, D>), dim3(blocks), dim3(256), 0, st,
+                     (const float*)x, (const float*)B, dt_t, g, init, states, fin,
+                     (int)s.seqlen, (int)s.nheads, (int)s.ngroups, (int)s.nchunks());
   return (int)hipGetLastError();
 }
 
-template <bool BF16, int T, int N>
-int launch_bn(const void* x, const void* B, const float* dt_t, const float* g,
-              const float* init, float* states, float* fin, const Shape& s,
-              hipStream_t st) {
+template <int T, int N>
+int launch_f32_n(const void* x, const void* B, const float* dt_t, const float* g,
+                 const float* init, float* states, float* fin, const Shape& s,
+                 hipStream_t st) {
   switch (choose_bn(s)) {
-    case 64: return launch_t<BF16, T, N, 64>(x, B, dt_t, g, init, states, fin, s, st);
-    case 32: return launch_t<BF16, T, N, 32>(x, B, dt_t, g, init, states, fin, s, st);
-    default: return launch_t<BF16, T, N, 16>(x, B, dt_t, g, init, states, fin, s, st);
+    case 64: return launch_f32<T, N, 64>(x, B, dt_t, g, init, states, fin, s, st);
+    case 32: return launch_f32<T, N, 32>(x, B, dt_t, g, init, states, fin, s, st);
+    default: return launch_f32<T, N, 16>(x, B, dt_t, g, init, states, fin, s, st);
   }
 }
 
@@ -496,8 +595,13 @@ template <bool BF16, int T>
 int launch_n(const void* x, const void* B, const float* dt_t, const float* g,
              const float* init, float* states, float* fin, const Shape& s,
              hipStream_t st) {
-  if (s.dstate == 64) return launch_bn<BF16, T, 64>(x, B, dt_t, g, init, states, fin, s, st);
-  return launch_bn<BF16, T, 128>(x, B, dt_t, g, init, states, fin, s, st);
+  if constexpr (BF16) {
+    if (s.dstate == 64) return launch_bf_n<T, 64>(x, B, dt_t, g, init, states, fin, s, st);
+    return launch_bf_n<T, 128>(x, B, dt_t, g, init, states, fin, s, st);
+  } else {
+    if (s.dstate == 64) return launch_f32_n<T, 64>(x, B, dt_t, g, init, states, fin, s, st);
+    return launch_f32_n<T, 128>(x, B, dt_t, g, init, states, fin, s, st);
+  }
 }
 
 template <bool BF16>

@@ -39,6 +39,12 @@ SMALL = [
     _wl("fp32_T64_N128_wide_batch", "fp32", 5, 130, 3, 1, 128, 64, False),
     _wl("bf16_T64_N64_shorter_than_chunk", "bf16", 3, 37, 2, 1, 64, 64, False),
     _wl("bf16_T64_N64_grouped_init", "bf16", 2, 450, 6, 3, 64, 64, True),
+    # shapes that select each bf16 state-pass tile (heads x columns per workgroup)
+    _wl("bf16_T64_N128_3head_tiles", "bf16", 16, 130, 6, 1, 128, 64, True),
+    _wl("bf16_T128_N128_5head_tiles_grouped", "bf16", 16, 300, 10, 2, 128, 128, False),
+    _wl("bf16_T256_N128_2head_tiles_ragged", "bf16", 8, 300, 8, 1, 128, 256, True),
+    _wl("bf16_T64_N128_4head_tiles", "bf16", 16, 100, 8, 1, 128, 64, False),
+    _wl("bf16_T128_N128_1head_tiles_group_per_head", "bf16", 4, 150, 8, 8, 128, 128, True),
     _wl("bf16_T128_N128_single_token", "bf16", 1, 1, 1, 1, 128, 128, True),
     _wl("fp32_T256_N64_single_token", "fp32", 2, 1, 2, 2, 64, 256, True),
 ]
