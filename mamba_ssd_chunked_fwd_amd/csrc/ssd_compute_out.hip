@@ -49,6 +49,9 @@
 namespace ssd {
 namespace {
 
+// A byte offset past every buffer range used here (reads return zero).
+constexpr uint32_t kPastRange = 0x7FFFFFF0u;
+
 template <bool YBF16>
 __device__ __forceinline__ void store_y(void* y, size_t off, f32x4 v) {
   if constexpr (YBF16) {
@@ -139,26 +142,45 @@ __global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_bf16(
     f32x4 s[SU];
     float gd, dh;
   } r;
-  auto issue = [&](int k) {
-    const Item it = decode_item(k, H, nc, hpg);
-    const rsrc_t xr = make_rsrc(x + (size_t)it.b * L * H * kHeadDim, xbytes);
+  // The loads of one item, as NLOAD single-instruction slots that the
+  // compute of the previous item interleaves (see the item loop).  An item
+  // index past this workgroup's run gets empty buffer ranges: its loads
+  // return zero without touching memory, so every slot is issued on every
+  // pass and the loop body has no branch around them.
+  constexpr int NLOAD = XU + SU + 2;
+  struct Src {
+    rsrc_t xr, sr, gdr;
+    uint32_t xo[XU], gdo;
+    int h;
+  };
+  auto prepare = [&](int k, Src& sc) {
+    const bool live = k < k1;
+    const Item it = decode_item(live ? k : k0, H, nc, hpg);
+    sc.xr = make_rsrc(x + (size_t)it.b * L * H * kHeadDim, live ? xbytes : 0u);
 #pragma unroll
     for (int u = 0; u < XU; ++u) {
       const int e = tid + NTHR * u, row = e >> 3, c8 = e & 7;
-      r.x[u] = load_b128(xr, ((uint32_t)(it.c * T + row) * H + it.h) * (kHeadDim * 2) + 16 * c8);
+      sc.xo[u] = ((uint32_t)(it.c * T + row) * H + it.h) * (kHeadDim * 2) + 16 * c8;
     }
-    const rsrc_t sr = make_rsrc(
-        states + (((size_t)it.b * H + it.h) * nc + it.c) * kHeadDim * N, kHeadDim * N * 4);
-#pragma unroll
-    for (int u = 0; u < SU; ++u) r.s[u] = load_f32x4(sr, 16 * (tid + NTHR * u));
+    sc.sr = make_rsrc(states + (((size_t)it.b * H + it.h) * nc + it.c) * kHeadDim * N,
+                      live ? kHeadDim * N * 4u : 0u);
+    // waves [0, T/64) read g, waves [T/64, 2T/64) read dt (a uniform choice)
     const size_t row = ((size_t)it.b * H + it.h) * L;
-    const uint32_t toff = 4 * (uint32_t)(it.c * T + (tid % T));
-    if (tid < T) {
-      r.gd = load_f32(make_rsrc(g + row, (uint32_t)L * 4), toff);
-    } else if (tid < 2 * T) {
-      r.gd = load_f32(make_rsrc(dt_t + row, (uint32_t)L * 4), toff);
+    const bool wave_g = __builtin_amdgcn_readfirstlane(tid >> 6) < T / 64;
+    sc.gdr = make_rsrc((wave_g ? g : dt_t) + row, live ? (uint32_t)L * 4 : 0u);
+    sc.gdo = tid < 2 * T ? 4 * (uint32_t)(it.c * T + (tid % T)) : kPastRange;
+    sc.h = it.h;
+  };
+  auto issue_slot = [&](int j, const Src& sc) {
+    if (j < XU) {
+      r.x[j] = load_b128(sc.xr, sc.xo[j]);
+    } else if (j < XU + SU) {
+      r.s[j - XU] = load_f32x4(sc.sr, 16 * (tid + NTHR * (j - XU)));
+    } else if (j == XU + SU) {
+      r.gd = load_f32(sc.gdr, sc.gdo);
+    } else {
+      r.dh = load_f32(drs, 4 * sc.h);
     }
-    r.dh = load_f32(drs, 4 * it.h);
   };
   auto commit = [&]() {
 #pragma unroll
@@ -219,7 +241,12 @@ __global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_bf16(
     }
   };
 
-  issue(k0);
+  {
+    Src sc;
+    prepare(k0, sc);
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) issue_slot(j, sc);
+  }
   int key = -1;
   for (int k = k0; k < k1; ++k) {
     const Item it = decode_item(k, H, nc, hpg);
@@ -231,7 +258,8 @@ __global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_bf16(
     __syncthreads();  // the previous item's LDS reads are done
     commit();
     const float Dh = r.dh;
-    if (k + 1 < k1) issue(k + 1);
+    Src nxt;
+    prepare(k + 1, nxt);
     __syncthreads();
 
     const int t0 = it.c * T;
@@ -247,10 +275,16 @@ __global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_bf16(
       for (int kk = 0; kk < KN; ++kk) {
 #pragma unroll
         for (int pb = 0; pb < 4; ++pb) {
+          // the next item's loads, one per pair of matrix instructions
+          if (m == 0 && 4 * kk + pb < NLOAD) issue_slot(4 * kk + pb, nxt);
           const int off = (16 * pb + lr) * SS + 32 * kk + 8 * lq;
           yacc[pb] = mfma_bf16(*(const u32x4*)(sh + off), cf[m][kk], yacc[pb]);
           yacc[pb] = mfma_bf16(*(const u32x4*)(sl + off), cf[m][kk], yacc[pb]);
         }
+      }
+      if (m == 0) {
+#pragma unroll
+        for (int j = 4 * KN; j < NLOAD; ++j) issue_slot(j, nxt);
       }
       const float gi = gs[i];
       const float ei = exp2_hw(gi);
