@@ -215,6 +215,30 @@ def main() -> int:
     dur = {n: statistics.mean(e[k].elapsed_time(e[k + 1]) for e in st_ev)
            for k, n in enumerate(stage_names)}
 
+    # ---- the streaming decode step at the same batch and heads: one token
+    #      per sequence from the carried state (read and written in place)
+    dec_states = [torch.randn(b, H, P, N, device=dev) for _ in range(nsets)]
+    dec_in = [(s["x"][:, 0].contiguous(), s["dt"][:, 0].contiguous(),
+               s["B"][:, 0].contiguous(), s["C"][:, 0].contiguous(),
+               torch.empty(b, H, P, device=dev, dtype=ty)) for s in sets]
+    for i in range(5):
+        xt, dtt, Bt, Ct, yt = dec_in[i % nsets]
+        ssd.ssd_decode_step(xt, dtt, sets[0]["A"], Bt, Ct, sets[0]["D"],
+                            dec_states[i % nsets], yt)
+    ndec = max(50, args.steps)
+    dec_ev = [torch.cuda.Event(enable_timing=True) for _ in range(ndec + 1)]
+    torch.cuda.synchronize()
+    dec_ev[0].record(stream)
+    for i in range(ndec):
+        xt, dtt, Bt, Ct, yt = dec_in[i % nsets]
+        ssd.ssd_decode_step(xt, dtt, sets[0]["A"], Bt, Ct, sets[0]["D"],
+                            dec_states[i % nsets], yt)
+        dec_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = statistics.mean(dec_ev[i].elapsed_time(dec_ev[i + 1]) for i in range(ndec))
+    dec_bytes = (8 * b * H * P * N + (2 if w.dtype == "bf16" else 4) * (b * H * P + 2 * b * G * N)
+                 + 4 * b * H + 8 * H + y_bytes * b * H * P)
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -263,6 +287,11 @@ def main() -> int:
                      "traffic": traffic},
         "stages": stages,
         "ssd_forward_event_ms": round(fwd_ms, 5),
+        "decode_step": {"ms": round(dec_ms, 5), "tokens_per_s": round(b / (dec_ms * 1e-3), 1),
+                        "alg_bytes": dec_bytes,
+                        "GB_per_s": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "note": "one token for each of the batch's sequences, state in place"},
         "effective_TFLOP_per_s": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
     }

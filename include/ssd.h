@@ -154,6 +154,27 @@ ssd_status ssd_forward(const void *x, const float *dt, const float *A,
                        size_t workspace_bytes, int in_dtype, int y_dtype,
                        const ssd_dims *dims, void *stream);
 
+/*
+ * The streaming decode step [P1 "The Mamba-2 Recurrence"; P1 "Why Would a
+ * Trading Firm Care About Mamba-2 Kernels?" (at inference the fixed-size
+ * state is carried forward and updated per new event); P1 "Kernel 2" (the
+ * final state is the next call's init_state)]: one token through the
+ * recurrence for every (b, h), with the state updated in place:
+ *   state = exp(A_h dt) state + dt x B^T;   y = state C + D_h x
+ * (y reads the updated state, as in the forward pass).  `state` is the
+ * final_state of a previous ssd_forward (or any [b, H, P, N] fp32 state) and
+ * holds the state after this token on return.
+ *   x [b, H, P] in_dtype       dt [b, H] fp32 (already softplus'd)
+ *   A [H] fp32                 B, C [b, G, N] in_dtype      D [H] fp32
+ *   state [b, H, P, N] fp32 (read and written)   y [b, H, P] in y_dtype
+ * These are the layouts of one token of the forward pass's tensors.  Only
+ * batch, nheads, headdim, dstate and ngroups of `dims` are read.
+ */
+ssd_status ssd_decode_step(const void *x, const float *dt, const float *A,
+                           const void *B, const void *C, const float *D,
+                           float *state, void *y, int in_dtype, int y_dtype,
+                           const ssd_dims *dims, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.ssd_compute_out.restype = i
     lib.ssd_forward.argtypes = [vp] * 11 + [sz, i, i, dims, vp]
     lib.ssd_forward.restype = i
+    lib.ssd_decode_step.argtypes = [vp] * 8 + [i, i, dims, vp]
+    lib.ssd_decode_step.restype = i
     return lib
 
 
@@ -249,6 +251,35 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
         _ptr(init_state), _ptr(y), _ptr(states), _ptr(final_state),
         _ptr(workspace), nbytes, _dtype_code(x.dtype), _dtype_code(y.dtype),
         ctypes.byref(d), _stream(dev)), "ssd_forward")
+
+
+def ssd_decode_step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+                    B: torch.Tensor, C: torch.Tensor, D: torch.Tensor,
+                    state: torch.Tensor, y: torch.Tensor) -> None:
+    """One token for every (batch, head): ``state`` [b, H, P, N] fp32 is
+    updated in place and ``y`` [b, H, P] written.  x [b, H, P], dt [b, H],
+    B, C [b, G, N]."""
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [batch, nheads, headdim] and B "
+                         "[batch, ngroups, dstate]")
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    d = SsdDims(b, 1, H, P, N, G, 64)
+    dev = x.device
+    ins = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _check(x, "x", None, ins)
+    _check(B, "B", (b, G, N), (x.dtype,), dev)
+    _check(C, "C", (b, G, N), (x.dtype,), dev)
+    _check(dt, "dt", (b, H), f32, dev)
+    _check(A, "A", (H,), f32, dev)
+    _check(D, "D", (H,), f32, dev)
+    _check(state, "state", (b, H, P, N), f32, dev)
+    _check(y, "y", (b, H, P), ins, dev)
+    _raise(_lib.ssd_decode_step(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
+        _ptr(y), _dtype_code(x.dtype), _dtype_code(y.dtype), ctypes.byref(d),
+        _stream(dev)), "ssd_decode_step")
 
 
 # ------------------------------------------------------------ convenience

@@ -153,4 +153,25 @@ ssd_status ssd_forward(const void* x, const float* dt, const float* A,
   return from_hip(err);
 }
 
+ssd_status ssd_decode_step(const void* x, const float* dt, const float* A,
+                           const void* B, const void* C, const float* D, float* state,
+                           void* y, int in_dtype, int y_dtype, const ssd_dims* dims,
+                           void* stream) {
+  if (dims == nullptr) return SSD_ERR_INVALID_ARGUMENT;
+  // One token: seqlen and chunk_size are not read; check the rest with
+  // those two fixed to supported values.
+  ssd_dims d1 = *dims;
+  d1.seqlen = 1;
+  d1.chunk_size = 64;
+  ssd::Shape s;
+  const ssd_status st = check_dims(&d1, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype) || !ok_dtype(y_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(x) || !ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(D) ||
+      !ok_ptr(state) || !ok_ptr(y))
+    return SSD_ERR_INVALID_ARGUMENT;
+  return from_hip(ssd::launch_decode_step(x, dt, A, B, C, D, state, y, in_dtype == SSD_BF16,
+                                          y_dtype == SSD_BF16, s, stream));
+}
+
 }  // extern "C"

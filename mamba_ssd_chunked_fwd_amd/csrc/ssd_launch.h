@@ -26,4 +26,8 @@ int launch_compute_out(const void* x, const void* B, const void* C,
                        const float* D, void* y, bool bf16_in, bool bf16_out,
                        const Shape& s, void* stream);
 
+int launch_decode_step(const void* x, const float* dt, const float* A, const void* B,
+                       const void* C, const float* D, float* state, void* y, bool bf16_in,
+                       bool bf16_out, const Shape& s, void* stream);
+
 }  // namespace ssd

@@ -39,7 +39,7 @@ def test_every_declared_function_is_exported():
     names = ssd.header_functions()
     assert set(names) == {"ssd_status_string", "ssd_forward_workspace_bytes",
                           "ssd_chunk_cumsum", "ssd_fwd_pass_state",
-                          "ssd_compute_out", "ssd_forward"}
+                          "ssd_compute_out", "ssd_forward", "ssd_decode_step"}
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -111,6 +111,23 @@ def test_forward_rejects_small_workspace():
     assert _fwd(d, wsb=need - 1) == WS
     assert _fwd(d, ws=None) == WS
     assert _fwd(d, ws=MISALIGNED) == WS
+
+
+def test_decode_step_validates():
+    d = dims()
+    call = lambda dd, **o: lib.ssd_decode_step(
+        o.get("x", FAKE), o.get("dt", FAKE), o.get("A", FAKE), o.get("B", FAKE),
+        o.get("C", FAKE), o.get("D", FAKE), o.get("state", FAKE), o.get("y", FAKE),
+        o.get("ind", ssd.SSD_BF16), o.get("yd", ssd.SSD_F32),
+        ctypes.byref(dd) if dd is not None else None, None)
+    assert call(None) == INV
+    for name in ("x", "dt", "A", "B", "C", "D", "state", "y"):
+        assert call(d, **{name: None}) == INV, name
+        assert call(d, **{name: MISALIGNED}) == INV, name
+    assert call(d, ind=3) == INV
+    assert call(dims(dstate=96)) == UNS
+    assert call(dims(headdim=128)) == UNS
+    assert call(dims(nheads=5)) == INV          # 5 heads, 2 groups
 
 
 def test_stage_entry_points_validate():
