@@ -59,7 +59,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // ---------------------------------------------------------------- bf16 path
 // Workgroup tile: HB heads of one group x 16 state rows (p0..p0+15) x BN
 // state columns (n0..n0+BN-1); one wave per (head, NBW blocks of 16 columns).
-// The chunk is streamed in token tiles of TK = min(T, 128).  Per tile, the
+// The chunk is streamed in token tiles of TK = 128 tokens: a chunk of 256
+// spans two tiles, a tile holds two chunks of 64 (halving the sequential
+// steps, whose fixed cost dominates at small batch x heads).  Per tile, the
 // B columns n0..n0+BN-1 are staged once, exact, and serve all HB heads; the
 // decay weight is folded into x instead:
 //   P^T[n][p] = sum_t B[t][n] (w_t x_t[p]),  w_t = dt_t 2^{g_last - g_t},
@@ -91,8 +93,9 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
     const float* __restrict__ dt_t, const float* __restrict__ g,
     const float* __restrict__ init, float* __restrict__ states,
     float* __restrict__ final_state, int L, int H, int G, int nc) {
-  constexpr int TK = T < 128 ? T : 128;        // tokens per tile
-  constexpr int R = T / TK;                    // tiles per chunk
+  constexpr int TK = 128;                      // tokens per tile
+  constexpr int R = T > TK ? T / TK : 1;       // tiles per chunk
+  constexpr int CPT = T < TK ? TK / T : 1;     // chunks per tile
   constexpr int WPH = BfTile<HB, BN, NBW>::WPH;
   constexpr int NTHR = BfTile<HB, BN, NBW>::NTHR;
   constexpr int XS = 16;                       // w o x row stride (bf16)
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
   const int hh = wave / WPH;                   // this wave's head in the block
   const int nb0 = (wave % WPH) * NBW;          // its first 16-column block
   const int h = h0 + hh;
-  const int ntiles = nc * R;
+  const int ntiles = R > 1 ? nc * R : (nc + CPT - 1) / CPT;
 
   // Buffer descriptors.  x and B: reads past the sequence's last token
   // return zero.  g and dt_t: the HB heads' rows, [hh][L]; token indices at
@@ -176,13 +179,13 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
     u32x4 x[XU];
     float g[XU], dt[XU], gl[XU];
     u32x4 b[BU];
-    float dl;
+    float dl[CPT];
   };
 
   auto issue = [&](int k, Tile& tl) {
-    const int c = k / R;
+    // the tile's first chunk; a token t of the tile lies in chunk c + t / T
+    const int c = R > 1 ? k / R : k * CPT;
     const uint32_t t0 = (uint32_t)(k * TK);
-    const uint32_t tlast = (uint32_t)(min(c * T + T, L) - 1);
 #pragma unroll
     for (int i = 0; i < XU; ++i) {
       tl.x[i] = load_b128(xr, xoff[i] + t0 * xstep);
@@ -190,11 +193,15 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
       const uint32_t go = tt < (uint32_t)L ? (ghead[i] + tt) * 4u : kPastRange;
       tl.g[i] = load_f32(gr, go);
       tl.dt[i] = load_f32(dr, go);
+      const int cu = c + (CPT > 1 ? (int)(gtok[i] % TK) / T : 0);
+      const uint32_t tlast = (uint32_t)(min(cu * T + T, L) - 1);
       tl.gl[i] = load_f32(gr, (ghead[i] + tlast) * 4u);
     }
 #pragma unroll
     for (int i = 0; i < BU; ++i) tl.b[i] = load_b128(br, boff[i] + t0 * bstep);
-    tl.dl = load_f32(gr, ((uint32_t)hh * L + tlast) * 4u);
+#pragma unroll
+    for (int part = 0; part < CPT; ++part)
+      tl.dl[part] = load_f32(gr, ((uint32_t)hh * L + (uint32_t)(min((c + part) * T + T, L) - 1)) * 4u);
   };
 
   // B (as loaded) and the split w o x of a tile into LDS buffer `buf`.
@@ -223,47 +230,58 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
   const int brd = rsel * BS + 16 * nb0 + csel;
 
   f32x4 ph[NBW], pl[NBW];
-  // One step of the sequential pass for tile k: the state store at a chunk
-  // start, tile k's matrix products from LDS buffer k & 1, the staging of
-  // tile k + 1 into the other buffer (independent of the products, so the
-  // two overlap), the state update S = 2^{g_last} S + P at a chunk end, and
-  // one barrier.
+  // One step of the sequential pass for tile k: for each chunk part of the
+  // tile, the state store at a chunk start, the part's matrix products from
+  // LDS buffer k & 1 and the state update S = 2^{g_last} S + P at a chunk
+  // end; then the staging of tile k + 1 into the other buffer and one
+  // barrier.
   auto step = [&](int k, const Tile& cur, const Tile& next) {
-    const int sub = k % R;
-    if (sub == 0) {
-      float* dst = states + (((size_t)b * H + h) * nc + k / R) * kHeadDim * N +
-                   (size_t)(p0 + lr) * N + n0 + 16 * nb0 + 4 * lq;
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        *(f32x4*)(dst + 16 * j) = acc[j];
-        ph[j] = pl[j] = (f32x4){0, 0, 0, 0};
-      }
-    }
     const int buf = k & 1;
+    // The tile's token k-steps: part `part` (one chunk of T tokens when a
+    // tile holds several chunks) covers k-steps [part T/32, (part+1) T/32).
+    constexpr int KPP = TK / 32 / CPT;
 #pragma unroll
-    for (int kk = 0; kk < TK / 32; ++kk) {
-      const u32x2 a0 = lds_read_tr16(whs[buf] + wrd + 32 * kk * XS);
-      const u32x2 a1 = lds_read_tr16(whs[buf] + wrd + (32 * kk + 16) * XS);
-      const u32x2 c0 = lds_read_tr16(wls[buf] + wrd + 32 * kk * XS);
-      const u32x2 c1 = lds_read_tr16(wls[buf] + wrd + (32 * kk + 16) * XS);
-      const u32x4 wxh = {a0[0], a0[1], a1[0], a1[1]};
-      const u32x4 wxl = {c0[0], c0[1], c1[0], c1[1]};
+    for (int part = 0; part < CPT; ++part) {
+      const int c = R > 1 ? k / R : k * CPT + part;      // chunk of this part
+      const bool first = R > 1 ? k % R == 0 : true;      // the chunk starts here
+      const bool last = R > 1 ? k % R == R - 1 : true;   // the chunk ends here
+      if (c < nc) {
+        if (first) {
+          float* dst = states + (((size_t)b * H + h) * nc + c) * kHeadDim * N +
+                       (size_t)(p0 + lr) * N + n0 + 16 * nb0 + 4 * lq;
 #pragma unroll
-      for (int j = 0; j < NBW; ++j) {
-        const int o0 = brd + 32 * kk * BS + 16 * j;
-        const u32x2 e0 = lds_read_tr16(bts[buf] + o0);
-        const u32x2 e1 = lds_read_tr16(bts[buf] + o0 + 16 * BS);
-        const u32x4 bv = {e0[0], e0[1], e1[0], e1[1]};
-        ph[j] = mfma_bf16(bv, wxh, ph[j]);
-        pl[j] = mfma_bf16(bv, wxl, pl[j]);
+          for (int j = 0; j < NBW; ++j) {
+            *(f32x4*)(dst + 16 * j) = acc[j];
+            ph[j] = pl[j] = (f32x4){0, 0, 0, 0};
+          }
+        }
+#pragma unroll
+        for (int kq = 0; kq < KPP; ++kq) {
+          const int kk = part * KPP + kq;
+          const u32x2 a0 = lds_read_tr16(whs[buf] + wrd + 32 * kk * XS);
+          const u32x2 a1 = lds_read_tr16(whs[buf] + wrd + (32 * kk + 16) * XS);
+          const u32x2 c0 = lds_read_tr16(wls[buf] + wrd + 32 * kk * XS);
+          const u32x2 c1 = lds_read_tr16(wls[buf] + wrd + (32 * kk + 16) * XS);
+          const u32x4 wxh = {a0[0], a0[1], a1[0], a1[1]};
+          const u32x4 wxl = {c0[0], c0[1], c1[0], c1[1]};
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) {
+            const int o0 = brd + 32 * kk * BS + 16 * j;
+            const u32x2 e0 = lds_read_tr16(bts[buf] + o0);
+            const u32x2 e1 = lds_read_tr16(bts[buf] + o0 + 16 * BS);
+            const u32x4 bv = {e0[0], e0[1], e1[0], e1[1]};
+            ph[j] = mfma_bf16(bv, wxh, ph[j]);
+            pl[j] = mfma_bf16(bv, wxl, pl[j]);
+          }
+        }
+        if (last) {
+          const float decay = exp2_hw(cur.dl[part]);
+#pragma unroll
+          for (int j = 0; j < NBW; ++j) acc[j] = decay * acc[j] + (ph[j] + pl[j]);
+        }
       }
     }
     if (k + 1 < ntiles) commit(buf ^ 1, next);
-    if (sub == R - 1) {
-      const float decay = exp2_hw(cur.dl);
-#pragma unroll
-      for (int j = 0; j < NBW; ++j) acc[j] = decay * acc[j] + (ph[j] + pl[j]);
-    }
     __syncthreads();
   };
 
@@ -531,7 +549,12 @@ int launch_bf(const uint16_t* x, const uint16_t* B, const float* dt_t, const flo
               const float* init, float* states, float* fin, const Shape& s,
               hipStream_t st) {
   constexpr int NTHR = BfTile<HB, BN, NBW>::NTHR;
-  constexpr int Q = 2;   // tiles per group (measured: deeper is no faster)
+  // tiles per group: two, unless one tile's registers are many (deeper
+  // groups measured no faster)
+  constexpr int CPT = T < 128 ? 128 / T : 1;
+  constexpr int XU = (HB * 128 * 2 + NTHR - 1) / NTHR;
+  constexpr int BU = (128 * (BN / 8) + NTHR - 1) / NTHR;
+  constexpr int Q = 7 * XU + 4 * BU + CPT <= 24 ? 2 : 1;
   const unsigned blocks =
       (unsigned)(s.batch * (s.nheads / HB) * (kHeadDim / 16) * (N / BN));
   hipLaunchKernelGGL((state_pass_bf16<T, N, HB, BN, NBW, Q>), dim3(blocks), dim3(NTHR), 0,
