@@ -58,6 +58,9 @@ def _load():
                                              + [ctypes.c_void_p, i64,
                                                 ctypes.c_int])
             lib.oracle_chunk_out.restype = None
+            lib.oracle_causal_conv1d.argtypes = [f32p, f32p, ctypes.c_void_p,
+                                                 f64p, i64, i64, i64, i64]
+            lib.oracle_causal_conv1d.restype = None
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
@@ -164,3 +167,20 @@ def chunk_out(x, dt, A, B, C, D, states, *, chunk_size: int,
     if pairs is None:
         return y.reshape(b, H, L, P).transpose(0, 2, 1, 3)
     return y
+
+
+def causal_conv1d(x: np.ndarray, weight: np.ndarray,
+                  bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Causal depthwise conv1d in fp64: x [batch, dim, seqlen], weight
+    [dim, width], bias [dim] or None -> out [batch, dim, seqlen]."""
+    lib = _load()
+    x = _f32(x)
+    weight = _f32(weight)
+    b, d, L = x.shape
+    W = weight.shape[1]
+    assert weight.shape == (d, W)
+    bb = None if bias is None else _f32(bias)
+    out = np.empty((b, d, L), np.float64)
+    lib.oracle_causal_conv1d(_ptr(x), _ptr(weight), _ptr(bb), _ptr(out),
+                             b, d, L, W)
+    return out

@@ -191,6 +191,36 @@ void oracle_chunk_out(const float *x, const float *dt, const float *A,
     }
 }
 
+/*
+ * Causal depthwise 1-D convolution, the Mamba-2 block step upstream of the
+ * SSD (page 3, the Helion hackathon gallery, its causal_conv1d entries: each
+ * channel is convolved on its own with a short filter of W taps, the input
+ * padded with zeros on the left):
+ *   out[b,d,t] = bias[d] + sum_{k=0}^{W-1} weight[d,k] * x[b,d,t-W+1+k],
+ * where x at a negative time index is zero.  No activation is applied (the
+ * page's formula has none).
+ *   x, out [batch, dim, seqlen]; weight [dim, width]; bias [dim] or NULL.
+ */
+void oracle_causal_conv1d(const float *x, const float *weight, const float *bias,
+                          double *out, int64_t batch, int64_t dim,
+                          int64_t seqlen, int64_t width)
+{
+    for (int64_t b = 0; b < batch; ++b) {
+        for (int64_t d = 0; d < dim; ++d) {
+            const float *row = x + (b * dim + d) * seqlen;
+            double *o = out + (b * dim + d) * seqlen;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                double acc = bias ? (double)bias[d] : 0.0;
+                for (int64_t k = 0; k < width; ++k) {
+                    const int64_t s = t - width + 1 + k;
+                    if (s >= 0) acc += (double)weight[d * width + k] * (double)row[s];
+                }
+                o[t] = acc;
+            }
+        }
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
