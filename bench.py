@@ -130,7 +130,8 @@ def main() -> int:
     import torch
 
     import mamba_ssd_chunked_fwd_amd as ssd
-    from ssd_workloads import WORKLOADS, make_inputs
+    from ssd_workloads import (WORKLOADS, conv_workload_for, make_conv_inputs,
+                               make_inputs)
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -239,6 +240,33 @@ def main() -> int:
     dec_bytes = (8 * b * H * P * N + (2 if w.dtype == "bf16" else 4) * (b * H * P + 2 * b * G * N)
                  + 4 * b * H + 8 * H + y_bytes * b * H * P)
 
+    # ---- the causal depthwise conv1d that feeds this layer's SSD (over the
+    #      x, B and C channels), x and out in the workload's storage type
+    cw = conv_workload_for(w)
+    cinp = make_conv_inputs(cw, seed=7)
+    cx0 = torch.from_numpy(cinp["x"]).to(dev, tin)
+    cwt = torch.from_numpy(cinp["weight"]).to(dev)
+    cbias = torch.from_numpy(cinp["bias"]).to(dev)
+    cset_bytes = 2 * cx0.numel() * cx0.element_size()
+    nconv = max(2, min(16, -(-(1 << 30) // cset_bytes)))
+    conv_sets = [((cx0 if i == 0 else cx0.clone()), torch.empty_like(cx0)) for i in range(nconv)]
+    for i in range(5):
+        cx, co = conv_sets[i % nconv]
+        ssd.ssd_causal_conv1d(cx, cwt, cbias, co)
+    nconv_steps = max(50, args.steps)
+    conv_ev = [torch.cuda.Event(enable_timing=True) for _ in range(nconv_steps + 1)]
+    torch.cuda.synchronize()
+    conv_ev[0].record(stream)
+    for i in range(nconv_steps):
+        cx, co = conv_sets[i % nconv]
+        ssd.ssd_causal_conv1d(cx, cwt, cbias, co)
+        conv_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    conv_ms = statistics.mean(conv_ev[i].elapsed_time(conv_ev[i + 1])
+                              for i in range(nconv_steps))
+    conv_bytes = cset_bytes + 4 * cw.dim * (cw.width + 1)
+    del conv_sets
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -292,6 +320,13 @@ def main() -> int:
                         "GB_per_s": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
                         "hbm_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "note": "one token for each of the batch's sequences, state in place"},
+        "causal_conv1d": {"ms": round(conv_ms, 5),
+                          "shape": {"batch": cw.batch, "dim": cw.dim, "seqlen": cw.seqlen,
+                                    "width": cw.width, "dtype": cw.dtype},
+                          "alg_bytes": conv_bytes,
+                          "GB_per_s": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "note": "the conv over the layer's x, B, C channels; not part of the step"},
         "effective_TFLOP_per_s": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
     }

@@ -7,6 +7,7 @@
  *        NVIDIA CUDA Tile" (trishampatil.com)
  *   [P2] the zhiding.cn rendering of the same write-up, section
  *        "Mamba-2架构" (where the display formulas survive)
+ *   [P3] the Helion hackathon project gallery (cerebralvalley.ai)
  *
  * The method.  Per batch b and head h, with group g = h / (nheads/ngroups):
  *     S_t = exp(A_h dt_t) S_{t-1} + dt_t x_t B_t^T      (state, headdim x dstate)
@@ -174,6 +175,26 @@ ssd_status ssd_decode_step(const void *x, const float *dt, const float *A,
                            const void *B, const void *C, const float *D,
                            float *state, void *y, int in_dtype, int y_dtype,
                            const ssd_dims *dims, void *stream);
+
+/*
+ * The causal depthwise conv1d of the Mamba block, upstream of the SSD [P3,
+ * the causal_conv1d entries]: each channel row is filtered on its own over
+ * the current and the width-1 previous tokens, with zeros before the first
+ * token:
+ *   out[b,d,t] = bias[d] + sum_{k=0}^{width-1} weight[d,k] x[b,d,t-width+1+k]
+ * No activation is applied.  Arithmetic is fp32.
+ *   x [batch, dim, seqlen] x_dtype (read)       weight [dim, width] fp32
+ *   bias [dim] fp32 or NULL (no bias)           out [batch, dim, seqlen] out_dtype
+ * The size arguments replace ssd_dims (this op has no heads or state).
+ * Supported: width 1..4 (the gallery's filters have 3 or 4 taps) and seqlen
+ * up to 2^29 - 2^14; wider filters or longer rows return
+ * SSD_ERR_UNSUPPORTED.  out must not overlap x.  Any seqlen works; rows
+ * whose byte length is a multiple of 16 take the vectorised kernel.
+ */
+ssd_status ssd_causal_conv1d(const void *x, const float *weight,
+                             const float *bias, void *out, int64_t batch,
+                             int64_t dim, int64_t seqlen, int64_t width,
+                             int x_dtype, int out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

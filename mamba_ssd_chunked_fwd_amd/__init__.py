@@ -6,7 +6,8 @@ tensor shapes/dtypes, builds the dims struct and passes device pointers and
 the current HIP stream.  PyTorch supplies device memory and streams.
 
 Entry points (same names as the C ABI):
-  ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_compute_out, ssd_forward
+  ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_compute_out, ssd_forward,
+  ssd_decode_step, ssd_causal_conv1d
 and the allocating convenience wrapper ``forward``.
 
 Importing fails loudly (ImportError) when libssd.so has not been built:
@@ -69,6 +70,9 @@ def _load() -> ctypes.CDLL:
     lib.ssd_forward.restype = i
     lib.ssd_decode_step.argtypes = [vp] * 8 + [i, i, dims, vp]
     lib.ssd_decode_step.restype = i
+    i64 = ctypes.c_int64
+    lib.ssd_causal_conv1d.argtypes = [vp] * 4 + [i64] * 4 + [i, i, vp]
+    lib.ssd_causal_conv1d.restype = i
     return lib
 
 
@@ -85,7 +89,7 @@ def header_functions() -> list:
     text = open(HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
-                      r"(ssd_[a-z_]+)\s*\(", text, flags=re.M)
+                      r"(ssd_[a-z0-9_]+)\s*\(", text, flags=re.M)
 
 
 def status_string(status: int) -> str:
@@ -280,6 +284,29 @@ def ssd_decode_step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
         _ptr(y), _dtype_code(x.dtype), _dtype_code(y.dtype), ctypes.byref(d),
         _stream(dev)), "ssd_decode_step")
+
+
+def ssd_causal_conv1d(x: torch.Tensor, weight: torch.Tensor,
+                      bias: Optional[torch.Tensor], out: torch.Tensor) -> None:
+    """Causal depthwise conv1d: x [batch, dim, seqlen] (fp32 or bf16),
+    weight [dim, width] fp32, bias [dim] fp32 or None; writes ``out``
+    [batch, dim, seqlen] (fp32 or bf16)."""
+    if x.dim() != 3 or weight.dim() != 2:
+        raise ValueError("x must be [batch, dim, seqlen] and weight "
+                         "[dim, width]")
+    b, dim, L = x.shape
+    W = weight.shape[1]
+    dev = x.device
+    ins = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _check(x, "x", None, ins)
+    _check(weight, "weight", (dim, W), f32, dev)
+    _check(bias, "bias", (dim,), f32, dev, optional=True)
+    _check(out, "out", (b, dim, L), ins, dev)
+    _raise(_lib.ssd_causal_conv1d(
+        _ptr(x), _ptr(weight), _ptr(bias), _ptr(out), b, dim, L, W,
+        _dtype_code(x.dtype), _dtype_code(out.dtype), _stream(dev)),
+        "ssd_causal_conv1d")
 
 
 # ------------------------------------------------------------ convenience

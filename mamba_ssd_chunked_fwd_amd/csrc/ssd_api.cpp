@@ -174,4 +174,22 @@ ssd_status ssd_decode_step(const void* x, const float* dt, const float* A,
                                           y_dtype == SSD_BF16, s, stream));
 }
 
+ssd_status ssd_causal_conv1d(const void* x, const float* weight, const float* bias, void* out,
+                             int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
+                             int x_dtype, int out_dtype, void* stream) {
+  if (batch < 1 || dim < 1 || seqlen < 1 || width < 1) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_dtype(x_dtype) || !ok_dtype(out_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(x) || !ok_ptr(weight) || !ok_opt(bias) || !ok_ptr(out))
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (width > 4) return SSD_ERR_UNSUPPORTED;
+  // A row is addressed with 32-bit byte offsets (fp32 rows plus one
+  // wavefront run of slack); the element count must not overflow.
+  if (seqlen > ((int64_t)1 << 29) - (1 << 14)) return SSD_ERR_UNSUPPORTED;
+  if (batch > ((int64_t)1 << 40) / dim || batch * dim > ((int64_t)1 << 44) / seqlen)
+    return SSD_ERR_UNSUPPORTED;
+  return from_hip(ssd::launch_causal_conv1d(x, weight, bias, out, batch, dim, seqlen,
+                                            (int)width, x_dtype == SSD_BF16,
+                                            out_dtype == SSD_BF16, stream));
+}
+
 }  // extern "C"

@@ -1,4 +1,4 @@
-// ssd_launch.h -- host-side launchers of the three stage kernels (internal to
+// ssd_launch.h -- host-side launchers of the kernels (internal to
 // libssd).  Arguments arrive already validated by the C ABI layer; each
 // launcher returns the hipError_t of its launch as an int (0 = success).
 #pragma once
@@ -29,5 +29,9 @@ int launch_compute_out(const void* x, const void* B, const void* C,
 int launch_decode_step(const void* x, const float* dt, const float* A, const void* B,
                        const void* C, const float* D, float* state, void* y, bool bf16_in,
                        bool bf16_out, const Shape& s, void* stream);
+
+int launch_causal_conv1d(const void* x, const float* weight, const float* bias, void* out,
+                         int64_t batch, int64_t dim, int64_t seqlen, int width, bool bf16_in,
+                         bool bf16_out, void* stream);
 
 }  // namespace ssd

@@ -130,6 +130,43 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Dict[str, np.ndarray
             "init_state": init}
 
 
+@dataclasses.dataclass(frozen=True)
+class ConvWorkload:
+    """Shape of the Mamba block's causal depthwise conv1d, x [batch, dim,
+    seqlen].  In a Mamba-2 layer the conv runs over the channels that become
+    x, B and C: dim = nheads * headdim + 2 * ngroups * dstate."""
+    name: str
+    batch: int
+    dim: int
+    seqlen: int
+    width: int
+    dtype: str        # storage type of x (and of the output the bench times)
+    bias: bool = True
+
+
+def conv_workload_for(w: Workload, width: int = 4) -> ConvWorkload:
+    """The conv1d that feeds workload ``w``'s SSD (same batch, seqlen, dtype)."""
+    dim = w.nheads * w.headdim + 2 * w.ngroups * w.dstate
+    return ConvWorkload("conv_" + w.name, w.batch, dim, w.seqlen, width, w.dtype)
+
+
+def make_conv_inputs(c: ConvWorkload, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Draw x [batch, dim, seqlen] ~ N(0, 1) (rounded to bf16 for bf16
+    workloads), weight [dim, width] and bias [dim] ~ U(-k, k), k =
+    1/sqrt(width) (the fan-in scale of a depthwise filter).  Draw order: x,
+    weight, bias.  Returns float32 arrays; bias is None without a bias."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((c.batch, c.dim, c.seqlen), dtype=np.float32)
+    k = 1.0 / np.sqrt(c.width)
+    weight = rng.uniform(-k, k, size=(c.dim, c.width)).astype(np.float32)
+    bias = rng.uniform(-k, k, size=c.dim).astype(np.float32)
+    if c.dtype == "bf16":
+        x = round_to_bf16(x)
+    elif c.dtype != "fp32":
+        raise ValueError(f"unknown dtype {c.dtype!r}")
+    return {"x": x, "weight": weight, "bias": bias if c.bias else None}
+
+
 def small_variant(w: Workload, **kw) -> Workload:
     """A reduced copy of ``w`` (same dtype and distributions)."""
     return w.with_(name=w.name + "_small", **kw)

@@ -39,7 +39,8 @@ def test_every_declared_function_is_exported():
     names = ssd.header_functions()
     assert set(names) == {"ssd_status_string", "ssd_forward_workspace_bytes",
                           "ssd_chunk_cumsum", "ssd_fwd_pass_state",
-                          "ssd_compute_out", "ssd_forward", "ssd_decode_step"}
+                          "ssd_compute_out", "ssd_forward", "ssd_decode_step",
+                          "ssd_causal_conv1d"}
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -128,6 +129,25 @@ def test_decode_step_validates():
     assert call(dims(dstate=96)) == UNS
     assert call(dims(headdim=128)) == UNS
     assert call(dims(nheads=5)) == INV          # 5 heads, 2 groups
+
+
+def test_causal_conv1d_validates():
+    def call(b=2, d=8, L=64, W=4, **o):
+        return lib.ssd_causal_conv1d(
+            o.get("x", FAKE), o.get("w", FAKE), o.get("bias", FAKE),
+            o.get("out", FAKE), b, d, L, W, o.get("xd", ssd.SSD_BF16),
+            o.get("od", ssd.SSD_BF16), None)
+    for name in ("x", "w", "out"):
+        assert call(**{name: None}) == INV, name
+        assert call(**{name: MISALIGNED}) == INV, name
+    assert call(bias=MISALIGNED) == INV
+    for kw in (dict(b=0), dict(d=0), dict(L=0), dict(W=0), dict(L=-5)):
+        assert call(**kw) == INV, kw
+    assert call(xd=2) == INV
+    assert call(od=-1) == INV
+    assert call(W=5) == UNS
+    assert call(L=1 << 29) == UNS
+    assert call(b=1 << 30, d=1 << 12, L=1 << 12) == UNS
 
 
 def test_stage_entry_points_validate():
