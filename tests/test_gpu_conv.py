@@ -68,7 +68,7 @@ CASES = [
     ("bf16", "fp32", 2, 3, 1000, 4, True),    # L % 8 = 0, 125 units
     ("bf16", "bf16", 2, 3, 1001, 4, True),    # per-token kernel
     ("bf16", "bf16", 2, 6, 3, 4, True),       # shorter than the filter
-    ("fp32", "fp32", 2, 5, 2048, 4, True),    # two runs per row
+    ("fp32", "fp32", 2, 5, 2048, 4, True),    # eight runs per row
     ("fp32", "bf16", 2, 3, 1028, 3, True),    # ragged last run
     ("fp32", "fp32", 1, 4, 1030, 4, False),   # per-token kernel
     ("fp32", "fp32", 3, 2, 1, 4, True),       # one token
@@ -98,16 +98,17 @@ def test_conv_small_layer_full_size(ssd, odt):
     _check(_run(ssd, inp, c.dtype, odt), inp, odt, "conv full")
 
 
-def test_conv_impulse_places_taps(ssd):
-    """A unit impulse at a run boundary: the taps land in reverse order on
-    the impulse and the W-1 tokens after it, in every row independently."""
+@pytest.mark.parametrize("xdt,t0", [("bf16", 2047), ("fp32", 255)])
+def test_conv_impulse_places_taps(ssd, xdt, t0):
+    """A unit impulse on the last token of a wavefront's run (2048 bf16 or
+    256 fp32 tokens): the taps land in reverse order on the impulse and the
+    W-1 tokens after it, in every row independently."""
     b, dim, L, W = 1, 3, 4096, 4
     x = np.zeros((b, dim, L), np.float32)
-    t0 = 2047                                  # last token of the first run
     x[0, :, t0] = 1.0
     w = np.arange(1, dim * W + 1, dtype=np.float32).reshape(dim, W)
     inp = {"x": x, "weight": w, "bias": None}
-    got = _run(ssd, inp, "bf16", "fp32")
+    got = _run(ssd, inp, xdt, "fp32")
     expect = np.zeros_like(got)
     for j in range(W):
         expect[0, :, t0 + j] = w[:, W - 1 - j]
