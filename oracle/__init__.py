@@ -61,6 +61,14 @@ def _load():
             lib.oracle_causal_conv1d.argtypes = [f32p, f32p, ctypes.c_void_p,
                                                  f64p, i64, i64, i64, i64]
             lib.oracle_causal_conv1d.restype = None
+            lib.oracle_gdn_chunk_fwd_h.argtypes = ([f32p] * 4 + [ctypes.c_void_p, f64p, f64p,
+                                                   ctypes.c_void_p] + [i64] * 6
+                                                  + [ctypes.c_int])
+            lib.oracle_gdn_chunk_fwd_h.restype = None
+            lib.oracle_gdn_chunk_fwd_o.argtypes = ([f32p, f32p, f64p, f64p, f32p, f64p,
+                                                   ctypes.c_double] + [i64] * 6
+                                                  + [ctypes.c_int])
+            lib.oracle_gdn_chunk_fwd_o.restype = None
             lib.oracle_max_threads.argtypes = []
             lib.oracle_max_threads.restype = ctypes.c_int
             _lib = lib
@@ -184,3 +192,47 @@ def causal_conv1d(x: np.ndarray, weight: np.ndarray,
     lib.oracle_causal_conv1d(_ptr(x), _ptr(weight), _ptr(bb), _ptr(out),
                              b, d, L, W)
     return out
+
+
+def gdn_chunk_fwd_h(k, w, u, g, h0=None, *, chunk_size: int = 64,
+                    nthreads: int = 0) -> Dict[str, np.ndarray]:
+    """Gated DeltaNet inter-chunk state pass in fp64.
+
+    k, w [b, L, H, K]; u [b, L, H, V]; g [b, L, H] (chunk-local cumulative
+    log-gates); h0 [b, H, K, V] or None.  Returns
+      h      [b, H, NT, K, V]  state at the start of each chunk
+      v_new  [b, L, H, V]      u - w h
+      final  [b, H, K, V]
+    """
+    lib = _load()
+    k, w, u, g = map(_f32, (k, w, u, g))
+    b, L, H, K = k.shape
+    V = u.shape[3]
+    assert w.shape == k.shape and u.shape[:3] == (b, L, H) and g.shape == (b, L, H)
+    h0 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64)
+    nt = -(-L // chunk_size)
+    h = np.empty((b, H, nt, K, V), np.float64)
+    vn = np.empty((b, L, H, V), np.float64)
+    fin = np.empty((b, H, K, V), np.float64)
+    lib.oracle_gdn_chunk_fwd_h(_ptr(k), _ptr(w), _ptr(u), _ptr(g), _ptr(h0),
+                               _ptr(h), _ptr(vn), _ptr(fin), b, L, H, K, V,
+                               chunk_size, nthreads)
+    return {"h": h, "v_new": vn, "final": fin}
+
+
+def gdn_chunk_fwd_o(q, k, v_new, h, g, *, scale: float = 1.0,
+                    chunk_size: int = 64, nthreads: int = 0) -> np.ndarray:
+    """Gated DeltaNet output in fp64: q, k [b, L, H, K]; v_new [b, L, H, V]
+    and h [b, H, NT, K, V] (any float type; used as doubles); g [b, L, H].
+    Returns o [b, L, H, V]."""
+    lib = _load()
+    q, k, g = map(_f32, (q, k, g))
+    v_new = np.ascontiguousarray(v_new, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    b, L, H, K = q.shape
+    V = v_new.shape[3]
+    o = np.empty((b, L, H, V), np.float64)
+    lib.oracle_gdn_chunk_fwd_o(_ptr(q), _ptr(k), _ptr(v_new), _ptr(h), _ptr(g),
+                               _ptr(o), float(scale), b, L, H, K, V, chunk_size,
+                               nthreads)
+    return o

@@ -221,6 +221,114 @@ void oracle_causal_conv1d(const float *x, const float *weight, const float *bias
     }
 }
 
+/*
+ * Gated DeltaNet, chunked forward: the inter-chunk state pass (chunk_fwd_h)
+ * and the output (chunk_fwd_o), taken in the order the Helion hackathon
+ * gallery states them (page 3, its gated_deltanet_chunk_fwd_h and
+ * gated_deltanet_chunk_fwd_o entries).  The state h is K x V per (b, h) and
+ * chunks have C tokens; per chunk c with tokens t in [t0, t1):
+ *   h_out[b,h,c] = h                                       (1) store h
+ *   v_new[t] = u[t] - w[t] h           (row vectors, 1xV)  (2)
+ *   h = exp(g_last) h + sum_t k[t]^T (exp(g_last - g[t]) v_new[t])   (3)-(5)
+ * with g_last = g at the chunk's last token (the last valid token of a
+ * ragged chunk).  g is the chunk-local cumulative sum of the log-gates
+ * (natural log, so exp), as the gate exp(g_last - g_t) implies; w and u are
+ * the WY-transformed keys and values (inputs here).  Output, per chunk:
+ *   o[t] = scale * ( exp(g[t]) q[t] h_out[b,h,c]
+ *                    + sum_{j in chunk, j <= t} (q[t] . k[j]) exp(g[t] - g[j]) v_new[j] )
+ * (the gallery's inter + intra terms; scale = 1 is its formula as written).
+ * Layouts: q, k, w [b, L, H, K]; u, v_new, o [b, L, H, V]; g [b, L, H];
+ * h0 and final [b, H, K, V]; h_out [b, H, NT, K, V], NT = ceil(L / C).
+ * h0 and final may be NULL (zero initial state / not wanted).
+ */
+void oracle_gdn_chunk_fwd_h(const float *k, const float *w, const float *u,
+                            const float *g, const double *h0, double *h_out,
+                            double *v_new, double *final_state, int64_t batch,
+                            int64_t seqlen, int64_t nheads, int64_t dk,
+                            int64_t dv, int64_t chunk, int nthreads)
+{
+    const int64_t nt = (seqlen + chunk - 1) / chunk;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#else
+    (void)nthreads;
+#endif
+    for (int64_t bh = 0; bh < batch * nheads; ++bh) {
+        const int64_t b = bh / nheads, hd = bh % nheads;
+        double *h = (double *)malloc((size_t)(dk * dv) * sizeof(double));
+        double *vn = (double *)malloc((size_t)(chunk * dv) * sizeof(double));
+        for (int64_t i = 0; i < dk * dv; ++i) h[i] = h0 ? h0[bh * dk * dv + i] : 0.0;
+        for (int64_t c = 0; c < nt; ++c) {
+            const int64_t t0 = c * chunk;
+            const int64_t t1 = t0 + chunk < seqlen ? t0 + chunk : seqlen;
+            memcpy(h_out + (bh * nt + c) * dk * dv, h, (size_t)(dk * dv) * sizeof(double));
+            for (int64_t t = t0; t < t1; ++t) {
+                const int64_t row = (b * seqlen + t) * nheads + hd;
+                for (int64_t j = 0; j < dv; ++j) {
+                    double acc = (double)u[row * dv + j];
+                    for (int64_t i = 0; i < dk; ++i)
+                        acc -= (double)w[row * dk + i] * h[i * dv + j];
+                    vn[(t - t0) * dv + j] = acc;
+                    v_new[row * dv + j] = acc;
+                }
+            }
+            const double gl = (double)g[(b * seqlen + t1 - 1) * nheads + hd];
+            const double decay = exp(gl);
+            for (int64_t i = 0; i < dk * dv; ++i) h[i] *= decay;
+            for (int64_t t = t0; t < t1; ++t) {
+                const int64_t row = (b * seqlen + t) * nheads + hd;
+                const double gate = exp(gl - (double)g[row]);
+                for (int64_t i = 0; i < dk; ++i) {
+                    const double ki = (double)k[row * dk + i] * gate;
+                    for (int64_t j = 0; j < dv; ++j) h[i * dv + j] += ki * vn[(t - t0) * dv + j];
+                }
+            }
+        }
+        if (final_state)
+            memcpy(final_state + bh * dk * dv, h, (size_t)(dk * dv) * sizeof(double));
+        free(h);
+        free(vn);
+    }
+}
+
+void oracle_gdn_chunk_fwd_o(const float *q, const float *k, const double *v_new,
+                            const double *h_out, const float *g, double *o,
+                            double scale, int64_t batch, int64_t seqlen,
+                            int64_t nheads, int64_t dk, int64_t dv,
+                            int64_t chunk, int nthreads)
+{
+    const int64_t nt = (seqlen + chunk - 1) / chunk;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#else
+    (void)nthreads;
+#endif
+    for (int64_t bh = 0; bh < batch * nheads; ++bh) {
+        const int64_t b = bh / nheads, hd = bh % nheads;
+        for (int64_t t = 0; t < seqlen; ++t) {
+            const int64_t c = t / chunk, t0 = c * chunk;
+            const int64_t row = (b * seqlen + t) * nheads + hd;
+            const double *hc = h_out + (bh * nt + c) * dk * dv;
+            const double gt = (double)g[row];
+            for (int64_t j = 0; j < dv; ++j) {
+                double inter = 0.0;
+                for (int64_t i = 0; i < dk; ++i) inter += (double)q[row * dk + i] * hc[i * dv + j];
+                double intra = 0.0;
+                for (int64_t s = t0; s <= t; ++s) {
+                    const int64_t rs = (b * seqlen + s) * nheads + hd;
+                    double qk = 0.0;
+                    for (int64_t i = 0; i < dk; ++i)
+                        qk += (double)q[row * dk + i] * (double)k[rs * dk + i];
+                    intra += qk * exp(gt - (double)g[rs]) * v_new[rs * dv + j];
+                }
+                o[row * dv + j] = scale * (exp(gt) * inter + intra);
+            }
+        }
+    }
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
