@@ -177,6 +177,43 @@ ssd_status ssd_decode_step(const void *x, const float *dt, const float *A,
                            const ssd_dims *dims, void *stream);
 
 /*
+ * Gated DeltaNet, chunked forward [P3, the gated_deltanet_chunk_fwd_h and
+ * gated_deltanet_chunk_fwd_o entries].  Problem shape: batch b, seqlen L,
+ * nheads H, key size dk (K), value size dv (V), chunk_size (C).  Supported:
+ * K and V in {64, 128}, C = 64, bf16 q/k/w/u; anything else valid returns
+ * SSD_ERR_UNSUPPORTED.  (L + 128) * H * max(K, V) * 4 must stay below 2 GiB.
+ */
+typedef struct {
+    int64_t batch;      /* b                                     */
+    int64_t seqlen;     /* L, tokens per sequence                 */
+    int64_t nheads;     /* H                                      */
+    int64_t dk;         /* K, key size (rows of the state)        */
+    int64_t dv;         /* V, value size (columns of the state)   */
+    int64_t chunk_size; /* C                                      */
+} ssd_gdn_dims;
+
+/*
+ * The inter-chunk state pass [P3, chunk_fwd_h]: per (b, h), h = h0 (zeros if
+ * NULL); for each chunk c of C tokens (the last may be shorter), in order:
+ *   h_out[b,h,c] = h
+ *   v_new[t] = u[t] - w[t] h                       (t in the chunk)
+ *   h = exp(g_last) h + sum_t k[t]^T (exp(g_last - g[t]) v_new[t])
+ * with g_last = g at the chunk's last valid token; final_state = h at the
+ * end.  g is the chunk-local cumulative sum of the per-token log-gates
+ * (natural log); w and u are the WY-transformed keys and values.
+ *   k, w [b, L, H, K] in_dtype      u [b, L, H, V] in_dtype     g [b, L, H] fp32
+ *   h0 [b, H, K, V] fp32 or NULL    h [b, H, nt, K, V] fp32 (written), nt = ceil(L / C)
+ *   v_new [b, L, H, V] v_dtype (written)   final_state [b, H, K, V] fp32 or NULL
+ * Arithmetic is fp32 (the fp32 state enters the matrix products as bf16
+ * hi + lo pairs).
+ */
+ssd_status ssd_gdn_chunk_fwd_h(const void *k, const void *w, const void *u,
+                               const float *g, const float *h0, float *h,
+                               void *v_new, float *final_state, int in_dtype,
+                               int v_dtype, const ssd_gdn_dims *dims,
+                               void *stream);
+
+/*
  * The causal depthwise conv1d of the Mamba block, upstream of the SSD [P3,
  * the causal_conv1d entries]: each channel row is filtered on its own over
  * the current and the width-1 previous tokens, with zeros before the first

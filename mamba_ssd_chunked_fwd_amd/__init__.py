@@ -7,7 +7,7 @@ the current HIP stream.  PyTorch supplies device memory and streams.
 
 Entry points (same names as the C ABI):
   ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_compute_out, ssd_forward,
-  ssd_decode_step, ssd_causal_conv1d
+  ssd_decode_step, ssd_causal_conv1d, ssd_gdn_chunk_fwd_h
 and the allocating convenience wrapper ``forward``.
 
 Importing fails loudly (ImportError) when libssd.so has not been built:
@@ -42,6 +42,12 @@ class SsdDims(ctypes.Structure):
                 ("chunk_size", ctypes.c_int64)]
 
 
+class GdnDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("dk", ctypes.c_int64),
+                ("dv", ctypes.c_int64), ("chunk_size", ctypes.c_int64)]
+
+
 class SsdError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -71,6 +77,9 @@ def _load() -> ctypes.CDLL:
     lib.ssd_decode_step.argtypes = [vp] * 8 + [i, i, dims, vp]
     lib.ssd_decode_step.restype = i
     i64 = ctypes.c_int64
+    gdims = ctypes.POINTER(GdnDims)
+    lib.ssd_gdn_chunk_fwd_h.argtypes = [vp] * 8 + [i, i, gdims, vp]
+    lib.ssd_gdn_chunk_fwd_h.restype = i
     lib.ssd_causal_conv1d.argtypes = [vp] * 4 + [i64] * 4 + [i, i, vp]
     lib.ssd_causal_conv1d.restype = i
     return lib
@@ -284,6 +293,38 @@ def ssd_decode_step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
         _ptr(y), _dtype_code(x.dtype), _dtype_code(y.dtype), ctypes.byref(d),
         _stream(dev)), "ssd_decode_step")
+
+
+def ssd_gdn_chunk_fwd_h(k: torch.Tensor, w: torch.Tensor, u: torch.Tensor,
+                        g: torch.Tensor, h0: Optional[torch.Tensor],
+                        h: torch.Tensor, v_new: torch.Tensor,
+                        final_state: Optional[torch.Tensor],
+                        chunk_size: int = 64) -> None:
+    """Gated DeltaNet state pass: k, w [b, L, H, K] and u [b, L, H, V] (bf16),
+    g [b, L, H] fp32, h0 [b, H, K, V] fp32 or None; writes h [b, H, nt, K, V]
+    fp32, v_new [b, L, H, V] (fp32 or bf16) and final_state (or None)."""
+    if k.dim() != 4 or u.dim() != 4:
+        raise ValueError("k must be [batch, seqlen, nheads, dk] and u "
+                         "[batch, seqlen, nheads, dv]")
+    b, L, H, K = k.shape
+    V = u.shape[3]
+    nt = -(-L // chunk_size)
+    dev = k.device
+    ins = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _check(k, "k", None, ins)
+    _check(w, "w", (b, L, H, K), (k.dtype,), dev)
+    _check(u, "u", (b, L, H, V), (k.dtype,), dev)
+    _check(g, "g", (b, L, H), f32, dev)
+    _check(h0, "h0", (b, H, K, V), f32, dev, optional=True)
+    _check(h, "h", (b, H, nt, K, V), f32, dev)
+    _check(v_new, "v_new", (b, L, H, V), ins, dev)
+    _check(final_state, "final_state", (b, H, K, V), f32, dev, optional=True)
+    d = GdnDims(b, L, H, K, V, chunk_size)
+    _raise(_lib.ssd_gdn_chunk_fwd_h(
+        _ptr(k), _ptr(w), _ptr(u), _ptr(g), _ptr(h0), _ptr(h), _ptr(v_new),
+        _ptr(final_state), _dtype_code(k.dtype), _dtype_code(v_new.dtype),
+        ctypes.byref(d), _stream(dev)), "ssd_gdn_chunk_fwd_h")
 
 
 def ssd_causal_conv1d(x: torch.Tensor, weight: torch.Tensor,

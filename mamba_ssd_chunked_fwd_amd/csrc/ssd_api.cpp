@@ -50,6 +50,26 @@ ssd_status check_dims(const ssd_dims* d, ssd::Shape* out) {
 
 bool ok_dtype(int t) { return t == SSD_F32 || t == SSD_BF16; }
 
+ssd_status check_gdn_dims(const ssd_gdn_dims* d, ssd::GdnShape* out) {
+  if (d == nullptr) return SSD_ERR_INVALID_ARGUMENT;
+  const int64_t v[6] = {d->batch, d->seqlen, d->nheads, d->dk, d->dv, d->chunk_size};
+  for (int64_t e : v)
+    if (e < 1 || e > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  if (d->batch * d->seqlen > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  const int64_t nt = (d->seqlen + 63) / 64;
+  if (d->batch * d->nheads * (nt > 8 ? nt : 8) > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  if (d->chunk_size != 64) return SSD_ERR_UNSUPPORTED;
+  if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128))
+    return SSD_ERR_UNSUPPORTED;
+  // Each sequence is addressed with 32-bit byte offsets, up to two chunks
+  // past its end.
+  const int64_t span = d->seqlen + 128;
+  const int64_t wide = d->dk > d->dv ? d->dk : d->dv;
+  if (span * d->nheads * wide * 4 >= INT32_MAX) return SSD_ERR_UNSUPPORTED;
+  if (out) *out = ssd::GdnShape{d->batch, d->seqlen, d->nheads, d->dk, d->dv};
+  return SSD_OK;
+}
+
 ssd_status from_hip(int err) { return err == 0 ? SSD_OK : SSD_ERR_HIP; }
 
 }  // namespace
@@ -172,6 +192,22 @@ ssd_status ssd_decode_step(const void* x, const float* dt, const float* A,
     return SSD_ERR_INVALID_ARGUMENT;
   return from_hip(ssd::launch_decode_step(x, dt, A, B, C, D, state, y, in_dtype == SSD_BF16,
                                           y_dtype == SSD_BF16, s, stream));
+}
+
+ssd_status ssd_gdn_chunk_fwd_h(const void* k, const void* w, const void* u, const float* g,
+                               const float* h0, float* h, void* v_new, float* final_state,
+                               int in_dtype, int v_dtype, const ssd_gdn_dims* dims,
+                               void* stream) {
+  ssd::GdnShape s;
+  const ssd_status st = check_gdn_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype) || !ok_dtype(v_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(k) || !ok_ptr(w) || !ok_ptr(u) || !ok_ptr(g) || !ok_opt(h0) || !ok_ptr(h) ||
+      !ok_ptr(v_new) || !ok_opt(final_state))
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (in_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+  return from_hip(ssd::launch_gdn_fwd_h(k, w, u, g, h0, h, v_new, final_state,
+                                        v_dtype == SSD_BF16, s, stream));
 }
 
 ssd_status ssd_causal_conv1d(const void* x, const float* weight, const float* bias, void* out,

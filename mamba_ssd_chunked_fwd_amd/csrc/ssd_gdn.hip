@@ -1,0 +1,324 @@
+// Gated DeltaNet, chunked forward: the inter-chunk state pass (chunk_fwd_h)
+// and the per-chunk output (chunk_fwd_o), as the Helion hackathon gallery
+// describes them (its gated_deltanet_chunk_fwd_h and chunk_fwd_o entries).
+// The state h is K x V per (batch, head); chunks have C = 64 tokens.  Per
+// chunk, with g the chunk-local cumulative log-gate and g_last its value at
+// the chunk's last (valid) token:
+//   h_out[c] = h;   v_new = u - w h;   h = e^{g_last} h + k^T (e^{g_last - g} o v_new)
+//   o = scale (e^{g} o (q h_out[c]) + causal(q k^T o e^{g_i - g_j}) v_new)
+// w and u are the WY-transformed keys and values; they are inputs here.
+//
+// MI355X design (bf16 inputs; fp32 state and accumulation).
+// chunk_fwd_h: one workgroup owns the state columns of one (b, h) v-tile of
+// 16 NW columns and walks the chunks in order; wave w owns 16 columns, all
+// K rows, as K/16 accumulator blocks H[K][v] (lane: column v, four
+// consecutive K).  Both products of a chunk take an operand straight from
+// accumulators:
+//   v_new = u - w h: for lane group q the k-slots carry K = 32kk + 4q + 0..3
+//     and 32kk + 16 + 4q + 0..3, exactly the rows two state blocks hold, so
+//     the state (split bf16 hi + lo) is the B operand as it sits; w is read
+//     from LDS as two 8-byte pieces per lane.
+//   h += k^T v_gated: the v_new accumulator blocks hold, per lane, four
+//     consecutive tokens of one column, again the k-slot map, so the gated
+//     v_new (split hi + lo) is the B operand as it sits; k^T comes from the
+//     LDS transpose read.
+// So the sequential chain of a wave never leaves registers except for the
+// stores.  The state and v_new are written with 16-byte stores after a
+// per-wave transpose through LDS.  The w, k and u tiles of the next chunk
+// are loaded into registers while the current one is processed, then staged
+// into the other half of a double-buffered LDS tile set (one barrier per
+// chunk).
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+namespace {
+
+constexpr uint32_t kPastRange = 0x7FFFFFF0u;
+constexpr int kGdnC = 64;    // tokens per chunk
+constexpr int kTrS = 20;     // row stride (floats) of the per-wave transpose scratch
+
+__device__ __forceinline__ int gdn_xcd_remap(int bid, int total) {
+  if (total % 8) return bid;
+  return (bid % 8) * (total / 8) + bid / 8;
+}
+
+// hi/lo bf16 split of eight fp32 values (slots 0..3 from a, 4..7 from b).
+__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, u32x4& hi, u32x4& lo) {
+  uint32_t h[4], l[4];
+  split_bf16(a[0], a[1], h[0], l[0]);
+  split_bf16(a[2], a[3], h[1], l[1]);
+  split_bf16(b[0], b[1], h[2], l[2]);
+  split_bf16(b[2], b[3], h[3], l[3]);
+  hi = make_u32x4(h);
+  lo = make_u32x4(l);
+}
+
+template <int K, int V, int NW, bool VBF16>
+__global__ __launch_bounds__(64 * NW) void gdn_fwd_h_kernel(
+    const uint16_t* __restrict__ kin, const uint16_t* __restrict__ win,
+    const uint16_t* __restrict__ uin, const float* __restrict__ g,
+    const float* __restrict__ h0, float* __restrict__ hout, void* __restrict__ vnew,
+    float* __restrict__ fin, int L, int H) {
+  constexpr int C = kGdnC;
+  constexpr int BV = 16 * NW;
+  constexpr int NTHR = 64 * NW;
+  constexpr int NKB = K / 16;                  // state row blocks per wave
+  constexpr int NKK = K / 32;                  // 32-wide k-steps over K
+  constexpr int WS = K + 8;                    // w tile row stride (bf16)
+  constexpr int KSt = K + 16;                  // k tile row stride (bf16)
+  constexpr int US = BV + 16;                  // u tile row stride (bf16)
+  constexpr int TRR = K > C ? K : C;           // transpose scratch rows
+  constexpr int kWUnits = C * K / 8;           // 16-byte units of a w (or k) tile
+  constexpr int WU = (kWUnits + NTHR - 1) / NTHR;
+  constexpr int kUUnits = C * BV / 8;
+  constexpr int UU = (kUUnits + NTHR - 1) / NTHR;
+  __shared__ __attribute__((aligned(16))) uint16_t ws_[2][C * WS];
+  __shared__ __attribute__((aligned(16))) uint16_t ks_[2][C * KSt];
+  __shared__ __attribute__((aligned(16))) uint16_t us_[2][C * US];
+  __shared__ __attribute__((aligned(16))) float gs_[2][C];
+  __shared__ __attribute__((aligned(16))) float tr_[NW][TRR * kTrS];
+
+  const int nvt = V / BV;
+  const int logical = gdn_xcd_remap(blockIdx.x, gridDim.x);
+  const int vt = logical % nvt;
+  const int bh = logical / nvt;
+  const int b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int v0 = vt * BV + 16 * wave;          // this wave's first state column
+  const int nt = (L + C - 1) / C;
+
+  // Per-sequence buffer descriptors: reads past the last token return zero.
+  const uint32_t krow = (uint32_t)(H * K), urow = (uint32_t)(H * V);
+  const rsrc_t kr = make_rsrc(kin + ((size_t)b * L * H + h) * K, ((uint32_t)(L - 1) * krow + K) * 2u);
+  const rsrc_t wr = make_rsrc(win + ((size_t)b * L * H + h) * K, ((uint32_t)(L - 1) * krow + K) * 2u);
+  const rsrc_t ur = make_rsrc(uin + ((size_t)b * L * H + h) * V, ((uint32_t)(L - 1) * urow + V) * 2u);
+  const rsrc_t gr = make_rsrc(g + (size_t)b * L * H + h, ((uint32_t)(L - 1) * H + 1) * 4u);
+  constexpr int VES = VBF16 ? 2 : 4;
+  const rsrc_t vr = make_rsrc((char*)vnew + ((size_t)b * L * H + h) * V * VES,
+                              ((uint32_t)(L - 1) * urow + V) * VES);
+
+  // State blocks: acc[kb][r] = h[16 kb + 4 lq + r][v0 + lr].
+  f32x4 acc[NKB];
+  const size_t sbase = (size_t)bh * K * V;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      acc[kb][r] = h0 ? h0[sbase + (size_t)(16 * kb + 4 * lq + r) * V + v0 + lr] : 0.0f;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // Staging units of this thread (idle units read past the range).
+  uint32_t woff[WU], uoff[UU];
+  int wlds[WU], klds[WU], ulds[UU];
+#pragma unroll
+  for (int i = 0; i < WU; ++i) {
+    const int u = tid + NTHR * i;
+    const int t = u / (K / 8), c8 = u % (K / 8);
+    woff[i] = u < kWUnits ? ((uint32_t)t * krow + 8 * c8) * 2u : kPastRange;
+    wlds[i] = t * WS + 8 * c8;
+    klds[i] = t * KSt + 8 * c8;
+  }
+#pragma unroll
+  for (int i = 0; i < UU; ++i) {
+    const int u = tid + NTHR * i;
+    const int t = u / (BV / 8), c8 = u % (BV / 8);
+    uoff[i] = u < kUUnits ? ((uint32_t)t * urow + vt * BV + 8 * c8) * 2u : kPastRange;
+    ulds[i] = t * US + 8 * c8;
+  }
+
+  struct Tile {
+    u32x4 w[WU], k[WU], u[UU];
+    float g;
+  };
+  auto issue = [&](int c, Tile& tl) {
+    const uint32_t t0 = (uint32_t)(c * C);
+#pragma unroll
+    for (int i = 0; i < WU; ++i) {
+      tl.w[i] = load_b128(wr, woff[i] + t0 * krow * 2u);
+      tl.k[i] = load_b128(kr, woff[i] + t0 * krow * 2u);
+    }
+#pragma unroll
+    for (int i = 0; i < UU; ++i) tl.u[i] = load_b128(ur, uoff[i] + t0 * urow * 2u);
+    const uint32_t tt = t0 + (uint32_t)tid;
+    tl.g = load_f32(gr, (tid < C && tt < (uint32_t)L) ? tt * (uint32_t)H * 4u : kPastRange);
+  };
+  auto commit = [&](int buf, const Tile& tl) {
+#pragma unroll
+    for (int i = 0; i < WU; ++i) {
+      if (tid + NTHR * i < kWUnits) {
+        *(u32x4*)(ws_[buf] + wlds[i]) = tl.w[i];
+        *(u32x4*)(ks_[buf] + klds[i]) = tl.k[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UU; ++i)
+      if (tid + NTHR * i < kUUnits) *(u32x4*)(us_[buf] + ulds[i]) = tl.u[i];
+    if (tid < C) gs_[buf][tid] = tl.g;
+  };
+
+  float* tr = tr_[wave];
+  // The wave's 16 state columns (all K rows) as 16-byte rows of 4 columns.
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tr[(16 * kb + 4 * lq + r) * kTrS + lr] = acc[kb][r];
+    }
+#pragma unroll
+    for (int i = 0; i < K / 16; ++i) {
+      const int row = 16 * i + (lane >> 2), cg = lane & 3;
+      *(f32x4*)(dst + (size_t)row * V + v0 + 4 * cg) = *(const f32x4*)(tr + row * kTrS + 4 * cg);
+    }
+  };
+
+  auto step = [&](int c, const Tile& next) {
+    const int buf = c & 1;
+    const uint16_t* wsb = ws_[buf];
+    const uint16_t* ksb = ks_[buf];
+    const uint16_t* usb = us_[buf];
+    const float* gsb = gs_[buf];
+    const int n = min(C, L - c * C);            // valid tokens of the chunk
+
+    // (1) the state at the chunk start
+    store_state(hout + ((size_t)bh * nt + c) * K * V);
+
+    // (2) v_new = u - w h, as -(w h - u); rows t = 16 tb + 4 lq + r, column v0 + lr
+    u32x4 hh[NKK], hl[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) split8(acc[2 * kk], acc[2 * kk + 1], hh[kk], hl[kk]);
+    f32x4 vn[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const u32x2 uu = lds_read_tr16(usb + (16 * tb + 4 * lq + (lr >> 2)) * US + 16 * wave +
+                                     4 * (lr & 3));
+      vn[tb] = -(f32x4){bf16_lo(uu[0]), bf16_hi(uu[0]), bf16_lo(uu[1]), bf16_hi(uu[1])};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const uint16_t* wp = wsb + (16 * tb + lr) * WS + 32 * kk + 4 * lq;
+        const u32x2 a0 = *(const u32x2*)wp;
+        const u32x2 a1 = *(const u32x2*)(wp + 16);
+        const u32x4 av = {a0[0], a0[1], a1[0], a1[1]};
+        vn[tb] = mfma_bf16(av, hh[kk], vn[tb]);
+        vn[tb] = mfma_bf16(av, hl[kk], vn[tb]);
+      }
+      vn[tb] = -vn[tb];
+    }
+
+    // (3) v_new out, 16-byte rows of 4 columns (tokens past the end fall
+    //     outside the buffer range and are dropped)
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tr[(16 * tb + 4 * lq + r) * kTrS + lr] = vn[tb][r];
+    }
+    const uint32_t t0 = (uint32_t)(c * C);
+#pragma unroll
+    for (int i = 0; i < C / 16; ++i) {
+      const int row = 16 * i + (lane >> 2), cg = lane & 3;
+      const f32x4 vv = *(const f32x4*)(tr + row * kTrS + 4 * cg);
+      const uint32_t off = ((t0 + row) * urow + v0 + 4 * cg) * VES;
+      if constexpr (VBF16) {
+        __builtin_amdgcn_raw_buffer_store_b64(
+            (u32x2){pack_bf16(vv[0], vv[1]), pack_bf16(vv[2], vv[3])}, vr, (int)off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, vv), vr, (int)off, 0,
+                                               0);
+      }
+    }
+
+    // (4) gate and (5) update: h = e^{g_last} h + k^T (e^{g_last - g} o v_new).
+    //     Tokens past the end have u = w = 0, so v_new = 0 there.
+    const float gl = gsb[n - 1];
+    const float decay = exp2_hw(gl * kLog2e);
+    u32x4 gh[2], glo[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      f32x4 e[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int tb = 2 * kk + s;
+        const f32x4 gv = *(const f32x4*)(gsb + 16 * tb + 4 * lq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[s][r] = vn[tb][r] * exp2_hw((gl - gv[r]) * kLog2e);
+      }
+      split8(e[0], e[1], gh[kk], glo[kk]);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      acc[kb] = decay * acc[kb];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint16_t* kp = ksb + (32 * kk + 4 * lq + (lr >> 2)) * KSt + 16 * kb + 4 * (lr & 3);
+        const u32x2 e0 = lds_read_tr16(kp);
+        const u32x2 e1 = lds_read_tr16(kp + 16 * KSt);
+        const u32x4 kv = {e0[0], e0[1], e1[0], e1[1]};
+        acc[kb] = mfma_bf16(kv, gh[kk], acc[kb]);
+        acc[kb] = mfma_bf16(kv, glo[kk], acc[kb]);
+      }
+    }
+    if (c + 1 < nt) commit(buf ^ 1, next);
+    __syncthreads();
+  };
+
+  // Two register tiles: one is staged while the other's loads are in flight.
+  Tile ga, gb;
+  issue(0, ga);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(1, gb);
+  __builtin_amdgcn_sched_barrier(0);
+  commit(0, ga);
+  __syncthreads();
+  for (int c0 = 0; c0 < nt; c0 += 2) {
+    step(c0, gb);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(c0 + 2, ga);
+    __builtin_amdgcn_sched_barrier(0);
+    if (c0 + 1 < nt) step(c0 + 1, ga);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(c0 + 3, gb);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (fin) store_state(fin + sbase);
+}
+
+template <int K, int V, int NW, bool VBF16>
+int launch_h(const void* k, const void* w, const void* u, const float* g, const float* h0,
+             float* hout, void* vnew, float* fin, const GdnShape& s, hipStream_t st) {
+  const unsigned blocks = (unsigned)(s.batch * s.nheads * (V / (16 * NW)));
+  hipLaunchKernelGGL((gdn_fwd_h_kernel<K, V, NW, VBF16>), dim3(blocks), dim3(64 * NW), 0, st,
+                     (const uint16_t*)k, (const uint16_t*)w, (const uint16_t*)u, g, h0, hout,
+                     vnew, fin, (int)s.seqlen, (int)s.nheads);
+  return (int)hipGetLastError();
+}
+
+template <int K, int V>
+int launch_h_kv(const void* k, const void* w, const void* u, const float* g, const float* h0,
+                float* hout, void* vnew, float* fin, bool vbf16, const GdnShape& s,
+                hipStream_t st) {
+  // four waves (64 columns) per workgroup when that still gives a workgroup
+  // per CU, else two
+  const bool wide = V >= 64 && s.batch * s.nheads * (V / 64) >= 256;
+  if (wide)
+    return vbf16 ? launch_h<K, V, 4, true>(k, w, u, g, h0, hout, vnew, fin, s, st)
+                 : launch_h<K, V, 4, false>(k, w, u, g, h0, hout, vnew, fin, s, st);
+  return vbf16 ? launch_h<K, V, 2, true>(k, w, u, g, h0, hout, vnew, fin, s, st)
+               : launch_h<K, V, 2, false>(k, w, u, g, h0, hout, vnew, fin, s, st);
+}
+
+}  // namespace
+
+int launch_gdn_fwd_h(const void* k, const void* w, const void* u, const float* g,
+                     const float* h0, float* hout, void* vnew, float* fin, bool vbf16,
+                     const GdnShape& s, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (s.dk == 64)
+    return s.dv == 64 ? launch_h_kv<64, 64>(k, w, u, g, h0, hout, vnew, fin, vbf16, s, st)
+                      : launch_h_kv<64, 128>(k, w, u, g, h0, hout, vnew, fin, vbf16, s, st);
+  return s.dv == 64 ? launch_h_kv<128, 64>(k, w, u, g, h0, hout, vnew, fin, vbf16, s, st)
+                    : launch_h_kv<128, 128>(k, w, u, g, h0, hout, vnew, fin, vbf16, s, st);
+}
+
+}  // namespace ssd

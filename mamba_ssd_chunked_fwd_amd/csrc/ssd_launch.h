@@ -30,6 +30,17 @@ int launch_decode_step(const void* x, const float* dt, const float* A, const voi
                        const void* C, const float* D, float* state, void* y, bool bf16_in,
                        bool bf16_out, const Shape& s, void* stream);
 
+// Gated DeltaNet shapes: q, k, w [b, L, H, K]; u, v_new, o [b, L, H, V];
+// chunks of 64 tokens.
+struct GdnShape {
+  int64_t batch, seqlen, nheads, dk, dv;
+  int64_t nchunks() const { return (seqlen + 63) / 64; }
+};
+
+int launch_gdn_fwd_h(const void* k, const void* w, const void* u, const float* g,
+                     const float* h0, float* hout, void* vnew, float* fin, bool vbf16,
+                     const GdnShape& s, void* stream);
+
 int launch_causal_conv1d(const void* x, const float* weight, const float* bias, void* out,
                          int64_t batch, int64_t dim, int64_t seqlen, int width, bool bf16_in,
                          bool bf16_out, void* stream);

@@ -167,6 +167,75 @@ def make_conv_inputs(c: ConvWorkload, seed: int = 0) -> Dict[str, np.ndarray]:
     return {"x": x, "weight": weight, "bias": bias if c.bias else None}
 
 
+@dataclasses.dataclass(frozen=True)
+class GdnWorkload:
+    """Shape of a Gated DeltaNet layer's chunked forward: q, k, w
+    [batch, seqlen, nheads, dk]; u [batch, seqlen, nheads, dv]; chunks of 64."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    dk: int
+    dv: int
+    dtype: str = "bf16"
+    init_std: Optional[float] = None
+    chunk_size: int = 64
+
+    @property
+    def nchunks(self) -> int:
+        return -(-self.seqlen // self.chunk_size)
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+
+GDN_WORKLOADS: Dict[str, GdnWorkload] = {
+    # A 16-head GDN layer with 128-wide keys and values, 8 x 2048 tokens.
+    "gdn_layer_bf16": GdnWorkload("gdn_layer_bf16", 8, 2048, 16, 128, 128),
+}
+
+
+def make_gdn_inputs(c: GdnWorkload, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Draw the chunked Gated DeltaNet inputs.
+
+    Draw order: q, k, k2, v, beta, a, h0.  q ~ N(0, 1); k and k2 are N(0, 1)
+    rows scaled to unit L2 norm; beta ~ U(0.1, 0.9); the per-token log-gates
+    a ~ U(-0.5, -0.01).  The kernels take the WY-transformed keys and values
+    as inputs, so w and u are drawn with the same shapes and scale: w_t =
+    beta_t k2_t (a unit row independent of k_t) and u_t = beta_t v_t.  g, the
+    gate input, is the chunk-local running sum of a (float64, then float32),
+    the form the chunked kernels read.  q, k, w, u are rounded to bf16 for
+    bf16 workloads.  h0 ~ N(0, init_std) or None.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    b, L, H, K, V, C = c.batch, c.seqlen, c.nheads, c.dk, c.dv, c.chunk_size
+    q = rng.standard_normal((b, L, H, K), dtype=np.float32)
+    k = rng.standard_normal((b, L, H, K), dtype=np.float32)
+    k2 = rng.standard_normal((b, L, H, K), dtype=np.float32)
+    v = rng.standard_normal((b, L, H, V), dtype=np.float32)
+    beta = rng.uniform(0.1, 0.9, size=(b, L, H)).astype(np.float32)
+    a = rng.uniform(-0.5, -0.01, size=(b, L, H))
+    h0 = None
+    if c.init_std is not None:
+        h0 = (rng.standard_normal((b, H, K, V), dtype=np.float32)
+              * np.float32(c.init_std))
+    k = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    k2 = k2 / np.linalg.norm(k2, axis=-1, keepdims=True)
+    w = beta[..., None] * k2
+    u = beta[..., None] * v
+    g = np.empty((b, L, H), np.float64)
+    for t0 in range(0, L, C):
+        g[:, t0:t0 + C] = np.cumsum(a[:, t0:t0 + C], axis=1)
+    g = g.astype(np.float32)
+    if c.dtype == "bf16":
+        q, k, w, u = (round_to_bf16(x) for x in (q, k, w, u))
+    elif c.dtype != "fp32":
+        raise ValueError(f"unknown dtype {c.dtype!r}")
+    f = lambda x: np.ascontiguousarray(x, dtype=np.float32)
+    return {"q": f(q), "k": f(k), "w": f(w), "u": f(u), "g": f(g), "h0": h0}
+
+
 def small_variant(w: Workload, **kw) -> Workload:
     """A reduced copy of ``w`` (same dtype and distributions)."""
     return w.with_(name=w.name + "_small", **kw)

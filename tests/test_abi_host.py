@@ -40,7 +40,7 @@ def test_every_declared_function_is_exported():
     assert set(names) == {"ssd_status_string", "ssd_forward_workspace_bytes",
                           "ssd_chunk_cumsum", "ssd_fwd_pass_state",
                           "ssd_compute_out", "ssd_forward", "ssd_decode_step",
-                          "ssd_causal_conv1d"}
+                          "ssd_causal_conv1d", "ssd_gdn_chunk_fwd_h"}
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
