@@ -214,6 +214,25 @@ ssd_status ssd_gdn_chunk_fwd_h(const void *k, const void *w, const void *u,
                                void *stream);
 
 /*
+ * The output [P3, chunk_fwd_o]: for every (b, chunk c, h) and token t of the
+ * chunk,
+ *   o[t] = scale * ( exp(g[t]) q[t] h[b,h,c]
+ *                    + sum_{j in chunk, j <= t} (q[t] . k[j]) exp(g[t] - g[j]) v_new[j] )
+ * (scale = 1 is the gallery's formula).  Entries with j > t are replaced by
+ * zero after their exponent is formed (a select, never a multiply by a 0/1
+ * mask).
+ *   q, k [b, L, H, K] in_dtype    v_new [b, L, H, V] v_dtype (from chunk_fwd_h)
+ *   h [b, H, nt, K, V] fp32 (from chunk_fwd_h)    g [b, L, H] fp32
+ *   o [b, L, H, V] o_dtype (written)
+ * Supported: in_dtype and v_dtype bf16; o_dtype fp32 or bf16.
+ */
+ssd_status ssd_gdn_chunk_fwd_o(const void *q, const void *k, const void *v_new,
+                               const float *h, const float *g, void *o,
+                               float scale, int in_dtype, int v_dtype,
+                               int o_dtype, const ssd_gdn_dims *dims,
+                               void *stream);
+
+/*
  * The causal depthwise conv1d of the Mamba block, upstream of the SSD [P3,
  * the causal_conv1d entries]: each channel row is filtered on its own over
  * the current and the width-1 previous tokens, with zeros before the first

@@ -7,7 +7,7 @@ the current HIP stream.  PyTorch supplies device memory and streams.
 
 Entry points (same names as the C ABI):
   ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_compute_out, ssd_forward,
-  ssd_decode_step, ssd_causal_conv1d, ssd_gdn_chunk_fwd_h
+  ssd_decode_step, ssd_causal_conv1d, ssd_gdn_chunk_fwd_h, ssd_gdn_chunk_fwd_o
 and the allocating convenience wrapper ``forward``.
 
 Importing fails loudly (ImportError) when libssd.so has not been built:
@@ -80,6 +80,8 @@ def _load() -> ctypes.CDLL:
     gdims = ctypes.POINTER(GdnDims)
     lib.ssd_gdn_chunk_fwd_h.argtypes = [vp] * 8 + [i, i, gdims, vp]
     lib.ssd_gdn_chunk_fwd_h.restype = i
+    lib.ssd_gdn_chunk_fwd_o.argtypes = [vp] * 6 + [ctypes.c_float, i, i, i, gdims, vp]
+    lib.ssd_gdn_chunk_fwd_o.restype = i
     lib.ssd_causal_conv1d.argtypes = [vp] * 4 + [i64] * 4 + [i, i, vp]
     lib.ssd_causal_conv1d.restype = i
     return lib
@@ -325,6 +327,33 @@ def ssd_gdn_chunk_fwd_h(k: torch.Tensor, w: torch.Tensor, u: torch.Tensor,
         _ptr(k), _ptr(w), _ptr(u), _ptr(g), _ptr(h0), _ptr(h), _ptr(v_new),
         _ptr(final_state), _dtype_code(k.dtype), _dtype_code(v_new.dtype),
         ctypes.byref(d), _stream(dev)), "ssd_gdn_chunk_fwd_h")
+
+
+def ssd_gdn_chunk_fwd_o(q: torch.Tensor, k: torch.Tensor, v_new: torch.Tensor,
+                        h: torch.Tensor, g: torch.Tensor, o: torch.Tensor,
+                        scale: float = 1.0, chunk_size: int = 64) -> None:
+    """Gated DeltaNet output: q, k [b, L, H, K] bf16; v_new [b, L, H, V] bf16;
+    h [b, H, nt, K, V] fp32; g [b, L, H] fp32; writes o [b, L, H, V]
+    (fp32 or bf16)."""
+    if q.dim() != 4 or v_new.dim() != 4:
+        raise ValueError("q must be [batch, seqlen, nheads, dk] and v_new "
+                         "[batch, seqlen, nheads, dv]")
+    b, L, H, K = q.shape
+    V = v_new.shape[3]
+    nt = -(-L // chunk_size)
+    dev = q.device
+    ins = (torch.float32, torch.bfloat16)
+    _check(q, "q", None, ins)
+    _check(k, "k", (b, L, H, K), (q.dtype,), dev)
+    _check(v_new, "v_new", (b, L, H, V), ins, dev)
+    _check(h, "h", (b, H, nt, K, V), (torch.float32,), dev)
+    _check(g, "g", (b, L, H), (torch.float32,), dev)
+    _check(o, "o", (b, L, H, V), ins, dev)
+    d = GdnDims(b, L, H, K, V, chunk_size)
+    _raise(_lib.ssd_gdn_chunk_fwd_o(
+        _ptr(q), _ptr(k), _ptr(v_new), _ptr(h), _ptr(g), _ptr(o),
+        ctypes.c_float(scale), _dtype_code(q.dtype), _dtype_code(v_new.dtype),
+        _dtype_code(o.dtype), ctypes.byref(d), _stream(dev)), "ssd_gdn_chunk_fwd_o")
 
 
 def ssd_causal_conv1d(x: torch.Tensor, weight: torch.Tensor,

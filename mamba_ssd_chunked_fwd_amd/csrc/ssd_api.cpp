@@ -210,6 +210,21 @@ ssd_status ssd_gdn_chunk_fwd_h(const void* k, const void* w, const void* u, cons
                                         v_dtype == SSD_BF16, s, stream));
 }
 
+ssd_status ssd_gdn_chunk_fwd_o(const void* q, const void* k, const void* v_new, const float* h,
+                               const float* g, void* o, float scale, int in_dtype, int v_dtype,
+                               int o_dtype, const ssd_gdn_dims* dims, void* stream) {
+  ssd::GdnShape s;
+  const ssd_status st = check_gdn_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype) || !ok_dtype(v_dtype) || !ok_dtype(o_dtype))
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v_new) || !ok_ptr(h) || !ok_ptr(g) || !ok_ptr(o))
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (in_dtype != SSD_BF16 || v_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+  return from_hip(
+      ssd::launch_gdn_fwd_o(q, k, v_new, h, g, o, scale, o_dtype == SSD_BF16, s, stream));
+}
+
 ssd_status ssd_causal_conv1d(const void* x, const float* weight, const float* bias, void* out,
                              int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
                              int x_dtype, int out_dtype, void* stream) {

@@ -308,7 +308,223 @@ int launch_h_kv(const void* k, const void* w, const void* u, const float* g, con
                : launch_h<K, V, 2, false>(k, w, u, g, h0, hout, vnew, fin, s, st);
 }
 
+// ------------------------------------------------------------ chunk_fwd_o
+// One workgroup per (b, chunk, head, 64-column block of V); wave w owns the
+// 16 tokens t of block w and computes o^T[v][t] for the block's columns, so
+// each lane's accumulators are four consecutive v of one token (16-byte
+// stores).  Per wave:
+//   (i)   D = k q^T over K for the key blocks j <= t (rows j, columns t); with
+//         the decay e^{g_t - g_j} and the causal select (j <= t, applied
+//         after the exponent is formed) it is A^T, and a lane holds exactly
+//         the four consecutive j of the k-slot map, so A^T (split hi + lo)
+//         is the B operand of the next product as it sits;
+//   (ii)  o^T = h^T q^T (the state from LDS as bf16 hi + lo, read with the
+//         transpose read), scaled per token by e^{g_t};
+//   (iii) o^T += v_new^T A^T (v_new from LDS with the transpose read).
+// q stays in registers (each wave reads only its own 16 rows); k, v_new
+// and the state are staged once per workgroup in LDS.  The LDS footprint
+// lets two workgroups share a CU, so one loads while the other computes.
+template <int K, int V, bool OBF16>
+__global__ __launch_bounds__(256) void gdn_fwd_o_kernel(
+    const uint16_t* __restrict__ qin, const uint16_t* __restrict__ kin,
+    const uint16_t* __restrict__ vnin, const float* __restrict__ hin,
+    const float* __restrict__ g, void* __restrict__ out, float scale, int L, int H, int nt) {
+  constexpr int C = kGdnC;
+  constexpr int VB = 64;                       // columns of V per workgroup
+  constexpr int NVB = VB / 16;
+  constexpr int NKK = K / 32;
+  constexpr int HS = VB + 16;                  // state tile row stride (bf16)
+  constexpr int KS = K + 8;                    // k tile row stride (bf16)
+  constexpr int VS = VB + 16;                  // v_new tile row stride (bf16)
+  constexpr int kHUnits = K * VB / 4;          // 16-byte fp32 units of the state tile
+  constexpr int HU = kHUnits / 256;
+  constexpr int kKUnits = C * K / 8;
+  constexpr int KU = kKUnits / 256;
+  constexpr int kVUnits = C * VB / 8;
+  constexpr int VU = kVUnits / 256;
+  static_assert(HU * 256 == kHUnits && KU * 256 == kKUnits && VU * 256 == kVUnits, "units");
+  __shared__ __attribute__((aligned(16))) uint16_t hhi[K * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t hlo[K * HS];
+  __shared__ __attribute__((aligned(16))) uint16_t ks[C * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[C * VS];
+  __shared__ __attribute__((aligned(16))) float gs[C];
+
+  constexpr int NVH = V / VB;
+  const int logical = gdn_xcd_remap(blockIdx.x, gridDim.x);
+  const int vh = logical % NVH;
+  const int item = logical / NVH;
+  const int h = item % H;
+  const int c = (item / H) % nt;
+  const int b = item / (H * nt);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const uint32_t t0 = (uint32_t)(c * C);
+
+  const uint32_t krow = (uint32_t)(H * K), vrow = (uint32_t)(H * V);
+  const rsrc_t qr = make_rsrc(qin + ((size_t)b * L * H + h) * K, ((uint32_t)(L - 1) * krow + K) * 2u);
+  const rsrc_t kr = make_rsrc(kin + ((size_t)b * L * H + h) * K, ((uint32_t)(L - 1) * krow + K) * 2u);
+  const rsrc_t vr = make_rsrc(vnin + ((size_t)b * L * H + h) * V, ((uint32_t)(L - 1) * vrow + V) * 2u);
+  const rsrc_t gr = make_rsrc(g + (size_t)b * L * H + h, ((uint32_t)(L - 1) * H + 1) * 4u);
+  const float* hsrc = hin + (((size_t)b * H + h) * nt + c) * K * V + vh * VB;
+
+  // All loads of the item first.
+  f32x4 hreg[HU];
+  u32x4 kreg[KU], vreg[VU];
+#pragma unroll
+  for (int i = 0; i < HU; ++i) {
+    const int u = tid + 256 * i, row = u / (VB / 4), c4 = u % (VB / 4);
+    hreg[i] = *(const f32x4*)(hsrc + (size_t)row * V + 4 * c4);
+  }
+#pragma unroll
+  for (int i = 0; i < KU; ++i) {
+    const int u = tid + 256 * i, t = u / (K / 8), c8 = u % (K / 8);
+    kreg[i] = load_b128(kr, ((t0 + t) * krow + 8 * c8) * 2u);
+  }
+#pragma unroll
+  for (int i = 0; i < VU; ++i) {
+    const int u = tid + 256 * i, t = u / (VB / 8), c8 = u % (VB / 8);
+    vreg[i] = load_b128(vr, ((t0 + t) * vrow + vh * VB + 8 * c8) * 2u);
+  }
+  const float gv = load_f32(gr, (tid < C && t0 + tid < (uint32_t)L) ? (t0 + tid) * (uint32_t)H * 4u
+                                                                    : kPastRange);
+  // q: this wave's 16 tokens, in the k-slot map (K = 32kk + 4lq + 0..3 and
+  // 32kk + 16 + 4lq + 0..3), straight into operand registers.
+  const uint32_t tq = t0 + 16 * wave + lr;
+  u32x4 qf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const u32x2 a = load_b64(qr, (tq * krow + 32 * kk + 4 * lq) * 2u);
+    const u32x2 bq = load_b64(qr, (tq * krow + 32 * kk + 16 + 4 * lq) * 2u);
+    qf[kk] = (u32x4){a[0], a[1], bq[0], bq[1]};
+  }
+
+  // Stage: the state split into bf16 hi + lo, k and v_new as loaded, g.
+#pragma unroll
+  for (int i = 0; i < HU; ++i) {
+    const int u = tid + 256 * i, row = u / (VB / 4), c4 = u % (VB / 4);
+    uint32_t hh0, hl0, hh1, hl1;
+    split_bf16(hreg[i][0], hreg[i][1], hh0, hl0);
+    split_bf16(hreg[i][2], hreg[i][3], hh1, hl1);
+    *(u32x2*)(hhi + row * HS + 4 * c4) = (u32x2){hh0, hh1};
+    *(u32x2*)(hlo + row * HS + 4 * c4) = (u32x2){hl0, hl1};
+  }
+#pragma unroll
+  for (int i = 0; i < KU; ++i) {
+    const int u = tid + 256 * i, t = u / (K / 8), c8 = u % (K / 8);
+    *(u32x4*)(ks + t * KS + 8 * c8) = kreg[i];
+  }
+#pragma unroll
+  for (int i = 0; i < VU; ++i) {
+    const int u = tid + 256 * i, t = u / (VB / 8), c8 = u % (VB / 8);
+    *(u32x4*)(vs + t * VS + 8 * c8) = vreg[i];
+  }
+  if (tid < C) gs[tid] = gv;
+  __syncthreads();
+
+  const int tl = 16 * wave + lr;               // this lane's token in the chunk
+  const float gt = gs[tl];
+
+  // (ii) inter term: o^T = h^T q^T, then e^{g_t} per token.
+  f32x4 oa[NVB];
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb) {
+    oa[vb] = (f32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int o0 = (32 * kk + 4 * lq + (lr >> 2)) * HS + 16 * vb + 4 * (lr & 3);
+      const u32x2 a0 = lds_read_tr16(hhi + o0), a1 = lds_read_tr16(hhi + o0 + 16 * HS);
+      const u32x2 c0 = lds_read_tr16(hlo + o0), c1 = lds_read_tr16(hlo + o0 + 16 * HS);
+      oa[vb] = mfma_bf16((u32x4){a0[0], a0[1], a1[0], a1[1]}, qf[kk], oa[vb]);
+      oa[vb] = mfma_bf16((u32x4){c0[0], c0[1], c1[0], c1[1]}, qf[kk], oa[vb]);
+    }
+    oa[vb] = exp2_hw(gt * kLog2e) * oa[vb];
+  }
+
+  // (i) A^T blocks for key blocks jb <= wave, then (iii) o^T += v_new^T A^T
+  // in pairs of key blocks (32 keys per matrix step).
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    if (2 * kp > wave) break;
+    f32x4 at[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int jb = 2 * kp + s2;
+      at[s2] = (f32x4){0, 0, 0, 0};
+      if (jb <= wave) {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const uint16_t* kp0 = ks + (16 * jb + lr) * KS + 32 * kk + 4 * lq;
+          const u32x2 a = *(const u32x2*)kp0;
+          const u32x2 bb = *(const u32x2*)(kp0 + 16);
+          at[s2] = mfma_bf16((u32x4){a[0], a[1], bb[0], bb[1]}, qf[kk], at[s2]);
+        }
+        const f32x4 gj = *(const f32x4*)(gs + 16 * jb + 4 * lq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jb + 4 * lq + r;
+          const float e = at[s2][r] * exp2_hw((gt - gj[r]) * kLog2e);
+          at[s2][r] = j <= tl ? e : 0.0f;
+        }
+      }
+    }
+    u32x4 bh, bl;
+    split8(at[0], at[1], bh, bl);
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      const int o0 = (32 * kp + 4 * lq + (lr >> 2)) * VS + 16 * vb + 4 * (lr & 3);
+      const u32x2 e0 = lds_read_tr16(vs + o0), e1 = lds_read_tr16(vs + o0 + 16 * VS);
+      const u32x4 av = {e0[0], e0[1], e1[0], e1[1]};
+      oa[vb] = mfma_bf16(av, bh, oa[vb]);
+      oa[vb] = mfma_bf16(av, bl, oa[vb]);
+    }
+  }
+
+  // o[t][v .. v+3] for v = 64 vh + 16 vb + 4 lq; tokens past the end are
+  // outside the buffer range and dropped.
+  constexpr int OES = OBF16 ? 2 : 4;
+  const rsrc_t orr = make_rsrc((char*)out + ((size_t)b * L * H + h) * V * OES,
+                               ((uint32_t)(L - 1) * vrow + V) * OES);
+#pragma unroll
+  for (int vb = 0; vb < NVB; ++vb) {
+    const f32x4 ov = scale * oa[vb];
+    const uint32_t off = (tq * vrow + vh * VB + 16 * vb + 4 * lq) * OES;
+    if constexpr (OBF16) {
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2){pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])},
+                                            orr, (int)off, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), orr, (int)off, 0, 0);
+    }
+  }
+}
+
+template <int K, int V>
+int launch_o_kv(const void* q, const void* k, const void* vnew, const float* h, const float* g,
+                void* o, float scale, bool obf16, const GdnShape& s, hipStream_t st) {
+  const int nt = (int)s.nchunks();
+  const unsigned blocks = (unsigned)(s.batch * nt * s.nheads * (V / 64));
+  if (obf16)
+    hipLaunchKernelGGL((gdn_fwd_o_kernel<K, V, true>), dim3(blocks), dim3(256), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vnew, h, g, o,
+                       scale, (int)s.seqlen, (int)s.nheads, nt);
+  else
+    hipLaunchKernelGGL((gdn_fwd_o_kernel<K, V, false>), dim3(blocks), dim3(256), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vnew, h, g, o,
+                       scale, (int)s.seqlen, (int)s.nheads, nt);
+  return (int)hipGetLastError();
+}
+
 }  // namespace
+
+int launch_gdn_fwd_o(const void* q, const void* k, const void* vnew, const float* h,
+                     const float* g, void* o, float scale, bool obf16, const GdnShape& s,
+                     void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (s.dk == 64)
+    return s.dv == 64 ? launch_o_kv<64, 64>(q, k, vnew, h, g, o, scale, obf16, s, st)
+                      : launch_o_kv<64, 128>(q, k, vnew, h, g, o, scale, obf16, s, st);
+  return s.dv == 64 ? launch_o_kv<128, 64>(q, k, vnew, h, g, o, scale, obf16, s, st)
+                    : launch_o_kv<128, 128>(q, k, vnew, h, g, o, scale, obf16, s, st);
+}
 
 int launch_gdn_fwd_h(const void* k, const void* w, const void* u, const float* g,
                      const float* h0, float* hout, void* vnew, float* fin, bool vbf16,

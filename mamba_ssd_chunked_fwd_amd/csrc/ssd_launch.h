@@ -41,6 +41,10 @@ int launch_gdn_fwd_h(const void* k, const void* w, const void* u, const float* g
                      const float* h0, float* hout, void* vnew, float* fin, bool vbf16,
                      const GdnShape& s, void* stream);
 
+int launch_gdn_fwd_o(const void* q, const void* k, const void* vnew, const float* h,
+                     const float* g, void* o, float scale, bool obf16, const GdnShape& s,
+                     void* stream);
+
 int launch_causal_conv1d(const void* x, const float* weight, const float* bias, void* out,
                          int64_t batch, int64_t dim, int64_t seqlen, int width, bool bf16_in,
                          bool bf16_out, void* stream);

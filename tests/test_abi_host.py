@@ -40,7 +40,8 @@ def test_every_declared_function_is_exported():
     assert set(names) == {"ssd_status_string", "ssd_forward_workspace_bytes",
                           "ssd_chunk_cumsum", "ssd_fwd_pass_state",
                           "ssd_compute_out", "ssd_forward", "ssd_decode_step",
-                          "ssd_causal_conv1d", "ssd_gdn_chunk_fwd_h"}
+                          "ssd_causal_conv1d", "ssd_gdn_chunk_fwd_h",
+                          "ssd_gdn_chunk_fwd_o"}
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -148,6 +149,45 @@ def test_causal_conv1d_validates():
     assert call(W=5) == UNS
     assert call(L=1 << 29) == UNS
     assert call(b=1 << 30, d=1 << 12, L=1 << 12) == UNS
+
+
+def test_gdn_entry_points_validate():
+    GD = ssd.GdnDims
+
+    def gd(**kw):
+        base = dict(batch=2, seqlen=256, nheads=4, dk=128, dv=128, chunk_size=64)
+        base.update(kw)
+        return GD(**base)
+
+    def fh(d, **o):
+        return lib.ssd_gdn_chunk_fwd_h(
+            o.get("k", FAKE), o.get("w", FAKE), o.get("u", FAKE), o.get("g", FAKE),
+            o.get("h0", None), o.get("h", FAKE), o.get("vn", FAKE), o.get("fin", None),
+            o.get("ind", ssd.SSD_BF16), o.get("vd", ssd.SSD_BF16),
+            ctypes.byref(d) if d is not None else None, None)
+
+    def fo(d, **o):
+        return lib.ssd_gdn_chunk_fwd_o(
+            o.get("q", FAKE), o.get("k", FAKE), o.get("vn", FAKE), o.get("h", FAKE),
+            o.get("g", FAKE), o.get("o", FAKE), ctypes.c_float(1.0),
+            o.get("ind", ssd.SSD_BF16), o.get("vd", ssd.SSD_BF16), o.get("od", ssd.SSD_F32),
+            ctypes.byref(d) if d is not None else None, None)
+
+    d = gd()
+    assert fh(None) == INV and fo(None) == INV
+    for name in ("k", "w", "u", "g", "h", "vn"):
+        assert fh(d, **{name: None}) == INV, name
+        assert fh(d, **{name: MISALIGNED}) == INV, name
+    assert fh(d, h0=MISALIGNED) == INV and fh(d, fin=MISALIGNED) == INV
+    for name in ("q", "k", "vn", "h", "g", "o"):
+        assert fo(d, **{name: None}) == INV, name
+    assert fh(d, ind=7) == INV and fo(d, od=7) == INV
+    assert fh(d, ind=ssd.SSD_F32) == UNS          # fp32 inputs are not built
+    assert fo(d, vd=ssd.SSD_F32) == UNS           # fp32 v_new is not read
+    assert fh(gd(dk=96)) == UNS and fo(gd(dv=32)) == UNS
+    assert fh(gd(chunk_size=128)) == UNS
+    assert fh(gd(seqlen=0)) == INV and fo(gd(nheads=0)) == INV
+    assert fh(gd(seqlen=1 << 20, nheads=1024)) == UNS
 
 
 def test_stage_entry_points_validate():
