@@ -18,7 +18,10 @@ finds its operands in the 256 MB last-level cache from the previous step.
 
 Prints ONE JSON line: tokens/s (whole job), the roofline of the dominant
 kernel from algorithmic bytes and its event-measured duration, and the fp64
-CPU oracle timed on this host as a reported baseline.
+CPU oracle timed on this host as a reported baseline.  Side fields (not part
+of the step): the streaming decode step at the workload's batch and heads,
+the causal conv1d that feeds the layer's SSD, and the Gated DeltaNet
+chunk_fwd_h / chunk_fwd_o kernels on their own layer shape.
 """
 from __future__ import annotations
 
@@ -109,6 +112,61 @@ def cpu_baseline(w, inp):
                        f"runs of {', '.join('%.2f' % t for t in times)} s")}
 
 
+def gdn_bench(ssd, c, make, dev, stream, nrep):
+    """Event-timed chunk_fwd_h and chunk_fwd_o over two rotating input sets
+    (each larger than the 256 MB last-level cache)."""
+    import torch
+    inp = make(c, seed=3)
+    b, L, H, K, V, nt = c.batch, c.seqlen, c.nheads, c.dk, c.dv, c.nchunks
+    bf = torch.bfloat16
+
+    def one_set():
+        s = {k: torch.from_numpy(inp[k]).to(dev, bf) for k in ("q", "k", "w", "u")}
+        s["g"] = torch.from_numpy(inp["g"]).to(dev)
+        s["h"] = torch.empty(b, H, nt, K, V, device=dev)
+        s["vn"] = torch.empty(b, L, H, V, device=dev, dtype=bf)
+        s["fin"] = torch.empty(b, H, K, V, device=dev)
+        s["o"] = torch.empty(b, L, H, V, device=dev, dtype=bf)
+        return s
+    sets = [one_set() for _ in range(2)]
+
+    def fh(s):
+        ssd.ssd_gdn_chunk_fwd_h(s["k"], s["w"], s["u"], s["g"], None, s["h"], s["vn"], s["fin"])
+
+    def fo(s):
+        ssd.ssd_gdn_chunk_fwd_o(s["q"], s["k"], s["vn"], s["h"], s["g"], s["o"], 1.0)
+    for i in range(4):
+        fh(sets[i % 2])
+        fo(sets[i % 2])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nrep)]
+    torch.cuda.synchronize()
+    for i in range(nrep):
+        ev[i][0].record(stream)
+        fh(sets[i % 2])
+        ev[i][1].record(stream)
+        fo(sets[i % 2])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    h_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+    o_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in ev)
+    e = 2
+    h_bytes = (2 * e * b * L * H * K + e * b * L * H * V + 4 * b * L * H + 4 * b * H * nt * K * V
+               + e * b * L * H * V + 4 * b * H * K * V)
+    o_bytes = (2 * e * b * L * H * K + e * b * L * H * V + 4 * b * H * nt * K * V + 4 * b * L * H
+               + e * b * L * H * V)
+
+    def line(ms, by):
+        gbs = by / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 5), "alg_bytes": by, "GB_per_s": round(gbs, 1),
+                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del sets
+    return {"workload": {"name": c.name, "batch": b, "seqlen": L, "nheads": H, "dk": K,
+                         "dv": V, "chunk_size": c.chunk_size, "dtype": c.dtype},
+            "chunk_fwd_h": line(h_ms, h_bytes), "chunk_fwd_o": line(o_ms, o_bytes),
+            "tokens_per_s": round(b * L / ((h_ms + o_ms) * 1e-3), 1),
+            "note": "w, u synthetic (the WY transform is not on this path); bf16 v_new and o"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +175,8 @@ def main() -> int:
     ap.add_argument("--workload", default="small_bf16")
     ap.add_argument("--y-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true",
+                    help="skip the Gated DeltaNet kernels' timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter scale)")
     args = ap.parse_args()
@@ -130,8 +190,8 @@ def main() -> int:
     import torch
 
     import mamba_ssd_chunked_fwd_amd as ssd
-    from ssd_workloads import (WORKLOADS, conv_workload_for, make_conv_inputs,
-                               make_inputs)
+    from ssd_workloads import (GDN_WORKLOADS, WORKLOADS, conv_workload_for,
+                               make_conv_inputs, make_gdn_inputs, make_inputs)
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -267,6 +327,11 @@ def main() -> int:
     conv_bytes = cset_bytes + 4 * cw.dim * (cw.width + 1)
     del conv_sets
 
+    # ---- Gated DeltaNet chunked forward (chunk_fwd_h then chunk_fwd_o) on
+    #      its own layer shape, v_new and o in bf16
+    gdn = gdn_bench(ssd, GDN_WORKLOADS["gdn_layer_bf16"], make_gdn_inputs, dev, stream,
+                    max(20, args.steps // 2)) if not args.no_gdn else None
+
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -327,6 +392,7 @@ def main() -> int:
                           "GB_per_s": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
                           "hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "note": "the conv over the layer's x, B, C channels; not part of the step"},
+        "gated_deltanet": gdn,
         "effective_TFLOP_per_s": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
     }
