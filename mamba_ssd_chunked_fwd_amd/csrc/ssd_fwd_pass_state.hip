@@ -57,8 +57,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // ---------------------------------------------------------------- bf16 path
-// Workgroup tile: HB heads of one group x 16 state rows (p0..p0+15) x BN
-// state columns (n0..n0+BN-1); one wave per (head, NBW blocks of 16 columns).
+// Workgroup tile: HB heads of one group x 16 RS state rows (p0..) x BN state
+// columns (n0..n0+BN-1); one wave per (head, 16-row slice, NBW blocks of 16
+// columns).
 // The chunk is streamed in token tiles of TK = 128 tokens: a chunk of 256
 // spans two tiles, a tile holds two chunks of 64 (halving the sequential
 // steps, whose fixed cost dominates at small batch x heads).  Per tile, the
@@ -66,10 +67,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 // decay weight is folded into x instead:
 //   P^T[n][p] = sum_t B[t][n] (w_t x_t[p]),  w_t = dt_t 2^{g_last - g_t},
 // with w o x a computed fp32 value split into bf16 hi + lo (two MFMAs), so
-// the product keeps ~16 mantissa bits under fp32 accumulation.  Compared with
-// slicing only the state columns, a workgroup reads 16 columns of x per head
-// instead of all 64 and shares one B tile among its heads: about half the
-// bytes and a third of the load instructions per CU per chunk.
+// the product keeps ~16 mantissa bits under fp32 accumulation.  With 16-row
+// slices (RS = 1) a workgroup reads 16 columns of x per head and shares one
+// B tile among its heads, which keeps 256 equal tiles even at few (b, h)
+// pairs; with many pairs, whole heads (RS = 4, 128 columns) use every byte of
+// each x line they fetch.
 // Both operand tiles sit in LDS token-major ([t][n], [t][p]) and the matrix
 // operands are read with the LDS transpose read.  k-slot map of one 32-token
 // step kk for lane group lq: slots 0..3 <-> tokens 32kk + 4lq + 0..3, slots
@@ -81,14 +83,14 @@ struct BfTileStride {
   static constexpr int value = N == 16 ? 16 : N + 16;
 };
 
-template <int HB, int BN, int NBW>
+template <int HB, int RS, int BN, int NBW>
 struct BfTile {
-  static constexpr int WPH = BN / (16 * NBW);   // waves per head
-  static constexpr int NTHR = 64 * HB * WPH;
+  static constexpr int WPH = BN / (16 * NBW);   // waves per 16-row slice of a head
+  static constexpr int NTHR = 64 * HB * RS * WPH;
 };
 
-template <int T, int N, int HB, int BN, int NBW, int Q>
-__global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
+template <int T, int N, int HB, int RS, int BN, int NBW, int Q>
+__global__ __launch_bounds__(64 * HB * RS * (BN / (16 * NBW))) void state_pass_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt_t, const float* __restrict__ g,
     const float* __restrict__ init, float* __restrict__ states,
@@ -96,11 +98,11 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
   constexpr int TK = 128;                      // tokens per tile
   constexpr int R = T > TK ? T / TK : 1;       // tiles per chunk
   constexpr int CPT = T < TK ? TK / T : 1;     // chunks per tile
-  constexpr int WPH = BfTile<HB, BN, NBW>::WPH;
-  constexpr int NTHR = BfTile<HB, BN, NBW>::NTHR;
-  constexpr int XS = 16;                       // w o x row stride (bf16)
+  constexpr int WPH = BfTile<HB, RS, BN, NBW>::WPH;
+  constexpr int NTHR = BfTile<HB, RS, BN, NBW>::NTHR;
+  constexpr int XS = BfTileStride<16 * RS>::value;  // w o x row stride (bf16)
   constexpr int BS = BfTileStride<BN>::value;  // B row stride (bf16)
-  constexpr int kXUnits = HB * TK * 2;         // (head, token, 8 of the 16 p)
+  constexpr int kXUnits = HB * TK * 2 * RS;    // (head, token, 8 of the 16 RS p)
   constexpr int XU = (kXUnits + NTHR - 1) / NTHR;
   constexpr int kBUnits = TK * (BN / 8);       // (token, 8 n)
   constexpr int BU = (kBUnits + NTHR - 1) / NTHR;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t wls[2][HB * TK * XS];
 
   constexpr int NT = N / BN;
-  constexpr int NPS = kHeadDim / 16;           // 16-row slices of the state
+  constexpr int NPS = kHeadDim / (16 * RS);    // row tiles of the state
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int ntile = logical % NT;
   const int ps = (logical / NT) % NPS;
@@ -117,10 +119,11 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
   const int nhb = H / HB;
   const int b = hblk / nhb, h0 = (hblk % nhb) * HB;
   const int grp = h0 / (H / G);
-  const int n0 = ntile * BN, p0 = 16 * ps;
+  const int n0 = ntile * BN, p0 = 16 * RS * ps;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
-  const int hh = wave / WPH;                   // this wave's head in the block
+  const int hh = wave / (RS * WPH);            // this wave's head in the block
+  const int rs = (wave / WPH) % RS;            // its 16-row slice of the tile
   const int nb0 = (wave % WPH) * NBW;          // its first 16-column block
   const int h = h0 + hh;
   const int ntiles = R > 1 ? nc * R : (nc + CPT - 1) / CPT;
@@ -136,10 +139,11 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
   const rsrc_t gr = make_rsrc(g + grow, (uint32_t)(HB * L) * 4u);
   const rsrc_t dr = make_rsrc(dt_t + grow, (uint32_t)(HB * L) * 4u);
 
-  // State block of this wave: acc[j] holds S_h[p0 + lr][n0 + 16 (nb0 + j) + 4 lq + 0..3].
+  // State block of this wave: acc[j] holds
+  // S_h[p0 + 16 rs + lr][n0 + 16 (nb0 + j) + 4 lq + 0..3].
   f32x4 acc[NBW];
-  const size_t sbase = ((size_t)b * H + h) * kHeadDim * N + (size_t)(p0 + lr) * N + n0 +
-                       16 * nb0 + 4 * lq;
+  const size_t sbase = ((size_t)b * H + h) * kHeadDim * N + (size_t)(p0 + 16 * rs + lr) * N +
+                       n0 + 16 * nb0 + 4 * lq;
 #pragma unroll
   for (int j = 0; j < NBW; ++j)
     acc[j] = init ? *(const f32x4*)(init + sbase + 16 * j) : (f32x4){0, 0, 0, 0};
@@ -147,17 +151,17 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
   // the loop only ever concern tile loads.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // Staging units of this thread.  x unit u: head u / (2 TK), token
-  // (u / 2) % TK, columns p0 + 8 (u % 2) .. + 7.  B unit u: token u / (BN/8),
-  // columns n0 + 8 (u % (BN/8)) .. + 7.  Idle units read past the range, so
-  // every thread issues the same loads.
+  // Staging units of this thread.  x unit u: head u / (2 RS TK), token
+  // (u / (2 RS)) % TK, columns p0 + 8 (u % (2 RS)) .. + 7.  B unit u: token
+  // u / (BN/8), columns n0 + 8 (u % (BN/8)) .. + 7.  Idle units read past the
+  // range, so every thread issues the same loads.
   uint32_t xoff[XU], gtok[XU], ghead[XU], boff[BU];
   int xlds[XU], blds[BU];
 #pragma unroll
   for (int i = 0; i < XU; ++i) {
     const int u = tid + NTHR * i;
     const bool on = u < kXUnits;
-    const int uh = on ? u / (2 * TK) : 0, t = (u / 2) % TK, half = u % 2;
+    const int uh = on ? u / (2 * RS * TK) : 0, t = (u / (2 * RS)) % TK, half = u % (2 * RS);
     xoff[i] = on ? (((uint32_t)t * H + h0 + uh) * kHeadDim + p0 + 8 * half) * 2u : kPastRange;
     gtok[i] = on ? (uint32_t)t : (uint32_t)L;    // token within the tile (L: never valid)
     ghead[i] = (uint32_t)uh * L;
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
 
   // Transpose-read addresses of this lane (element offsets within a tile).
   const int rsel = 4 * lq + (lr >> 2), csel = 4 * (lr & 3);
-  const int wrd = (hh * TK + rsel) * XS + csel;
+  const int wrd = (hh * TK + rsel) * XS + 16 * rs + csel;
   const int brd = rsel * BS + 16 * nb0 + csel;
 
   f32x4 ph[NBW], pl[NBW];
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(64 * HB * (BN / (16 * NBW))) void state_pass_bf16(
       if (c < nc) {
         if (first) {
           float* dst = states + (((size_t)b * H + h) * nc + c) * kHeadDim * N +
-                       (size_t)(p0 + lr) * N + n0 + 16 * nb0 + 4 * lq;
+                       (size_t)(p0 + 16 * rs + lr) * N + n0 + 16 * nb0 + 4 * lq;
 #pragma unroll
           for (int j = 0; j < NBW; ++j) {
             *(f32x4*)(dst + 16 * j) = acc[j];
@@ -508,20 +512,31 @@ __global__ __launch_bounds__(256) void state_pass_f32(
 // with fewer bytes but more partial lines, and among those more heads per
 // tile (fewer x and B requests per state element) is faster.
 struct BfCfg {
-  int hb, bn, nbw;
+  int hb, rs, bn, nbw;
 };
-constexpr BfCfg kBfCfgs[] = {{5, 64, 2}, {4, 64, 2}, {3, 64, 1}, {2, 64, 1},
-                             {1, 64, 1}, {2, 32, 1}, {1, 32, 1}, {1, 16, 1}};
+// Workgroup tiles (heads, 16-row slices, columns, column blocks per wave).
+constexpr BfCfg kBfCfgs[] = {{4, 1, 64, 2}, {3, 1, 64, 1}, {2, 1, 64, 1}, {1, 1, 64, 1},
+                             {2, 1, 32, 1}, {1, 1, 32, 1}, {1, 1, 16, 1}, {1, 4, 128, 4}};
+constexpr int kWholeHeadCfg = 7;
 constexpr int kNumBfCfgs = sizeof(kBfCfgs) / sizeof(kBfCfgs[0]);
 
+int64_t bf_cfg_wgs(const BfCfg& c, const Shape& s) {
+  return s.batch * (s.nheads / c.hb) * (kHeadDim / (16 * c.rs)) * (s.dstate / c.bn);
+}
+
 int choose_bf_cfg(const Shape& s, int cus) {
+  // Whole-head tiles (64 rows x 128 columns) read each x line once per
+  // workgroup instead of once per 16-row slice; they win once there are
+  // enough (b, h) pairs to occupy most CUs (measured: 190 -> 163 us on the
+  // 2 x 8192-token, 80-head layer; slower with 96 or 32 pairs).
+  if (s.dstate == 128 && s.batch * s.nheads * 5 >= (int64_t)cus * 3) return kWholeHeadCfg;
   const int64_t hpg = s.nheads / s.ngroups;
   int most = -1;
   int64_t most_wgs = -1;
   for (int i = 0; i < kNumBfCfgs; ++i) {
     const BfCfg c = kBfCfgs[i];
-    if (hpg % c.hb != 0 || c.bn > s.dstate) continue;
-    const int64_t wgs = s.batch * (s.nheads / c.hb) * (kHeadDim / 16) * (s.dstate / c.bn);
+    if (c.rs != 1 || hpg % c.hb != 0 || c.bn > s.dstate) continue;
+    const int64_t wgs = bf_cfg_wgs(c, s);
     if (wgs >= cus) return i;
     if (wgs > most_wgs) {
       most = i;
@@ -544,23 +559,27 @@ int device_cus() {
   return cus;
 }
 
-template <int T, int N, int HB, int BN, int NBW>
+template <int T, int N, int HB, int RS, int BN, int NBW>
 int launch_bf(const uint16_t* x, const uint16_t* B, const float* dt_t, const float* g,
               const float* init, float* states, float* fin, const Shape& s,
               hipStream_t st) {
-  constexpr int NTHR = BfTile<HB, BN, NBW>::NTHR;
-  // tiles per group: two, unless one tile's registers are many (deeper
-  // groups measured no faster)
-  constexpr int CPT = T < 128 ? 128 / T : 1;
-  constexpr int XU = (HB * 128 * 2 + NTHR - 1) / NTHR;
-  constexpr int BU = (128 * (BN / 8) + NTHR - 1) / NTHR;
-  constexpr int Q = 7 * XU + 4 * BU + CPT <= 24 ? 2 : 1;
-  const unsigned blocks =
-      (unsigned)(s.batch * (s.nheads / HB) * (kHeadDim / 16) * (N / BN));
-  hipLaunchKernelGGL((state_pass_bf16<T, N, HB, BN, NBW, Q>), dim3(blocks), dim3(NTHR), 0,
-                     st, x, B, dt_t, g, init, states, fin, (int)s.seqlen, (int)s.nheads,
-                     (int)s.ngroups, (int)s.nchunks());
-  return (int)hipGetLastError();
+  if constexpr (BN > N) {
+    return (int)hipErrorInvalidValue;   // never chosen: the chooser checks BN <= N
+  } else {
+    constexpr int NTHR = BfTile<HB, RS, BN, NBW>::NTHR;
+    // tiles per group: two, unless one tile's registers are many (deeper
+    // groups measured no faster)
+    constexpr int CPT = T < 128 ? 128 / T : 1;
+    constexpr int XU = (HB * 128 * 2 * RS + NTHR - 1) / NTHR;
+    constexpr int BU = (128 * (BN / 8) + NTHR - 1) / NTHR;
+    constexpr int Q = 7 * XU + 4 * BU + CPT <= 24 ? 2 : 1;
+    const unsigned blocks =
+        (unsigned)(s.batch * (s.nheads / HB) * (kHeadDim / (16 * RS)) * (N / BN));
+    hipLaunchKernelGGL((state_pass_bf16<T, N, HB, RS, BN, NBW, Q>), dim3(blocks), dim3(NTHR),
+                       0, st, x, B, dt_t, g, init, states, fin, (int)s.seqlen, (int)s.nheads,
+                       (int)s.ngroups, (int)s.nchunks());
+    return (int)hipGetLastError();
+  }
 }
 
 template <int T, int N>
@@ -570,14 +589,15 @@ int launch_bf_n(const void* x, const void* B, const float* dt_t, const float* g,
   const uint16_t* xb = (const uint16_t*)x;
   const uint16_t* bb = (const uint16_t*)B;
   switch (choose_bf_cfg(s, device_cus())) {
-    case 0: return launch_bf<T, N, 5, 64, 2>(xb, bb, dt_t, g, init, states, fin, s, st);
-    case 1: return launch_bf<T, N, 4, 64, 2>(xb, bb, dt_t, g, init, states, fin, s, st);
-    case 2: return launch_bf<T, N, 3, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
-    case 3: return launch_bf<T, N, 2, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
-    case 4: return launch_bf<T, N, 1, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
-    case 5: return launch_bf<T, N, 2, 32, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
-    case 6: return launch_bf<T, N, 1, 32, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
-    default: return launch_bf<T, N, 1, 16, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 0: return launch_bf<T, N, 4, 1, 64, 2>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 1: return launch_bf<T, N, 3, 1, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 2: return launch_bf<T, N, 2, 1, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 3: return launch_bf<T, N, 1, 1, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 4: return launch_bf<T, N, 2, 1, 32, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case 5: return launch_bf<T, N, 1, 1, 32, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case kWholeHeadCfg:
+      return launch_bf<T, N, 1, 4, 128, 4>(xb, bb, dt_t, g, init, states, fin, s, st);
+    default: return launch_bf<T, N, 1, 1, 16, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
   }
 }
 

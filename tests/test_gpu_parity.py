@@ -41,7 +41,9 @@ SMALL = [
     _wl("bf16_T64_N64_grouped_init", "bf16", 2, 450, 6, 3, 64, 64, True),
     # shapes that select each bf16 state-pass tile (heads x columns per workgroup)
     _wl("bf16_T64_N128_3head_tiles", "bf16", 16, 130, 6, 1, 128, 64, True),
-    _wl("bf16_T128_N128_5head_tiles_grouped", "bf16", 16, 300, 10, 2, 128, 128, False),
+    _wl("bf16_T128_N128_whole_head_tiles_grouped", "bf16", 16, 300, 10, 2, 128, 128, False),
+    _wl("bf16_T64_N128_whole_head_tiles_ragged_init", "bf16", 2, 130, 80, 1, 128, 64, True),
+    _wl("bf16_T64_N128_4head_tiles_grouped", "bf16", 4, 100, 32, 4, 128, 64, True),
     _wl("bf16_T256_N128_2head_tiles_ragged", "bf16", 8, 300, 8, 1, 128, 256, True),
     _wl("bf16_T64_N128_4head_tiles", "bf16", 16, 100, 8, 1, 128, 64, False),
     _wl("bf16_T128_N128_1head_tiles_group_per_head", "bf16", 4, 150, 8, 8, 128, 128, True),
