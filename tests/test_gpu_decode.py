@@ -150,3 +150,28 @@ def test_decode_binding_rejects_bad_arguments(ssd):
         ssd.ssd_decode_step(xt, dtt, dev["A"], Bt[:, :, :96].contiguous(),
                             Ct[:, :, :96].contiguous(), dev["D"],
                             state[..., :96].contiguous(), y)
+
+
+def test_decode_step_replays_from_a_hip_graph(ssd):
+    """One decode step captured in a HIP graph and replayed several times
+    (with eager work and synchronisations in between) advances the state
+    exactly as the same number of eager steps does."""
+    w = _wl("bf16", 2, 1, 4, 2, 128)
+    dev = device_inputs(make_inputs(w, seed=46), "bf16")
+    xt, dtt, Bt, Ct = _token(dev, 0)
+    eager_state = dev["init_state"].clone()
+    graph_state = dev["init_state"].clone()
+    y_eager = torch.empty(2, 4, 64, device=DEV)
+    y_graph = torch.empty(2, 4, 64, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ssd.ssd_decode_step(xt, dtt, dev["A"], Bt, Ct, dev["D"], graph_state, y_graph)
+    torch.cuda.synchronize()
+    # capture only records: the state is still the initial one
+    assert torch.equal(graph_state, dev["init_state"])
+    for rep in range(4):
+        ssd.ssd_decode_step(xt, dtt, dev["A"], Bt, Ct, dev["D"], eager_state, y_eager)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(graph_state, eager_state), rep
+        assert torch.equal(y_graph, y_eager), rep
