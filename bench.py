@@ -8,9 +8,9 @@ synthetic input of the named workload (default: the small-model bf16 layer,
 batch 4 x 2048 tokens, 24 heads of 64, state 128, chunk 64).  The wall clock
 over K steps gives tokens/s.  A second timed loop calls the three stage entry
 points (ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_compute_out) -- exactly the
-kernels ssd_forward launches -- with HIP events between them on the launch
-stream, which gives each kernel's duration for the per-stage lines and the
-roofline.
+kernels ssd_forward launches -- each captured in a HIP graph and replayed
+between HIP events on the launch stream, which gives each kernel's mean
+duration for the per-stage lines and the roofline.
 
 Inputs are resident in HBM before timing.  Steps rotate over several
 independent input/output sets whose total footprint is >= 1 GiB, so no step
@@ -270,21 +270,28 @@ def main() -> int:
     for i in range(5):
         for _, f in stage_calls(sets[i % nsets]):
             f()
-    # One HIP event between consecutive launches.  (Back-to-back batches of
-    # one entry point were also tried: launches of the short kernels then
-    # outpace the host, which the mean would count.)
-    st_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
-             for _ in range(nst)]
-    torch.cuda.synchronize()
-    for i in range(nst):
-        ev = st_ev[i]
-        ev[0].record(stream)
-        for k, (_, f) in enumerate(stage_calls(sets[i % nsets])):
-            f()
-            ev[k + 1].record(stream)
-    torch.cuda.synchronize()
-    dur = {n: statistics.mean(e[k].elapsed_time(e[k + 1]) for e in st_ev)
-           for k, n in enumerate(stage_names)}
+    # Each entry point's nst launches (over the rotating sets, whose inputs
+    # the warm-up steps produced) are captured once in a HIP graph; the graph
+    # is replayed between two HIP events, so the mean launch duration holds
+    # neither host launch time nor an event between launches.  (Eager loops
+    # with one event per launch add about 3 us per launch; the short first
+    # stage is then host-bound.)
+    dur = {}
+    for k, n in enumerate(stage_names):
+        sg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sg):
+            for i in range(nst):
+                stage_calls(sets[i % nsets])[k][1]()
+        sg.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            sg.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dur[n] = e0.elapsed_time(e1) / (3 * nst)
+        del sg
 
     # ---- the streaming decode step at the same batch and heads: one token
     #      per sequence from the carried state (read and written in place)
