@@ -11,13 +11,15 @@
 //
 // MI355X design.  The step reads and writes the state once (8 P N bytes per
 // head) and touches little else, so it is HBM-bound; the kernel is a
-// coalesced stream over the state.  One workgroup (256 threads) per (b, h):
-// thread t owns the 16-byte state units t + 256 i (i = 0 .. P N / 1024 - 1),
-// so every load and store instruction covers 4 KB of contiguous state.  Unit
-// u sits in row p = u / (N/4), columns 4 (u % (N/4)) .. + 3; since 256 is a
-// multiple of N/4, a thread's columns are the same for every i, so its four
-// values of B and C are loaded once.  A row's N/4 units belong to N/4
-// consecutive lanes of one wave, so the row sum for y is a lane reduction.
+// coalesced stream over the state.  One workgroup (256 threads) per (b, h,
+// block of 64/RB state rows), RB = 1, 2 or 4 chosen so that small batches
+// still spread over all CUs (rows are independent: y_p reads row p only).
+// Thread t owns the 16-byte units t + 256 i of its row block, so every load
+// and store instruction covers 4 KB of contiguous state.  Unit u sits in row
+// p = u / (N/4), columns 4 (u % (N/4)) .. + 3; since 256 is a multiple of
+// N/4, a thread's columns are the same for every i, so its four values of B
+// and C are loaded once.  A row's N/4 units belong to N/4 consecutive lanes
+// of one wave, so the row sum for y is a lane reduction.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -44,7 +46,7 @@ struct DecIn<false> {
   static __device__ __forceinline__ float load1(const float* p) { return *p; }
 };
 
-template <int N, bool BF16, bool YBF16>
+template <int N, int RB, bool BF16, bool YBF16>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const void* __restrict__ xv, const float* __restrict__ dt, const float* __restrict__ A,
     const void* __restrict__ Bv, const void* __restrict__ Cv, const float* __restrict__ Dv,
@@ -52,16 +54,18 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   using In = DecIn<BF16>;
   using E = typename In::T;
   constexpr int UPR = N / 4;                 // 16-byte units per state row
-  constexpr int NU = kHeadDim * N / 4;       // units per head
+  constexpr int ROWS = kHeadDim / RB;        // state rows of this workgroup
+  constexpr int NU = ROWS * N / 4;           // units per workgroup
   constexpr int IT = NU / 256;               // units per thread
   static_assert(256 % UPR == 0 && NU % 256 == 0, "unit split");
-  __shared__ float xs[kHeadDim];
+  __shared__ float xs[ROWS];
 
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / RB, rb = blockIdx.x % RB;
   const int b = bh / H, h = bh % H, grp = h / (H / G);
   const int tid = threadIdx.x;
-  const E* x = (const E*)xv + (size_t)bh * kHeadDim;
-  if (tid < kHeadDim) xs[tid] = In::load1(x + tid);
+  const int p0 = rb * ROWS;
+  const E* x = (const E*)xv + (size_t)bh * kHeadDim + p0;
+  if (tid < ROWS) xs[tid] = In::load1(x + tid);
 
   const float d = dt[bh];
   const float decay = exp2_hw(A[h] * d * kLog2e);
@@ -70,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   const size_t bc = ((size_t)b * G + grp) * N + col;
   const f32x4 Bq = In::load4((const E*)Bv + bc) * d;
   const f32x4 Cq = In::load4((const E*)Cv + bc);
-  float* S = state + (size_t)bh * kHeadDim * N;
+  float* S = state + ((size_t)bh * kHeadDim + p0) * N;
   f32x4 s[IT];
 #pragma unroll
   for (int i = 0; i < IT; ++i) s[i] = *(const f32x4*)(S + 4 * (tid + 256 * i));
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int i = 0; i < IT; ++i) {
       const int p = (tid + 256 * i) / UPR;
       const float yv = part[i] + Dh * xs[p];
-      const size_t o = (size_t)bh * kHeadDim + p;
+      const size_t o = (size_t)bh * kHeadDim + p0 + p;
       if constexpr (YBF16) {
         ((uint16_t*)y)[o] = (uint16_t)(pack_bf16(yv, 0.0f) & 0xFFFFu);
       } else {
@@ -106,19 +110,31 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
   }
 }
 
+template <int N, int RB, bool BF16>
+int launch_rb(const void* x, const float* dt, const float* A, const void* B, const void* C,
+              const float* D, float* state, void* y, bool ybf16, const Shape& s,
+              hipStream_t st) {
+  const dim3 grid((unsigned)(s.batch * s.nheads * RB)), block(256);
+  const int H = (int)s.nheads, G = (int)s.ngroups;
+  if (ybf16)
+    hipLaunchKernelGGL((decode_step_kernel<N, RB, BF16, true>), grid, block, 0, st, x, dt, A, B,
+                       C, D, state, y, H, G);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<N, RB, BF16, false>), grid, block, 0, st, x, dt, A,
+                       B, C, D, state, y, H, G);
+  return (int)hipGetLastError();
+}
+
+// Row blocks per head: enough workgroups for two per CU where the state
+// allows (a workgroup keeps at least 256 units of 16 bytes).
 template <int N, bool BF16>
 int launch_y(const void* x, const float* dt, const float* A, const void* B, const void* C,
              const float* D, float* state, void* y, bool ybf16, const Shape& s,
              hipStream_t st) {
-  const dim3 grid((unsigned)(s.batch * s.nheads)), block(256);
-  const int H = (int)s.nheads, G = (int)s.ngroups;
-  if (ybf16)
-    hipLaunchKernelGGL((decode_step_kernel<N, BF16, true>), grid, block, 0, st, x, dt, A, B, C,
-                       D, state, y, H, G);
-  else
-    hipLaunchKernelGGL((decode_step_kernel<N, BF16, false>), grid, block, 0, st, x, dt, A, B,
-                       C, D, state, y, H, G);
-  return (int)hipGetLastError();
+  const int64_t pairs = s.batch * s.nheads;
+  if (pairs >= 512) return launch_rb<N, 1, BF16>(x, dt, A, B, C, D, state, y, ybf16, s, st);
+  if (pairs >= 256) return launch_rb<N, 2, BF16>(x, dt, A, B, C, D, state, y, ybf16, s, st);
+  return launch_rb<N, 4, BF16>(x, dt, A, B, C, D, state, y, ybf16, s, st);
 }
 
 }  // namespace

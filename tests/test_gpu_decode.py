@@ -47,6 +47,9 @@ CASES = [
     ("bf16", 2, 5, 6, 3, 64),
     ("fp32", 2, 5, 4, 1, 128),
     ("fp32", 4, 5, 6, 6, 64),
+    # enough (b, h) pairs for two and for one workgroup per head
+    ("bf16", 4, 2, 64, 2, 128),
+    ("fp32", 8, 2, 64, 4, 64),
 ]
 
 
