@@ -123,6 +123,34 @@ ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt_t,
                               const ssd_dims *dims, void *stream);
 
 /*
+ * Stage 2 in two levels [P1 "Step 1: Jump the State Across a Chunk with One
+ * Matmul"]: the jump S_{c+1} = 2^{g_last(c)} S_c + P_c, with P_c =
+ * X_c^T (w o B_c) the contribution of chunk c from a zero state, split into
+ * a fully parallel part and a short sequential one.  The two calls below,
+ * in this order, produce exactly what ssd_fwd_pass_state produces (same
+ * states and final_state); ssd_fwd_pass_state itself uses them where they
+ * are faster than its one-pass kernel.
+ *
+ * ssd_chunk_state: every P_c at once, written into the slot of the state it
+ * feeds: states[b,h,c+1] = P_c for c < nc-1, and final_state = P_{nc-1}
+ * (skipped when final_state is NULL).  states[b,h,0] is not touched.
+ *   x, B, dt_t, g, states, final_state as for ssd_fwd_pass_state.
+ *   Supported: in_dtype bf16 (fp32 returns SSD_ERR_UNSUPPORTED).
+ *
+ * ssd_state_passing: in place, element by element over the state:
+ *   states[b,h,0] = init (zeros if init_state is NULL);
+ *   states[b,h,c] = 2^{g_last(c-1)} states[b,h,c-1] + states[b,h,c], c >= 1;
+ *   final_state = 2^{g_last(nc-1)} states[b,h,nc-1] + final_state (if not NULL).
+ *   g [b, H, L] fp32 from ssd_chunk_cumsum; states, init, final fp32.
+ */
+ssd_status ssd_chunk_state(const void *x, const void *B, const float *dt_t,
+                           const float *g, float *states, float *final_state,
+                           int in_dtype, const ssd_dims *dims, void *stream);
+ssd_status ssd_state_passing(const float *g, const float *init_state,
+                             float *states, float *final_state,
+                             const ssd_dims *dims, void *stream);
+
+/*
  * Stage 3 [P1 "Kernel 3: compute_out, the Fused Output Kernel"; P1 "Step 2:
  * Compute a Chunk of Outputs from One State"]: for every (b, c, h), with S_c
  * = states[b,h,c], rows i and columns j tokens of chunk c:

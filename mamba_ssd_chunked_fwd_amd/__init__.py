@@ -6,7 +6,8 @@ tensor shapes/dtypes, builds the dims struct and passes device pointers and
 the current HIP stream.  PyTorch supplies device memory and streams.
 
 Entry points (same names as the C ABI):
-  ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_compute_out, ssd_forward,
+  ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_chunk_state, ssd_state_passing,
+  ssd_compute_out, ssd_forward,
   ssd_decode_step, ssd_causal_conv1d, ssd_gdn_chunk_fwd_h, ssd_gdn_chunk_fwd_o
 and the allocating convenience wrapper ``forward``.
 
@@ -70,6 +71,10 @@ def _load() -> ctypes.CDLL:
     lib.ssd_chunk_cumsum.restype = i
     lib.ssd_fwd_pass_state.argtypes = [vp] * 7 + [i, dims, vp]
     lib.ssd_fwd_pass_state.restype = i
+    lib.ssd_chunk_state.argtypes = [vp] * 6 + [i, dims, vp]
+    lib.ssd_chunk_state.restype = i
+    lib.ssd_state_passing.argtypes = [vp] * 4 + [dims, vp]
+    lib.ssd_state_passing.restype = i
     lib.ssd_compute_out.argtypes = [vp] * 8 + [i, i, dims, vp]
     lib.ssd_compute_out.restype = i
     lib.ssd_forward.argtypes = [vp] * 11 + [sz, i, i, dims, vp]
@@ -209,6 +214,50 @@ def ssd_fwd_pass_state(x: torch.Tensor, B: torch.Tensor, dt_t: torch.Tensor,
         _ptr(x), _ptr(B), _ptr(dt_t), _ptr(g), _ptr(init_state), _ptr(states),
         _ptr(final_state), _dtype_code(x.dtype), ctypes.byref(d),
         _stream(dev)), "ssd_fwd_pass_state")
+
+
+def ssd_chunk_state(x: torch.Tensor, B: torch.Tensor, dt_t: torch.Tensor,
+                    g: torch.Tensor, states: torch.Tensor,
+                    final_state: Optional[torch.Tensor], chunk_size: int) -> None:
+    """Every chunk's zero-state contribution P_c into states[:, :, c+1]
+    (P_{nc-1} into final_state); states[:, :, 0] is left as it is."""
+    d = make_dims(x, B, chunk_size)
+    dev = x.device
+    b, L, H, P, N, nc = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, nchunks(d)
+    f32 = (torch.float32,)
+    _check(x, "x", None, (torch.float32, torch.bfloat16))
+    _check(B, "B", None, (x.dtype,), dev)
+    _check(dt_t, "dt_t", (b, H, L), f32, dev)
+    _check(g, "g", (b, H, L), f32, dev)
+    _check(states, "states", (b, H, nc, P, N), f32, dev)
+    _check(final_state, "final_state", (b, H, P, N), f32, dev, optional=True)
+    _raise(_lib.ssd_chunk_state(
+        _ptr(x), _ptr(B), _ptr(dt_t), _ptr(g), _ptr(states), _ptr(final_state),
+        _dtype_code(x.dtype), ctypes.byref(d), _stream(dev)), "ssd_chunk_state")
+
+
+def ssd_state_passing(g: torch.Tensor, init_state: Optional[torch.Tensor],
+                      states: torch.Tensor, final_state: Optional[torch.Tensor],
+                      chunk_size: int) -> None:
+    """In place: the chunk contributions left by ssd_chunk_state become the
+    per-chunk starting states (and the final state)."""
+    if states.dim() != 5:
+        raise ValueError("states must be [batch, nheads, nchunks, headdim, dstate]")
+    b, H, nc, P, N = states.shape
+    L = g.shape[2] if g.dim() == 3 else -1
+    dev = states.device
+    f32 = (torch.float32,)
+    _check(g, "g", (b, H, L), f32, dev)
+    if -(-L // chunk_size) != nc:
+        raise ValueError(f"states has {nc} chunks; g's {L} tokens make "
+                         f"{-(-L // chunk_size)} chunks of {chunk_size}")
+    _check(states, "states", None, f32, dev)
+    _check(init_state, "init_state", (b, H, P, N), f32, dev, optional=True)
+    _check(final_state, "final_state", (b, H, P, N), f32, dev, optional=True)
+    d = SsdDims(b, L, H, P, N, 1, chunk_size)
+    _raise(_lib.ssd_state_passing(
+        _ptr(g), _ptr(init_state), _ptr(states), _ptr(final_state), ctypes.byref(d),
+        _stream(dev)), "ssd_state_passing")
 
 
 def ssd_compute_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

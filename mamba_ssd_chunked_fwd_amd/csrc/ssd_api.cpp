@@ -126,6 +126,30 @@ ssd_status ssd_fwd_pass_state(const void* x, const void* B, const float* dt_t,
                                              s, stream));
 }
 
+ssd_status ssd_chunk_state(const void* x, const void* B, const float* dt_t, const float* g,
+                           float* states, float* final_state, int in_dtype,
+                           const ssd_dims* dims, void* stream) {
+  ssd::Shape s;
+  const ssd_status st = check_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(dt_t) || !ok_ptr(g) || !ok_ptr(states) ||
+      !ok_opt(final_state))
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (in_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+  return from_hip(ssd::launch_chunk_state(x, B, dt_t, g, states, final_state, s, stream));
+}
+
+ssd_status ssd_state_passing(const float* g, const float* init_state, float* states,
+                             float* final_state, const ssd_dims* dims, void* stream) {
+  ssd::Shape s;
+  const ssd_status st = check_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_ptr(g) || !ok_opt(init_state) || !ok_ptr(states) || !ok_opt(final_state))
+    return SSD_ERR_INVALID_ARGUMENT;
+  return from_hip(ssd::launch_state_passing(g, init_state, states, final_state, s, stream));
+}
+
 ssd_status ssd_compute_out(const void* x, const void* B, const void* C,
                            const float* dt_t, const float* g,
                            const float* states, const float* D, void* y,

@@ -658,6 +658,22 @@ int launch_chunk(const void* x, const void* B, const float* dt_t, const float* g
   }
 }
 
+// The two-level form (chunk_state, then state_passing) moves about twice the
+// bytes of the one-pass kernel but has no chain per workgroup.  It wins
+// where the one-pass grid is long chains on few waves: measured on the
+// 65536-token, 32-head sequence (512 chunks, four waves per CU) it takes
+// 392 us against 492; with 32 chunks (small and large layers) it loses
+// (79 vs 53 us, 172 vs 160 us).
+bool use_two_level(const Shape& s, int cus) {
+  const int c = choose_bf_cfg(s, cus);
+  if (c < 0) return false;
+  const BfCfg k = kBfCfgs[c];
+  const int64_t chain_tiles = s.chunk > 128 ? s.nchunks() * (s.chunk / 128)
+                                            : (s.nchunks() * s.chunk + 127) / 128;
+  const int64_t waves = bf_cfg_wgs(k, s) * k.hb * k.rs * (k.bn / (16 * k.nbw));
+  return chain_tiles >= 128 && waves <= 8 * (int64_t)cus;
+}
+
 }  // namespace
 
 int launch_fwd_pass_state(const void* x, const void* B, const float* dt_t,
@@ -665,6 +681,11 @@ int launch_fwd_pass_state(const void* x, const void* B, const float* dt_t,
                           float* states, float* final_state, bool bf16_in,
                           const Shape& s, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (bf16_in && use_two_level(s, device_cus())) {
+    const int r = launch_chunk_state(x, B, dt_t, g, states, final_state, s, stream);
+    if (r != 0) return r;
+    return launch_state_passing(g, init_state, states, final_state, s, stream);
+  }
   if (bf16_in)
     return launch_chunk<true>(x, B, dt_t, g, init_state, states, final_state, s, st);
   return launch_chunk<false>(x, B, dt_t, g, init_state, states, final_state, s, st);

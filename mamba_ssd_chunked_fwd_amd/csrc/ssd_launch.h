@@ -26,6 +26,14 @@ int launch_compute_out(const void* x, const void* B, const void* C,
                        const float* D, void* y, bool bf16_in, bool bf16_out,
                        const Shape& s, void* stream);
 
+// The two-level form of stage 2 (chunk_state writes each chunk's zero-state
+// contribution into the slot of the state it feeds; state_passing turns the
+// slots into the states in place).
+int launch_chunk_state(const void* x, const void* B, const float* dt_t, const float* g,
+                       float* states, float* fin, const Shape& s, void* stream);
+int launch_state_passing(const float* g, const float* init, float* states, float* fin,
+                         const Shape& s, void* stream);
+
 int launch_decode_step(const void* x, const float* dt, const float* A, const void* B,
                        const void* C, const float* D, float* state, void* y, bool bf16_in,
                        bool bf16_out, const Shape& s, void* stream);

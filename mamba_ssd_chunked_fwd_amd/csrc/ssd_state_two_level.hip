@@ -1,0 +1,254 @@
+// The two-level form of stage 2: per-chunk local states computed for every
+// chunk in parallel, then a short sequential pass that carries the state
+// across chunks element by element.
+//
+// With P_c = X_c^T (w o B_c), w_t = dt_t 2^{g_last(c) - g_t}, the chunk's
+// contribution from a zero state, the jump of stage 2 is
+//   S_{c+1} = 2^{g_last(c)} S_c + P_c
+// ("Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+// CUDA Tile", "Step 1: Jump the State Across a Chunk with One Matmul" and
+// "Kernel 2: fwd_pass_state").  Chunk-state computes every P_c at once (no
+// chain), writing P_c into the slot of the state it feeds, states[c+1] (the
+// last one into final); state-passing then turns those slots into the states
+// in place: states[0] = init, states[c] = 2^{g_last(c-1)} states[c-1] +
+// states[c], final = 2^{g_last(nc-1)} states[nc-1] + final.
+//
+// MI355X design.
+// * chunk_state: one workgroup (4 waves) per (b, chunk, head); wave w owns
+//   state rows 16w..16w+15 and all N columns (N/16 accumulator blocks of
+//   P^T[n][p], lane: column p, four consecutive n, so stores are 16 bytes).
+//   The chunk is consumed in 64-token sub-tiles: x (as w o x, split bf16 hi +
+//   lo) and B staged in LDS, operands read with the LDS transpose read, the
+//   same k-slot map as the fused pass.  No state is carried, so every
+//   (b, chunk, head) is independent and the grid has b * nc * H workgroups.
+// * state_passing: a pure element-wise stream.  A thread owns one 16-byte
+//   unit (four consecutive n of one row p) of one (b, h) and walks the
+//   chunks in blocks of D.  The loads do not depend on the carried value,
+//   so the next block's loads are in flight while a block is combined.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+namespace {
+
+constexpr uint32_t kPastRange = 0x7FFFFFF0u;
+
+template <int N>
+struct TlStride {
+  static constexpr int value = N + 16;
+};
+
+template <int T, int N>
+__global__ __launch_bounds__(256) void chunk_state_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
+    const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
+    float* __restrict__ final_state, int L, int H, int G, int nc) {
+  constexpr int ST = 64;                       // tokens per sub-tile
+  constexpr int NSUB = T / ST;
+  constexpr int XS = kHeadDim + 16;            // w o x row stride (bf16)
+  constexpr int BS = TlStride<N>::value;       // B row stride (bf16)
+  constexpr int NB = N / 16;                   // accumulator blocks per wave
+  constexpr int XU = ST * kHeadDim / 8 / 256;  // 16-byte x units per thread (2)
+  constexpr int BU = ST * N / 8 / 256;         // 16-byte B units per thread
+  __shared__ __attribute__((aligned(16))) uint16_t whs[ST * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t wls[ST * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t bts[ST * BS];
+
+  // blocks: (b, c, h) with h fastest
+  const int item = blockIdx.x;
+  const int h = item % H;
+  const int c = (item / H) % nc;
+  const int b = item / (H * nc);
+  const int grp = h / (H / G);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+
+  const uint32_t xrow = (uint32_t)(H * kHeadDim), brow = (uint32_t)(G * N);
+  const rsrc_t xr = make_rsrc(x + ((size_t)b * L * H + h) * kHeadDim,
+                              ((uint32_t)(L - 1) * xrow + kHeadDim) * 2u);
+  const rsrc_t br = make_rsrc(Bm + ((size_t)b * L * G + grp) * N,
+                              ((uint32_t)(L - 1) * brow + N) * 2u);
+  const size_t grow = ((size_t)b * H + h) * L;
+  const rsrc_t gr = make_rsrc(g + grow, (uint32_t)L * 4u);
+  const rsrc_t dr = make_rsrc(dt_t + grow, (uint32_t)L * 4u);
+  const int tlast = min(c * T + T, L) - 1;
+  const float gl = g[grow + tlast];
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = (f32x4){0, 0, 0, 0};
+
+  // transpose-read offsets: rows t = 4 lq + (lr >> 2) (+32 kk, +16), column
+  // c0 + 4 (lr & 3)
+  const int rsel = 4 * lq + (lr >> 2), csel = 4 * (lr & 3);
+#pragma unroll 1
+  for (int sub = 0; sub < NSUB; ++sub) {
+    const uint32_t t0 = (uint32_t)(c * T + sub * ST);
+    // loads of the sub-tile: x units (token, 8 p), B units (token, 8 n)
+    u32x4 xv[XU], bv[BU];
+    float gv[XU], dv[XU];
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int u = tid + 256 * i, t = u >> 3, c8 = u & 7;
+      xv[i] = load_b128(xr, ((t0 + t) * xrow + 8 * c8) * 2u);
+      const uint32_t go = t0 + t < (uint32_t)L ? (t0 + t) * 4u : kPastRange;
+      gv[i] = load_f32(gr, go);
+      dv[i] = load_f32(dr, go);
+    }
+#pragma unroll
+    for (int i = 0; i < BU; ++i) {
+      const int u = tid + 256 * i, t = u / (N / 8), c8 = u % (N / 8);
+      bv[i] = load_b128(br, ((t0 + t) * brow + 8 * c8) * 2u);
+    }
+    if (sub > 0) __syncthreads();  // the previous sub-tile's reads are done
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int u = tid + 256 * i, t = u >> 3, c8 = u & 7;
+      // tokens past the end read dt = g = 0 and x = 0, so w o x = 0
+      const float w = dv[i] * exp2_hw(gl - gv[i]);
+      uint32_t hv[4], lv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        split_bf16(bf16_lo(xv[i][e]) * w, bf16_hi(xv[i][e]) * w, hv[e], lv[e]);
+      *(u32x4*)(whs + t * XS + 8 * c8) = make_u32x4(hv);
+      *(u32x4*)(wls + t * XS + 8 * c8) = make_u32x4(lv);
+    }
+#pragma unroll
+    for (int i = 0; i < BU; ++i) {
+      const int u = tid + 256 * i, t = u / (N / 8), c8 = u % (N / 8);
+      *(u32x4*)(bts + t * BS + 8 * c8) = bv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < ST / 32; ++kk) {
+      const int wo = (32 * kk + rsel) * XS + 16 * wave + csel;
+      const u32x2 a0 = lds_read_tr16(whs + wo), a1 = lds_read_tr16(whs + wo + 16 * XS);
+      const u32x2 c0 = lds_read_tr16(wls + wo), c1 = lds_read_tr16(wls + wo + 16 * XS);
+      const u32x4 wxh = {a0[0], a0[1], a1[0], a1[1]};
+      const u32x4 wxl = {c0[0], c0[1], c1[0], c1[1]};
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int bo = (32 * kk + rsel) * BS + 16 * j + csel;
+        const u32x2 e0 = lds_read_tr16(bts + bo), e1 = lds_read_tr16(bts + bo + 16 * BS);
+        const u32x4 bb = {e0[0], e0[1], e1[0], e1[1]};
+        acc[j] = mfma_bf16(bb, wxh, acc[j]);
+        acc[j] = mfma_bf16(bb, wxl, acc[j]);
+      }
+    }
+  }
+
+  // P_c into the slot of the state it feeds: states[c + 1], or final.
+  float* dst = nullptr;
+  if (c + 1 < nc) {
+    dst = states + (((size_t)b * H + h) * nc + c + 1) * kHeadDim * N;
+  } else if (final_state) {
+    dst = final_state + ((size_t)b * H + h) * kHeadDim * N;
+  }
+  if (dst) {
+    const int p = 16 * wave + lr;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) *(f32x4*)(dst + (size_t)p * N + 16 * j + 4 * lq) = acc[j];
+  }
+}
+
+// ---------------------------------------------------------------- passing
+template <int N, int D>
+__global__ __launch_bounds__(256) void state_passing_kernel(
+    const float* __restrict__ g, const float* __restrict__ init, float* __restrict__ states,
+    float* __restrict__ final_state, int L, int T, int nc) {
+  constexpr int UNITS = kHeadDim * N / 4;      // 16-byte units per state
+  constexpr int WPB = UNITS / 256;             // workgroups per (b, h)
+  const int bh = blockIdx.x / WPB;
+  const int u = (blockIdx.x % WPB) * 256 + threadIdx.x;
+  const size_t sstride = (size_t)kHeadDim * N;
+  float* st = states + (size_t)bh * nc * sstride + 4 * (size_t)u;
+  const float* gh = g + (size_t)bh * L;
+
+  f32x4 s = init ? *(const f32x4*)(init + bh * sstride + 4 * (size_t)u) : (f32x4){0, 0, 0, 0};
+  *(f32x4*)st = s;
+  // Chunks 1 .. nc-1 in blocks of D, software-pipelined over two register
+  // blocks: the loads of block j+1 are issued before block j is combined.
+  // Chunks past the end are clamped to the last one (a harmless re-read).
+  auto load_block = [&](int c0, f32x4 (&v)[D], float (&dec)[D]) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int c = min(c0 + d, nc - 1);
+      v[d] = *(const f32x4*)(st + (size_t)c * sstride);
+      dec[d] = exp2_hw(gh[min(c * T, L) - 1]);   // g_last of chunk c - 1
+    }
+  };
+  auto combine_block = [&](int c0, const f32x4 (&v)[D], const float (&dec)[D]) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int c = c0 + d;
+      if (c < nc) {
+        s = dec[d] * s + v[d];
+        *(f32x4*)(st + (size_t)c * sstride) = s;
+      }
+    }
+  };
+  f32x4 va[D], vb[D];
+  float da[D], db[D];
+  if (nc > 1) load_block(1, va, da);
+#pragma unroll 1
+  for (int c0 = 1; c0 < nc; c0 += 2 * D) {
+    if (c0 + D < nc) load_block(c0 + D, vb, db);
+    combine_block(c0, va, da);
+    if (c0 + 2 * D < nc) load_block(c0 + 2 * D, va, da);
+    if (c0 + D < nc) combine_block(c0 + D, vb, db);
+  }
+  if (final_state) {
+    float* f = final_state + bh * sstride + 4 * (size_t)u;
+    const float dec = exp2_hw(gh[min(nc * T, L) - 1]);
+    *(f32x4*)f = dec * s + *(const f32x4*)f;
+  }
+}
+
+template <int T, int N>
+int launch_cs(const void* x, const void* B, const float* dt_t, const float* g, float* states,
+              float* fin, const Shape& s, hipStream_t st) {
+  const int nc = (int)s.nchunks();
+  const unsigned blocks = (unsigned)(s.batch * nc * s.nheads);
+  hipLaunchKernelGGL((chunk_state_bf16<T, N>), dim3(blocks), dim3(256), 0, st,
+                     (const uint16_t*)x, (const uint16_t*)B, dt_t, g, states, fin,
+                     (int)s.seqlen, (int)s.nheads, (int)s.ngroups, nc);
+  return (int)hipGetLastError();
+}
+
+template <int N>
+int launch_sp(const float* g, const float* init, float* states, float* fin, const Shape& s,
+              hipStream_t st) {
+  constexpr int UNITS = kHeadDim * N / 4;
+  const unsigned blocks = (unsigned)(s.batch * s.nheads * (UNITS / 256));
+  hipLaunchKernelGGL((state_passing_kernel<N, 8>), dim3(blocks), dim3(256), 0, st, g, init,
+                     states, fin, (int)s.seqlen, (int)s.chunk, (int)s.nchunks());
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_chunk_state(const void* x, const void* B, const float* dt_t, const float* g,
+                       float* states, float* fin, const Shape& s, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  if (s.dstate == 64) {
+    switch (s.chunk) {
+      case 64: return launch_cs<64, 64>(x, B, dt_t, g, states, fin, s, st);
+      case 128: return launch_cs<128, 64>(x, B, dt_t, g, states, fin, s, st);
+      default: return launch_cs<256, 64>(x, B, dt_t, g, states, fin, s, st);
+    }
+  }
+  switch (s.chunk) {
+    case 64: return launch_cs<64, 128>(x, B, dt_t, g, states, fin, s, st);
+    case 128: return launch_cs<128, 128>(x, B, dt_t, g, states, fin, s, st);
+    default: return launch_cs<256, 128>(x, B, dt_t, g, states, fin, s, st);
+  }
+}
+
+int launch_state_passing(const float* g, const float* init, float* states, float* fin,
+                         const Shape& s, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  return s.dstate == 64 ? launch_sp<64>(g, init, states, fin, s, st)
+                        : launch_sp<128>(g, init, states, fin, s, st);
+}
+
+}  // namespace ssd

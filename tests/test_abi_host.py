@@ -41,7 +41,8 @@ def test_every_declared_function_is_exported():
                           "ssd_chunk_cumsum", "ssd_fwd_pass_state",
                           "ssd_compute_out", "ssd_forward", "ssd_decode_step",
                           "ssd_causal_conv1d", "ssd_gdn_chunk_fwd_h",
-                          "ssd_gdn_chunk_fwd_o"}
+                          "ssd_gdn_chunk_fwd_o", "ssd_chunk_state",
+                          "ssd_state_passing"}
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -149,6 +150,27 @@ def test_causal_conv1d_validates():
     assert call(W=5) == UNS
     assert call(L=1 << 29) == UNS
     assert call(b=1 << 30, d=1 << 12, L=1 << 12) == UNS
+
+
+def test_two_level_entry_points_validate():
+    d = dims()
+    cs = lambda dd, **o: lib.ssd_chunk_state(
+        o.get("x", FAKE), o.get("B", FAKE), o.get("dtt", FAKE), o.get("g", FAKE),
+        o.get("st", FAKE), o.get("fin", None), o.get("ind", ssd.SSD_BF16),
+        ctypes.byref(dd) if dd is not None else None, None)
+    sp = lambda dd, **o: lib.ssd_state_passing(
+        o.get("g", FAKE), o.get("init", None), o.get("st", FAKE), o.get("fin", None),
+        ctypes.byref(dd) if dd is not None else None, None)
+    assert cs(None) == INV and sp(None) == INV
+    for name in ("x", "B", "dtt", "g", "st"):
+        assert cs(d, **{name: None}) == INV, name
+        assert cs(d, **{name: MISALIGNED}) == INV, name
+    assert cs(d, fin=MISALIGNED) == INV and cs(d, ind=9) == INV
+    assert cs(d, ind=ssd.SSD_F32) == UNS
+    assert cs(dims(dstate=96)) == UNS and sp(dims(dstate=96)) == UNS
+    for name in ("g", "st"):
+        assert sp(d, **{name: None}) == INV, name
+    assert sp(d, init=MISALIGNED) == INV and sp(d, fin=MISALIGNED) == INV
 
 
 def test_gdn_entry_points_validate():
