@@ -14,13 +14,17 @@
 // states[c], final = 2^{g_last(nc-1)} states[nc-1] + final.
 //
 // MI355X design.
-// * chunk_state: one workgroup (4 waves) per (b, chunk, head); wave w owns
-//   state rows 16w..16w+15 and all N columns (N/16 accumulator blocks of
-//   P^T[n][p], lane: column p, four consecutive n, so stores are 16 bytes).
-//   The chunk is consumed in 64-token sub-tiles: x (as w o x, split bf16 hi +
+// * chunk_state: one workgroup per (b, chunk, block of HB heads of one
+//   group), four waves per head; wave (hh, w) owns rows 16w..16w+15 of head
+//   hh and all N columns (N/16 accumulator blocks of P^T[n][p], lane: column
+//   p, four consecutive n, so stores are 16 bytes).  The HB heads share one
+//   staged B tile.
+//   The chunk is consumed in sub-tiles (64 tokens, 32 with several heads, so
+//   the LDS stays under 90 KB): x (as w o x, split bf16 hi +
 //   lo) and B staged in LDS, operands read with the LDS transpose read, the
 //   same k-slot map as the fused pass.  No state is carried, so every
-//   (b, chunk, head) is independent and the grid has b * nc * H workgroups.
+//   (b, chunk, head) is independent and the grid has b * nc * H / HB
+//   workgroups.
 // * state_passing: a pure element-wise stream.  A thread owns one 16-byte
 //   unit (four consecutive n of one row p) of one (b, h) and walks the
 //   chunks in blocks of D.  The loads do not depend on the carried value,
@@ -38,41 +42,48 @@ struct TlStride {
   static constexpr int value = N + 16;
 };
 
-template <int T, int N>
-__global__ __launch_bounds__(256) void chunk_state_bf16(
+template <int T, int N, int HB>
+__global__ __launch_bounds__(256 * HB) void chunk_state_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
     float* __restrict__ final_state, int L, int H, int G, int nc) {
-  constexpr int ST = 64;                       // tokens per sub-tile
+  constexpr int ST = HB == 1 ? 64 : 32;        // tokens per sub-tile
   constexpr int NSUB = T / ST;
   constexpr int XS = kHeadDim + 16;            // w o x row stride (bf16)
   constexpr int BS = TlStride<N>::value;       // B row stride (bf16)
   constexpr int NB = N / 16;                   // accumulator blocks per wave
-  constexpr int XU = ST * kHeadDim / 8 / 256;  // 16-byte x units per thread (2)
-  constexpr int BU = ST * N / 8 / 256;         // 16-byte B units per thread
-  __shared__ __attribute__((aligned(16))) uint16_t whs[ST * XS];
-  __shared__ __attribute__((aligned(16))) uint16_t wls[ST * XS];
+  constexpr int NTHR = 256 * HB;
+  constexpr int XU = HB * ST * kHeadDim / 8 / NTHR;  // 16-byte x units per thread
+  constexpr int BUN = ST * N / 8;                     // 16-byte B units per sub-tile
+  constexpr int BU = (BUN + NTHR - 1) / NTHR;         // ... per thread (the last partial)
+  static_assert(XU * NTHR == HB * ST * kHeadDim / 8, "x units");
+  __shared__ __attribute__((aligned(16))) uint16_t whs[HB * ST * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t wls[HB * ST * XS];
   __shared__ __attribute__((aligned(16))) uint16_t bts[ST * BS];
 
-  // blocks: (b, c, h) with h fastest
+  // blocks: (b, c, block of HB heads of one group) with the head block
+  // fastest; the HB heads share the staged B tile
+  const int nhb = H / HB;
   const int item = blockIdx.x;
-  const int h = item % H;
-  const int c = (item / H) % nc;
-  const int b = item / (H * nc);
-  const int grp = h / (H / G);
+  const int h0 = (item % nhb) * HB;
+  const int c = (item / nhb) % nc;
+  const int b = item / (nhb * nc);
+  const int grp = h0 / (H / G);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
+  const int hh = wave >> 2, wr = wave & 3;      // this wave's head and 16-row slice
+  const int h = h0 + hh;
 
   const uint32_t xrow = (uint32_t)(H * kHeadDim), brow = (uint32_t)(G * N);
-  const rsrc_t xr = make_rsrc(x + ((size_t)b * L * H + h) * kHeadDim,
-                              ((uint32_t)(L - 1) * xrow + kHeadDim) * 2u);
+  const rsrc_t xr = make_rsrc(x + ((size_t)b * L * H + h0) * kHeadDim,
+                              ((uint32_t)(L - 1) * xrow + (uint32_t)HB * kHeadDim) * 2u);
   const rsrc_t br = make_rsrc(Bm + ((size_t)b * L * G + grp) * N,
                               ((uint32_t)(L - 1) * brow + N) * 2u);
-  const size_t grow = ((size_t)b * H + h) * L;
-  const rsrc_t gr = make_rsrc(g + grow, (uint32_t)L * 4u);
-  const rsrc_t dr = make_rsrc(dt_t + grow, (uint32_t)L * 4u);
+  // g and dt_t rows of the HB heads, [hh][L]
+  const size_t grow = ((size_t)b * H + h0) * L;
+  const rsrc_t gr = make_rsrc(g + grow, (uint32_t)(HB * L) * 4u);
+  const rsrc_t dr = make_rsrc(dt_t + grow, (uint32_t)(HB * L) * 4u);
   const int tlast = min(c * T + T, L) - 1;
-  const float gl = g[grow + tlast];
 
   f32x4 acc[NB];
 #pragma unroll
@@ -81,47 +92,58 @@ __global__ __launch_bounds__(256) void chunk_state_bf16(
   // transpose-read offsets: rows t = 4 lq + (lr >> 2) (+32 kk, +16), column
   // c0 + 4 (lr & 3)
   const int rsel = 4 * lq + (lr >> 2), csel = 4 * (lr & 3);
-#pragma unroll 1
-  for (int sub = 0; sub < NSUB; ++sub) {
+  // Loads of a sub-tile (x units: head, token, 8 p; B units: token, 8 n)
+  // land in registers; the next sub-tile's are issued before the current
+  // one is consumed from LDS.  Each x unit carries its head's g_last.
+  u32x4 xv[XU], bv[BU];
+  float gv[XU], dv[XU], glv[XU];
+#pragma unroll
+  for (int i = 0; i < XU; ++i) {
+    const int uh = (tid + NTHR * i) / (ST * 8);
+    glv[i] = g[grow + (size_t)uh * L + tlast];
+  }
+  auto issue = [&](int sub) {
     const uint32_t t0 = (uint32_t)(c * T + sub * ST);
-    // loads of the sub-tile: x units (token, 8 p), B units (token, 8 n)
-    u32x4 xv[XU], bv[BU];
-    float gv[XU], dv[XU];
 #pragma unroll
     for (int i = 0; i < XU; ++i) {
-      const int u = tid + 256 * i, t = u >> 3, c8 = u & 7;
-      xv[i] = load_b128(xr, ((t0 + t) * xrow + 8 * c8) * 2u);
-      const uint32_t go = t0 + t < (uint32_t)L ? (t0 + t) * 4u : kPastRange;
+      const int u = tid + NTHR * i, uh = u / (ST * 8), t = (u >> 3) % ST, c8 = u & 7;
+      xv[i] = load_b128(xr, ((t0 + t) * xrow + uh * kHeadDim + 8 * c8) * 2u);
+      const uint32_t go = t0 + t < (uint32_t)L ? ((uint32_t)uh * L + t0 + t) * 4u : kPastRange;
       gv[i] = load_f32(gr, go);
       dv[i] = load_f32(dr, go);
     }
 #pragma unroll
     for (int i = 0; i < BU; ++i) {
-      const int u = tid + 256 * i, t = u / (N / 8), c8 = u % (N / 8);
-      bv[i] = load_b128(br, ((t0 + t) * brow + 8 * c8) * 2u);
+      const int u = tid + NTHR * i, t = u / (N / 8), c8 = u % (N / 8);
+      if (BUN % NTHR == 0 || u < BUN) bv[i] = load_b128(br, ((t0 + t) * brow + 8 * c8) * 2u);
     }
+  };
+  issue(0);
+#pragma unroll 1
+  for (int sub = 0; sub < NSUB; ++sub) {
     if (sub > 0) __syncthreads();  // the previous sub-tile's reads are done
 #pragma unroll
     for (int i = 0; i < XU; ++i) {
-      const int u = tid + 256 * i, t = u >> 3, c8 = u & 7;
+      const int u = tid + NTHR * i, uh = u / (ST * 8), t = (u >> 3) % ST, c8 = u & 7;
       // tokens past the end read dt = g = 0 and x = 0, so w o x = 0
-      const float w = dv[i] * exp2_hw(gl - gv[i]);
+      const float w = dv[i] * exp2_hw(glv[i] - gv[i]);
       uint32_t hv[4], lv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         split_bf16(bf16_lo(xv[i][e]) * w, bf16_hi(xv[i][e]) * w, hv[e], lv[e]);
-      *(u32x4*)(whs + t * XS + 8 * c8) = make_u32x4(hv);
-      *(u32x4*)(wls + t * XS + 8 * c8) = make_u32x4(lv);
+      *(u32x4*)(whs + (uh * ST + t) * XS + 8 * c8) = make_u32x4(hv);
+      *(u32x4*)(wls + (uh * ST + t) * XS + 8 * c8) = make_u32x4(lv);
     }
 #pragma unroll
     for (int i = 0; i < BU; ++i) {
-      const int u = tid + 256 * i, t = u / (N / 8), c8 = u % (N / 8);
-      *(u32x4*)(bts + t * BS + 8 * c8) = bv[i];
+      const int u = tid + NTHR * i, t = u / (N / 8), c8 = u % (N / 8);
+      if (BUN % NTHR == 0 || u < BUN) *(u32x4*)(bts + t * BS + 8 * c8) = bv[i];
     }
+    if (sub + 1 < NSUB) issue(sub + 1);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < ST / 32; ++kk) {
-      const int wo = (32 * kk + rsel) * XS + 16 * wave + csel;
+      const int wo = (hh * ST + 32 * kk + rsel) * XS + 16 * wr + csel;
       const u32x2 a0 = lds_read_tr16(whs + wo), a1 = lds_read_tr16(whs + wo + 16 * XS);
       const u32x2 c0 = lds_read_tr16(wls + wo), c1 = lds_read_tr16(wls + wo + 16 * XS);
       const u32x4 wxh = {a0[0], a0[1], a1[0], a1[1]};
@@ -145,7 +167,7 @@ __global__ __launch_bounds__(256) void chunk_state_bf16(
     dst = final_state + ((size_t)b * H + h) * kHeadDim * N;
   }
   if (dst) {
-    const int p = 16 * wave + lr;
+    const int p = 16 * wr + lr;
 #pragma unroll
     for (int j = 0; j < NB; ++j) *(f32x4*)(dst + (size_t)p * N + 16 * j + 4 * lq) = acc[j];
   }
@@ -204,15 +226,30 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
   }
 }
 
-template <int T, int N>
-int launch_cs(const void* x, const void* B, const float* dt_t, const float* g, float* states,
-              float* fin, const Shape& s, hipStream_t st) {
+template <int T, int N, int HB>
+int launch_cs_hb(const void* x, const void* B, const float* dt_t, const float* g,
+                 float* states, float* fin, const Shape& s, hipStream_t st) {
   const int nc = (int)s.nchunks();
-  const unsigned blocks = (unsigned)(s.batch * nc * s.nheads);
-  hipLaunchKernelGGL((chunk_state_bf16<T, N>), dim3(blocks), dim3(256), 0, st,
+  const unsigned blocks = (unsigned)(s.batch * nc * (s.nheads / HB));
+  hipLaunchKernelGGL((chunk_state_bf16<T, N, HB>), dim3(blocks), dim3(256 * HB), 0, st,
                      (const uint16_t*)x, (const uint16_t*)B, dt_t, g, states, fin,
                      (int)s.seqlen, (int)s.nheads, (int)s.ngroups, nc);
   return (int)hipGetLastError();
+}
+
+// Heads per workgroup: the most (4, 2 or 1) that divides the heads of a
+// group while leaving at least two workgroups per CU; they share one
+// staged B tile.
+template <int T, int N>
+int launch_cs(const void* x, const void* B, const float* dt_t, const float* g, float* states,
+              float* fin, const Shape& s, hipStream_t st) {
+  const int64_t hpg = s.nheads / s.ngroups;
+  const int64_t items = s.batch * s.nchunks() * s.nheads;
+  if (hpg % 4 == 0 && items / 4 >= 512)
+    return launch_cs_hb<T, N, 4>(x, B, dt_t, g, states, fin, s, st);
+  if (hpg % 2 == 0 && items / 2 >= 512)
+    return launch_cs_hb<T, N, 2>(x, B, dt_t, g, states, fin, s, st);
+  return launch_cs_hb<T, N, 1>(x, B, dt_t, g, states, fin, s, st);
 }
 
 template <int N>
