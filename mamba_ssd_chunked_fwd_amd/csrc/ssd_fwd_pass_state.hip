@@ -516,8 +516,10 @@ struct BfCfg {
 };
 // Workgroup tiles (heads, 16-row slices, columns, column blocks per wave).
 constexpr BfCfg kBfCfgs[] = {{4, 1, 64, 2}, {3, 1, 64, 1}, {2, 1, 64, 1}, {1, 1, 64, 1},
-                             {2, 1, 32, 1}, {1, 1, 32, 1}, {1, 1, 16, 1}, {1, 4, 128, 4}};
+                             {2, 1, 32, 1}, {1, 1, 32, 1}, {1, 1, 16, 1}, {1, 4, 128, 4},
+                             {1, 4, 64, 1}};
 constexpr int kWholeHeadCfg = 7;
+constexpr int kHalfHeadCfg = 8;
 constexpr int kNumBfCfgs = sizeof(kBfCfgs) / sizeof(kBfCfgs[0]);
 
 int64_t bf_cfg_wgs(const BfCfg& c, const Shape& s) {
@@ -529,7 +531,14 @@ int choose_bf_cfg(const Shape& s, int cus) {
   // workgroup instead of once per 16-row slice; they win once there are
   // enough (b, h) pairs to occupy most CUs (measured: 190 -> 163 us on the
   // 2 x 8192-token, 80-head layer; slower with 96 or 32 pairs).
-  if (s.dstate == 128 && s.batch * s.nheads * 5 >= (int64_t)cus * 3) return kWholeHeadCfg;
+  const int64_t pairs = s.batch * s.nheads;
+  if (s.dstate == 128 && pairs * 5 >= (int64_t)cus * 3) return kWholeHeadCfg;
+  // Half-head tiles (64 rows x 64 columns, 16 waves) also read whole x
+  // lines; with 3/8 to 1/2 as many (b, h) pairs as CUs they give one tile
+  // per CU on 3/4 of the chip or more, and beat 16-row tiles on every CU
+  // (measured: 51.8 -> 47.3 us on the 4 x 2048-token, 24-head layer).
+  if (s.dstate == 128 && pairs * 8 >= (int64_t)cus * 3 && pairs * 2 <= (int64_t)cus)
+    return kHalfHeadCfg;
   const int64_t hpg = s.nheads / s.ngroups;
   int most = -1;
   int64_t most_wgs = -1;
@@ -597,6 +606,8 @@ int launch_bf_n(const void* x, const void* B, const float* dt_t, const float* g,
     case 5: return launch_bf<T, N, 1, 1, 32, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
     case kWholeHeadCfg:
       return launch_bf<T, N, 1, 4, 128, 4>(xb, bb, dt_t, g, init, states, fin, s, st);
+    case kHalfHeadCfg:
+      return launch_bf<T, N, 1, 4, 64, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
     default: return launch_bf<T, N, 1, 1, 16, 1>(xb, bb, dt_t, g, init, states, fin, s, st);
   }
 }
@@ -662,8 +673,9 @@ int launch_chunk(const void* x, const void* B, const float* dt_t, const float* g
 // bytes of the one-pass kernel but has no chain per workgroup.  It wins
 // where the one-pass grid is long chains on few waves: measured on the
 // 65536-token, 32-head sequence (512 chunks, four waves per CU) it takes
-// 392 us against 492; with 32 chunks (small and large layers) it loses
-// (79 vs 53 us, 172 vs 160 us).
+// about 395 us against 400-490 (the one-pass time varies from run to run);
+// with 32 chunks (small and large layers) it loses (80 vs 53 us, 166 vs
+// 159 us).
 bool use_two_level(const Shape& s, int cus) {
   const int c = choose_bf_cfg(s, cus);
   if (c < 0) return false;

@@ -40,7 +40,9 @@ SMALL = [
     _wl("bf16_T64_N64_shorter_than_chunk", "bf16", 3, 37, 2, 1, 64, 64, False),
     _wl("bf16_T64_N64_grouped_init", "bf16", 2, 450, 6, 3, 64, 64, True),
     # shapes that select each bf16 state-pass tile (heads x columns per workgroup)
-    _wl("bf16_T64_N128_3head_tiles", "bf16", 16, 130, 6, 1, 128, 64, True),
+    _wl("bf16_T64_N128_3head_tiles", "bf16", 22, 130, 6, 1, 128, 64, True),
+    _wl("bf16_T64_N128_half_head_tiles_ragged_init", "bf16", 16, 200, 6, 1, 128, 64, True),
+    _wl("bf16_T128_N128_half_head_tiles_grouped", "bf16", 4, 260, 30, 3, 128, 128, False),
     _wl("bf16_T128_N128_whole_head_tiles_grouped", "bf16", 16, 300, 10, 2, 128, 128, False),
     _wl("bf16_T64_N128_whole_head_tiles_ragged_init", "bf16", 2, 130, 80, 1, 128, 64, True),
     _wl("bf16_T64_N128_4head_tiles_grouped", "bf16", 4, 100, 32, 4, 128, 64, True),
