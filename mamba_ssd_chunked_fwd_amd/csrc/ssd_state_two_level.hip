@@ -20,7 +20,7 @@
 //   p, four consecutive n, so stores are 16 bytes).  The HB heads share one
 //   staged B tile.
 //   The chunk is consumed in sub-tiles (64 tokens, 32 with several heads, so
-//   the LDS stays under 90 KB): x (as w o x, split bf16 hi +
+//   the LDS stays near 46 KB for two heads): x (as w o x, split bf16 hi +
 //   lo) and B staged in LDS, operands read with the LDS transpose read, the
 //   same k-slot map as the fused pass.  No state is carried, so every
 //   (b, chunk, head) is independent and the grid has b * nc * H / HB
@@ -237,17 +237,18 @@ int launch_cs_hb(const void* x, const void* B, const float* dt_t, const float* g
   return (int)hipGetLastError();
 }
 
-// Heads per workgroup: the most (4, 2 or 1) that divides the heads of a
-// group while leaving at least two workgroups per CU; they share one
-// staged B tile.
+// Heads per workgroup: two (sharing one staged B tile) when the heads of a
+// group pair up and the grid keeps at least one workgroup per CU, else one.
+// Measured on MI355X, two heads beat one and four at every layer shape
+// (4 x 2048 tokens, 24 heads: 31.8 us against 33.9 and 34.1; 2 x 8192, 80
+// heads: 85.6 against 98.8 and 92.1; 65536 tokens, 32 heads: 183 against
+// 197 and 196): four heads need 83 KB of LDS, one workgroup per CU.
 template <int T, int N>
 int launch_cs(const void* x, const void* B, const float* dt_t, const float* g, float* states,
               float* fin, const Shape& s, hipStream_t st) {
   const int64_t hpg = s.nheads / s.ngroups;
   const int64_t items = s.batch * s.nchunks() * s.nheads;
-  if (hpg % 4 == 0 && items / 4 >= 512)
-    return launch_cs_hb<T, N, 4>(x, B, dt_t, g, states, fin, s, st);
-  if (hpg % 2 == 0 && items / 2 >= 512)
+  if (hpg % 2 == 0 && items / 2 >= 256)
     return launch_cs_hb<T, N, 2>(x, B, dt_t, g, states, fin, s, st);
   return launch_cs_hb<T, N, 1>(x, B, dt_t, g, states, fin, s, st);
 }

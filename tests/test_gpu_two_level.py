@@ -63,8 +63,8 @@ CASES = [
     (1, 1, 2, 2, 128, 128, True),       # one token
     (2, 450, 6, 3, 64, 64, True),
     (2, 4096, 8, 2, 128, 64, True),     # two heads per chunk_state workgroup
-    (2, 8170, 8, 2, 64, 64, False),     # four heads per workgroup, ragged
-    (1, 32768, 16, 1, 64, 256, False),  # four heads, 256-token chunks
+    (2, 8170, 8, 2, 64, 64, False),     # two heads per workgroup, ragged
+    (1, 16384, 16, 1, 64, 256, False),  # two heads, 256-token chunks
 ]
 
 
