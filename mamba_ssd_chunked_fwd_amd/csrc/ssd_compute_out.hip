@@ -124,6 +124,9 @@ __global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t sh[64 * SS];
   __shared__ __attribute__((aligned(16))) uint16_t sl[64 * SS];
   __shared__ float gs[T], ds[T];
+  // per wave: 2^{g_e - g_j} dt_j for the 32 tokens j of one k-step, e its
+  // last token
+  __shared__ __attribute__((aligned(16))) float cw[Gm::NW][32];
 
   int k0, k1;
   item_range(items, k0, k1);
@@ -293,21 +296,44 @@ __global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_bf16(
 
       // Y^T += X^T L'^T over 32-token k-steps s: slots 0..3 carry tokens
       // 32s + 4lq + rr and slots 4..7 tokens 32s + 16 + 4lq + rr.
+      // A step wholly below the row block (every j <= e = 32s + 31 < i)
+      // factors the decay as 2^{g_i - g_e} 2^{g_e - g_j}, both exponents
+      // <= 0: the wave forms the 32 column factors once (one exponential
+      // per lane) and shares them through its own LDS row, each lane adds
+      // one exponential for its row, and no causal select is needed.  The
+      // step that meets the diagonal takes the entries one by one.
+      const bool row_in = t0 + i < L;
 #pragma unroll
       for (int s = 0; s < NE / 2; ++s) {
         if (2 * s <= ib) {
           const int e0 = m == 0 ? 2 * s : NE - 1 - 2 * s;
           const int e1 = m == 0 ? 2 * s + 1 : NE - 2 - 2 * s;
           float v[8];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const f32x4 cbv = half ? cb[e1] : cb[e0];
+          if (2 * s + 2 <= ib) {
+            const float ge = gs[32 * s + 31];
+            const int jl = 32 * s + (lane & 31);
+            const float cl = exp2_hw(ge - gs[jl]) * ds[jl];
+            if (lane < 32) cw[wave][lane] = cl;
+            // rows past the sequence's end are never stored
+            const float ai = row_in ? exp2_hw(gi - ge) : 0.0f;
+            const f32x4 c0 = *(const f32x4*)(&cw[wave][4 * lq]);
+            const f32x4 c1 = *(const f32x4*)(&cw[wave][16 + 4 * lq]);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-              const int j = 32 * s + 16 * half + 4 * lq + rr;
-              float w = cbv[rr] * exp2_hw(gi - gs[j]) * ds[j];
-              if (j == i) w += Dh;
-              v[4 * half + rr] = j <= i ? w : 0.0f;
+              v[rr] = cb[e0][rr] * (c0[rr] * ai);
+              v[4 + rr] = cb[e1][rr] * (c1[rr] * ai);
+            }
+          } else {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const f32x4 cbv = half ? cb[e1] : cb[e0];
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int j = 32 * s + 16 * half + 4 * lq + rr;
+                float w = cbv[rr] * exp2_hw(gi - gs[j]) * ds[j];
+                if (j == i) w += Dh;
+                v[4 * half + rr] = j <= i ? w : 0.0f;
+              }
             }
           }
           uint32_t lh4[4], ll4[4];
