@@ -41,9 +41,11 @@ METRIC = "SSD forward tokens/sec + % of HBM/MFMA roofline, 1×MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_TFLOPS = 2500.0      # dense
 FP32_MFMA_TFLOPS = 157.3
-STAGE_SOURCES = {"chunk_cumsum": "ssd_chunk_cumsum.hip",
-                 "fwd_pass_state": "ssd_fwd_pass_state.hip",
-                 "compute_out": "ssd_compute_out.hip"}
+# the kernel sources of each stage (the state pass runs as one kernel or as
+# chunk_state + state_passing, chosen by shape)
+STAGE_SOURCES = {"chunk_cumsum": ["ssd_chunk_cumsum.hip"],
+                 "fwd_pass_state": ["ssd_fwd_pass_state.hip", "ssd_state_two_level.hip"],
+                 "compute_out": ["ssd_compute_out.hip"]}
 
 
 def algorithmic(w, y_bytes: int):
@@ -72,10 +74,11 @@ def algorithmic(w, y_bytes: int):
 
 
 def source_sha(stage: str) -> str:
-    path = os.path.join(ROOT, "mamba_ssd_chunked_fwd_amd", "csrc",
-                        STAGE_SOURCES[stage])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in STAGE_SOURCES[stage]:
+        with open(os.path.join(ROOT, "mamba_ssd_chunked_fwd_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, stage: str):
