@@ -94,25 +94,27 @@ def measured_traffic(workload: str, stage: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp):
+def cpu_baseline(w, inp, min_seconds: float = 10.0):
+    """The fp64 oracle on the host cores, over the full workload, repeated
+    until about `min_seconds` of CPU work (at least 3 runs)."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
     if threads <= 0:
         threads = len(os.sched_getaffinity(0))
     times = []
-    for _ in range(3):
+    while len(times) < 3 or (sum(times) < min_seconds and len(times) < 1000):
         t0 = time.perf_counter()
         oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
                        inp["D"], inp["init_state"], chunk_size=w.chunk_size,
                        nthreads=threads)
         times.append(time.perf_counter() - t0)
-    med = statistics.median(times)
-    return {"value": w.tokens / med, "unit": "tokens/s", "cores": threads,
+    total = sum(times)
+    return {"value": w.tokens * len(times) / total, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"the full {w.name} workload ({w.batch * w.nheads} "
                        f"(batch, head) pairs x {w.seqlen} tokens), fp64 "
-                       f"token recurrence, OpenMP over pairs; median of 3 "
-                       f"runs of {', '.join('%.2f' % t for t in times)} s")}
+                       f"token recurrence, OpenMP over pairs; {len(times)} runs, "
+                       f"{total:.1f} s in total (median run {statistics.median(times):.3f} s)")}
 
 
 def gdn_bench(ssd, c, make, dev, stream, nrep):
