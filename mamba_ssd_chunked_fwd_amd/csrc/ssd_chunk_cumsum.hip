@@ -10,53 +10,74 @@
 // one contiguous run (the pages transpose both decay_cumsum and dt to
 // [batch, head, token] among their optimizations).
 //
-// One workgroup per (chunk, 16-head tile, batch).  The [T x 16] dt tile is
-// read with coalesced row loads into LDS (the transpose), then each wave
-// scans one head at a time: every lane owns T/64 consecutive tokens, does a
-// serial inclusive scan over them, and a wavefront inclusive scan of the lane
-// totals (shuffles) supplies each lane's offset.  Output rows are written
-// contiguously.  The stage moves 12 bytes per (token, head) and is
-// HBM-bound.
+// One wavefront per (chunk, 4 consecutive heads, batch), four per workgroup.
+// Lane l owns tokens T/64 * l .. + T/64 - 1 of the chunk and loads each
+// token's 4 head values at once (one 16-byte load when H % 4 == 0, else
+// four 4-byte loads); all of a lane's loads are in flight together.  Each
+// head is then scanned as before: a serial inclusive scan over the lane's
+// tokens, and a wavefront inclusive scan of the lane totals (shuffles)
+// supplies the lane's offset.  No LDS and no barrier: the 4 heads' scans
+// run side by side in registers.  Output rows are written contiguously
+// (16 bytes per lane where the rows allow it).  The stage moves 12 bytes per
+// (token, head) and is HBM-bound.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 namespace {
 
-constexpr int kHeadTile = 16;
+constexpr int kHeadsPerWave = 4;
+constexpr int kWavesPerBlock = 4;
 
-template <int T>
+template <int T, bool VEC>
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ g, float* __restrict__ dt_t, int L, int H, int nc,
-    int nht) {
+    int nhq, int nwaves) {
   constexpr int kPer = T / kWave;  // tokens per lane
-  __shared__ float tile[T][kHeadTile + 1];
-
-  // Flat block id: chunk fastest, then head tile, then batch.
-  const int c = blockIdx.x % nc;
-  const int h0 = (blockIdx.x / nc) % nht * kHeadTile;
-  const int b = blockIdx.x / (nc * nht);
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  // Flat wave id: head quad fastest (the quads of one token row share its
+  // cache lines), then chunk, then batch.
+  const int wid = blockIdx.x * kWavesPerBlock + wave;
+  if (wid >= nwaves) return;   // the last workgroup's spare waves
+  const int hq = wid % nhq;
+  const int c = (wid / nhq) % nc;
+  const int b = wid / (nc * nhq);
+  const int h0 = hq * kHeadsPerWave;
   const int t0 = c * T;
   const int nt = min(T, L - t0);
-  const int nh = min(kHeadTile, H - h0);
+  const int nh = min(kHeadsPerWave, H - h0);
 
-  const float* src = dt + ((size_t)b * L + t0) * H + h0;
-  for (int e = threadIdx.x; e < T * kHeadTile; e += blockDim.x) {
-    const int t = e / kHeadTile, hh = e % kHeadTile;
-    tile[t][hh] = (t < nt && hh < nh) ? src[(size_t)t * H + hh] : 0.0f;
+  // d[k][j]: dt of token lane*kPer + k, head h0 + j (0 past the end)
+  const rsrc_t dr = make_rsrc(dt + (size_t)b * L * H, (uint32_t)L * H * 4u);
+  float d[kPer][kHeadsPerWave];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const uint32_t row = (uint32_t)(t0 + lane * kPer + k) * H + h0;
+    if constexpr (VEC) {
+      const f32x4 q = load_f32x4(dr, row * 4u);
+#pragma unroll
+      for (int j = 0; j < kHeadsPerWave; ++j) d[k][j] = q[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < kHeadsPerWave; ++j)
+        d[k][j] = load_f32(dr, j < nh ? (row + j) * 4u : 0x7FFFFFF0u);
+    }
   }
-  __syncthreads();
 
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  for (int hh = wave; hh < nh; hh += blockDim.x / kWave) {
-    const float a = A[h0 + hh];
-    float v[kPer], d[kPer];
+  // Rows start 16-byte aligned when L % 4 == 0 (8-byte when L is even), so
+  // a lane whose tokens are all real stores them as one vector.
+  const bool full = lane * kPer + kPer <= nt;
+  const bool vst = kPer > 1 && L % kPer == 0 && full;
+#pragma unroll
+  for (int j = 0; j < kHeadsPerWave; ++j) {
+    if (j >= nh) break;
+    const float a = A[h0 + j];
+    float v[kPer];
     float run = 0.0f;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
-      d[k] = tile[lane * kPer + k][hh];
-      run += a * d[k];
+      run += a * d[k][j];
       v[k] = run;
     }
     // Inclusive scan of the lane totals across the wavefront.
@@ -68,13 +89,23 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
     }
     float excl = __shfl_up(incl, 1, kWave);
     if (lane == 0) excl = 0.0f;
-    const size_t row = ((size_t)b * H + h0 + hh) * L + t0;
+    const size_t row = ((size_t)b * H + h0 + j) * L + t0 + lane * kPer;
+    if (vst) {
+      if constexpr (kPer == 4) {
+        *(f32x4*)(g + row) = (f32x4){(excl + v[0]) * kLog2e, (excl + v[1]) * kLog2e,
+                                     (excl + v[2]) * kLog2e, (excl + v[3]) * kLog2e};
+        *(f32x4*)(dt_t + row) = (f32x4){d[0][j], d[1][j], d[2][j], d[3][j]};
+      } else if constexpr (kPer == 2) {
+        *(f32x2*)(g + row) = (f32x2){(excl + v[0]) * kLog2e, (excl + v[1]) * kLog2e};
+        *(f32x2*)(dt_t + row) = (f32x2){d[0][j], d[1][j]};
+      }
+    } else {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int t = lane * kPer + k;
-      if (t < nt) {
-        g[row + t] = (excl + v[k]) * kLog2e;
-        dt_t[row + t] = d[k];
+      for (int k = 0; k < kPer; ++k) {
+        if (lane * kPer + k < nt) {
+          g[row + k] = (excl + v[k]) * kLog2e;
+          dt_t[row + k] = d[k][j];
+        }
       }
     }
   }
@@ -85,24 +116,28 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
 int launch_chunk_cumsum(const float* dt, const float* A, float* g,
                         float* dt_t, const Shape& s, void* stream) {
   const int nc = (int)s.nchunks();
-  const int nht = (int)((s.nheads + kHeadTile - 1) / kHeadTile);
-  const dim3 grid((unsigned)(s.batch * nc * nht));
-  const dim3 block(256);
+  const int nhq = (int)((s.nheads + kHeadsPerWave - 1) / kHeadsPerWave);
+  const int64_t nwaves = s.batch * nc * nhq;
+  const dim3 grid((unsigned)((nwaves + kWavesPerBlock - 1) / kWavesPerBlock));
+  const dim3 block(kWave * kWavesPerBlock);
   hipStream_t st = (hipStream_t)stream;
   const int L = (int)s.seqlen, H = (int)s.nheads;
+  const bool vec = H % 4 == 0;
+#define SSD_CUMSUM_LAUNCH(TT)                                                              \
+  if (vec)                                                                                 \
+    hipLaunchKernelGGL((chunk_cumsum_kernel<TT, true>), grid, block, 0, st, dt, A, g, dt_t, \
+                       L, H, nc, nhq, (int)nwaves);                                        \
+  else                                                                                     \
+    hipLaunchKernelGGL((chunk_cumsum_kernel<TT, false>), grid, block, 0, st, dt, A, g,      \
+                       dt_t, L, H, nc, nhq, (int)nwaves);
   switch (s.chunk) {
-    case 64:
-      hipLaunchKernelGGL(chunk_cumsum_kernel<64>, grid, block, 0, st, dt, A, g, dt_t, L, H, nc, nht);
-      break;
-    case 128:
-      hipLaunchKernelGGL(chunk_cumsum_kernel<128>, grid, block, 0, st, dt, A, g, dt_t, L, H, nc, nht);
-      break;
-    case 256:
-      hipLaunchKernelGGL(chunk_cumsum_kernel<256>, grid, block, 0, st, dt, A, g, dt_t, L, H, nc, nht);
-      break;
+    case 64: SSD_CUMSUM_LAUNCH(64) break;
+    case 128: SSD_CUMSUM_LAUNCH(128) break;
+    case 256: SSD_CUMSUM_LAUNCH(256) break;
     default:
       return (int)hipErrorInvalidValue;
   }
+#undef SSD_CUMSUM_LAUNCH
   return (int)hipGetLastError();
 }
 
