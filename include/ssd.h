@@ -134,8 +134,8 @@ ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt_t,
  * ssd_chunk_state: every P_c at once, written into the slot of the state it
  * feeds: states[b,h,c+1] = P_c for c < nc-1, and final_state = P_{nc-1}
  * (skipped when final_state is NULL).  states[b,h,0] is not touched.
- *   x, B, dt_t, g, states, final_state as for ssd_fwd_pass_state.
- *   Supported: in_dtype bf16 (fp32 returns SSD_ERR_UNSUPPORTED).
+ *   x, B, dt_t, g, states, final_state as for ssd_fwd_pass_state; in_dtype
+ *   bf16 or fp32.
  *
  * ssd_state_passing: in place, element by element over the state:
  *   states[b,h,0] = init (zeros if init_state is NULL);

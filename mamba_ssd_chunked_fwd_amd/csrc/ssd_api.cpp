@@ -136,8 +136,8 @@ ssd_status ssd_chunk_state(const void* x, const void* B, const float* dt_t, cons
   if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(dt_t) || !ok_ptr(g) || !ok_ptr(states) ||
       !ok_opt(final_state))
     return SSD_ERR_INVALID_ARGUMENT;
-  if (in_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
-  return from_hip(ssd::launch_chunk_state(x, B, dt_t, g, states, final_state, s, stream));
+  return from_hip(ssd::launch_chunk_state(x, B, dt_t, g, states, final_state,
+                                          in_dtype == SSD_BF16, s, stream));
 }
 
 ssd_status ssd_state_passing(const float* g, const float* init_state, float* states,

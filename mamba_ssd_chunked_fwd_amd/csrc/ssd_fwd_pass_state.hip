@@ -694,7 +694,7 @@ int launch_fwd_pass_state(const void* x, const void* B, const float* dt_t,
                           const Shape& s, void* stream) {
   hipStream_t st = (hipStream_t)stream;
   if (bf16_in && use_two_level(s, device_cus())) {
-    const int r = launch_chunk_state(x, B, dt_t, g, states, final_state, s, stream);
+    const int r = launch_chunk_state(x, B, dt_t, g, states, final_state, true, s, stream);
     if (r != 0) return r;
     return launch_state_passing(g, init_state, states, final_state, s, stream);
   }

@@ -30,7 +30,7 @@ int launch_compute_out(const void* x, const void* B, const void* C,
 // contribution into the slot of the state it feeds; state_passing turns the
 // slots into the states in place).
 int launch_chunk_state(const void* x, const void* B, const float* dt_t, const float* g,
-                       float* states, float* fin, const Shape& s, void* stream);
+                       float* states, float* fin, bool bf16_in, const Shape& s, void* stream);
 int launch_state_passing(const float* g, const float* init, float* states, float* fin,
                          const Shape& s, void* stream);
 

@@ -173,6 +173,74 @@ __global__ __launch_bounds__(256 * HB) void chunk_state_bf16(
   }
 }
 
+// fp32 inputs: one workgroup (4 waves) per (b, chunk, head), wave w owning
+// rows 16w..16w+15 and all N columns as in the bf16 kernel.  The fp32 matrix
+// instruction takes one k value per lane, so both operands are loaded
+// straight from memory into their lanes (no staging): lane (lr, lq) of a
+// 4-token step holds B[t][16j + lr] and (w o x)[t][16w + lr] for token
+// t = t0 + lq.  Four steps (16 tokens) of loads are issued before their
+// products.
+template <int T, int N>
+__global__ __launch_bounds__(256) void chunk_state_f32(
+    const float* __restrict__ x, const float* __restrict__ Bm,
+    const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
+    float* __restrict__ final_state, int L, int H, int G, int nc) {
+  constexpr int NB = N / 16;
+  const int item = blockIdx.x;
+  const int h = item % H;
+  const int c = (item / H) % nc;
+  const int b = item / (H * nc);
+  const int grp = h / (H / G);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+
+  const uint32_t xrow = (uint32_t)(H * kHeadDim), brow = (uint32_t)(G * N);
+  const rsrc_t xr = make_rsrc(x + ((size_t)b * L * H + h) * kHeadDim,
+                              ((uint32_t)(L - 1) * xrow + kHeadDim) * 4u);
+  const rsrc_t br = make_rsrc(Bm + ((size_t)b * L * G + grp) * N,
+                              ((uint32_t)(L - 1) * brow + N) * 4u);
+  const size_t grow = ((size_t)b * H + h) * L;
+  const rsrc_t gr = make_rsrc(g + grow, (uint32_t)L * 4u);
+  const rsrc_t dr = make_rsrc(dt_t + grow, (uint32_t)L * 4u);
+  const int tlast = min(c * T + T, L) - 1;
+  const float gl = g[grow + tlast];
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = (f32x4){0, 0, 0, 0};
+#pragma unroll 1
+  for (int s0 = 0; s0 < T; s0 += 16) {
+    float wx[4], bv[4][NB];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t t = (uint32_t)(c * T + s0 + 4 * u + lq);
+      // tokens past the end read dt = g = 0 and x = B = 0, so w o x = 0
+      const uint32_t go = t < (uint32_t)L ? t * 4u : kPastRange;
+      const float gv = load_f32(gr, go), dv = load_f32(dr, go);
+      const float xv = load_f32(xr, (t * xrow + 16 * wave + lr) * 4u);
+      wx[u] = dv * exp2_hw(gl - gv) * xv;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) bv[u][j] = load_f32(br, (t * brow + 16 * j + lr) * 4u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[j] = mfma_f32(bv[u][j], wx[u], acc[j]);
+  }
+
+  float* dst = nullptr;
+  if (c + 1 < nc) {
+    dst = states + (((size_t)b * H + h) * nc + c + 1) * kHeadDim * N;
+  } else if (final_state) {
+    dst = final_state + ((size_t)b * H + h) * kHeadDim * N;
+  }
+  if (dst) {
+    const int p = 16 * wave + lr;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) *(f32x4*)(dst + (size_t)p * N + 16 * j + 4 * lq) = acc[j];
+  }
+}
+
 // ---------------------------------------------------------------- passing
 template <int N, int D>
 __global__ __launch_bounds__(256) void state_passing_kernel(
@@ -253,6 +321,17 @@ int launch_cs(const void* x, const void* B, const float* dt_t, const float* g, f
   return launch_cs_hb<T, N, 1>(x, B, dt_t, g, states, fin, s, st);
 }
 
+template <int T, int N>
+int launch_cs_f32(const void* x, const void* B, const float* dt_t, const float* g,
+                  float* states, float* fin, const Shape& s, hipStream_t st) {
+  const int nc = (int)s.nchunks();
+  const unsigned blocks = (unsigned)(s.batch * nc * s.nheads);
+  hipLaunchKernelGGL((chunk_state_f32<T, N>), dim3(blocks), dim3(256), 0, st, (const float*)x,
+                     (const float*)B, dt_t, g, states, fin, (int)s.seqlen, (int)s.nheads,
+                     (int)s.ngroups, nc);
+  return (int)hipGetLastError();
+}
+
 template <int N>
 int launch_sp(const float* g, const float* init, float* states, float* fin, const Shape& s,
               hipStream_t st) {
@@ -266,8 +345,22 @@ int launch_sp(const float* g, const float* init, float* states, float* fin, cons
 }  // namespace
 
 int launch_chunk_state(const void* x, const void* B, const float* dt_t, const float* g,
-                       float* states, float* fin, const Shape& s, void* stream) {
+                       float* states, float* fin, bool bf16_in, const Shape& s, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  if (!bf16_in) {
+    if (s.dstate == 64) {
+      switch (s.chunk) {
+        case 64: return launch_cs_f32<64, 64>(x, B, dt_t, g, states, fin, s, st);
+        case 128: return launch_cs_f32<128, 64>(x, B, dt_t, g, states, fin, s, st);
+        default: return launch_cs_f32<256, 64>(x, B, dt_t, g, states, fin, s, st);
+      }
+    }
+    switch (s.chunk) {
+      case 64: return launch_cs_f32<64, 128>(x, B, dt_t, g, states, fin, s, st);
+      case 128: return launch_cs_f32<128, 128>(x, B, dt_t, g, states, fin, s, st);
+      default: return launch_cs_f32<256, 128>(x, B, dt_t, g, states, fin, s, st);
+    }
+  }
   if (s.dstate == 64) {
     switch (s.chunk) {
       case 64: return launch_cs<64, 64>(x, B, dt_t, g, states, fin, s, st);

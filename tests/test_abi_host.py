@@ -166,7 +166,6 @@ def test_two_level_entry_points_validate():
         assert cs(d, **{name: None}) == INV, name
         assert cs(d, **{name: MISALIGNED}) == INV, name
     assert cs(d, fin=MISALIGNED) == INV and cs(d, ind=9) == INV
-    assert cs(d, ind=ssd.SSD_F32) == UNS
     assert cs(dims(dstate=96)) == UNS and sp(dims(dstate=96)) == UNS
     for name in ("g", "st"):
         assert sp(d, **{name: None}) == INV, name

@@ -27,8 +27,8 @@ def ssd():
     return m
 
 
-def _wl(b, L, H, G, N, T, init):
-    return Workload("two_level", b, L, H, 64, N, G, T, "bf16", -2.0, 0.0, 1.5,
+def _wl(b, L, H, G, N, T, init, dtype="bf16"):
+    return Workload("two_level", b, L, H, 64, N, G, T, dtype, -2.0, 0.0, 1.5,
                     0.1 if init else None)
 
 
@@ -82,6 +82,31 @@ def test_two_level_matches_oracle(ssd, b, L, H, G, N, T, init):
                          inp["init_state"], chunk_size=T, want_y=False)
     assert_close(_np(states), ref["states"], "bf16", "states")
     assert_close(_np(fin), ref["final"], "bf16", "final")
+
+
+FP32_CASES = [
+    # b, L, H, G, N, T, init: fp32 inputs (chunk_state's fp32 kernel)
+    (2, 300, 4, 2, 128, 64, True),
+    (1, 700, 3, 1, 64, 256, False),
+    (2, 333, 2, 1, 128, 128, True),
+    (3, 37, 2, 1, 64, 64, False),
+]
+
+
+@pytest.mark.parametrize("b,L,H,G,N,T,init", FP32_CASES,
+                         ids=[f"fp32_b{c[0]}_L{c[1]}_H{c[2]}_G{c[3]}_N{c[4]}_T{c[5]}" + ("_init" if c[6] else "")
+                              for c in FP32_CASES])
+def test_two_level_fp32_matches_oracle(ssd, b, L, H, G, N, T, init):
+    w = _wl(b, L, H, G, N, T, init, "fp32")
+    inp = make_inputs(w, seed=190 + L)
+    log(f"[two-level fp32] {w}")
+    dev = device_inputs(inp, "fp32")
+    g, dtt = _cumsum(ssd, dev, w)
+    states, fin = _two_level(ssd, dev, w, g, dtt)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                         inp["init_state"], chunk_size=T, want_y=False)
+    assert_close(_np(states), ref["states"], "fp32", "states")
+    assert_close(_np(fin), ref["final"], "fp32", "final")
 
 
 def test_two_level_without_final(ssd):
