@@ -23,9 +23,13 @@
 //   registers.  C B^T and the C fragments depend only on (b, c, group), so
 //   they are formed once and reused for every head of the group in the run
 //   (the pages compute C B^T once per group as well).
-// * One workgroup covers the whole chunk.  Wave w owns query-row blocks
-//   (16 rows each) w and, for chunks of 128 and 256 tokens, NIB-1-w, so
-//   every wave has the same share of the causal triangle.  Y is computed
+// * One workgroup covers the whole chunk.  Wave w owns query-row block w
+//   (16 rows) and, for 256-token chunks (8 waves, 16 blocks), also block
+//   NIB-1-w, so every wave has the same share of the causal triangle.
+//   128-token chunks take 8 waves of one block each: the waves' shares of
+//   the triangle differ, but half the registers per wave allow twice the
+//   waves per CU, which measured faster (365 -> 325 us on the 65536-token
+//   sequence) than 4 balanced waves of two blocks.  Y is computed
 //   transposed (Y^T[p][i]) so each lane's accumulators are four consecutive
 //   p of one token: 16-byte stores of y.
 // * C B^T is computed transposed (B C^T, rows j, columns i), only for 16x16
@@ -65,7 +69,7 @@ __device__ __forceinline__ void store_y(void* y, size_t off, f32x4 v) {
 template <int T>
 struct Geo {
   static constexpr int NIB = T / 16;             // 16-token blocks per chunk
-  static constexpr int NW = T == 256 ? 8 : 4;    // waves per workgroup
+  static constexpr int NW = T >= 128 ? 8 : 4;    // waves per workgroup
   static constexpr int NTHR = 64 * NW;
   static constexpr int MB = NIB / NW;            // query-row blocks per wave
   static_assert(MB == 1 || MB == 2, "one or two row blocks per wave");
