@@ -37,8 +37,13 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
   constexpr int kPer = T / kWave;  // tokens per lane
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   // Flat wave id: head quad fastest (the quads of one token row share its
-  // cache lines), then chunk, then batch.
-  const int wid = blockIdx.x * kWavesPerBlock + wave;
+  // cache lines), then chunk, then batch.  Blocks are dealt to the 8 XCDs
+  // round-robin, so consecutive logical blocks are remapped onto one XCD:
+  // the quads of a row then meet in one L2 instead of fetching its lines
+  // from memory once per XCD.
+  int blk = blockIdx.x;
+  if (gridDim.x % 8 == 0) blk = (blk % 8) * (gridDim.x / 8) + blk / 8;
+  const int wid = blk * kWavesPerBlock + wave;
   if (wid >= nwaves) return;   // the last workgroup's spare waves
   const int hq = wid % nhq;
   const int c = (wid / nhq) % nc;
