@@ -22,9 +22,17 @@ def ssd():
     return m
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "wide_fp32"])
-def test_forward_replays_from_a_hip_graph(ssd, name):
-    w = small_variant(WORKLOADS[name], batch=2, seqlen=300)
+# (workload, batch, seqlen, heads): the last is a long chain on few heads,
+# for which the state pass runs as chunk_state + state_passing
+GRAPH_CASES = [("small_bf16", 2, 300, None), ("wide_fp32", 2, 300, None),
+               ("long_bf16", 1, 16384 + 77, 4)]
+
+
+@pytest.mark.parametrize("name,batch,seqlen,heads", GRAPH_CASES,
+                         ids=[c[0] + ("_two_level" if c[3] else "") for c in GRAPH_CASES])
+def test_forward_replays_from_a_hip_graph(ssd, name, batch, seqlen, heads):
+    w = small_variant(WORKLOADS[name], batch=batch, seqlen=seqlen,
+                      **({"nheads": heads} if heads else {}))
     log(f"[graph] {w}")
     dev = device_inputs(make_inputs(w, seed=77), w.dtype)
     d = ssd.make_dims(dev["x"], dev["B"], w.chunk_size)
