@@ -37,6 +37,12 @@ namespace {
 
 constexpr uint32_t kPastRange = 0x7FFFFFF0u;
 
+// Consecutive logical items on one XCD (blocks are dealt round-robin).
+__device__ __forceinline__ int xcd_item(int bid, int total) {
+  if (total % 8) return bid;
+  return (bid % 8) * (total / 8) + bid / 8;
+}
+
 template <int N>
 struct TlStride {
   static constexpr int value = N + 16;
@@ -62,9 +68,11 @@ __global__ __launch_bounds__(256 * HB) void chunk_state_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t bts[ST * BS];
 
   // blocks: (b, c, block of HB heads of one group) with the head block
-  // fastest; the HB heads share the staged B tile
+  // fastest; the HB heads share the staged B tile.  Consecutive items are
+  // remapped onto one XCD (blocks are dealt to the 8 XCDs round-robin), so
+  // the head blocks of a chunk read its B rows through one L2.
   const int nhb = H / HB;
-  const int item = blockIdx.x;
+  const int item = xcd_item(blockIdx.x, gridDim.x);
   const int h0 = (item % nhb) * HB;
   const int c = (item / nhb) % nc;
   const int b = item / (nhb * nc);
@@ -186,7 +194,7 @@ __global__ __launch_bounds__(256) void chunk_state_f32(
     const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
     float* __restrict__ final_state, int L, int H, int G, int nc) {
   constexpr int NB = N / 16;
-  const int item = blockIdx.x;
+  const int item = xcd_item(blockIdx.x, gridDim.x);   // as in the bf16 kernel
   const int h = item % H;
   const int c = (item / H) % nc;
   const int b = item / (H * nc);
