@@ -370,6 +370,25 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    # The practical streaming ceiling of this GPU in the same run: a 1 GiB
+    # device-to-device copy (read + write), timed from a graph of 5 copies.
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        for _ in range(5):
+            cdst.copy_(csrc)
+    cg.replay()
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ce[0].record(stream)
+    cg.replay()
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc.numel() * 4 * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
+    del cg, csrc, cdst
+
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = w.tokens / (wall / args.steps)
     peak_tf = BF16_MFMA_TFLOPS if w.dtype == "bf16" else FP32_MFMA_TFLOPS
@@ -380,6 +399,7 @@ def main() -> int:
         stages[n] = {"ms": round(ms, 5), "alg_bytes": by[n], "alg_flop": fl[n],
                      "GB_per_s": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "frac_of_copy": round(gbs / copy_gbs, 4),
                      "TFLOP_per_s": round(fl[n] / (ms * 1e-3) / 1e12, 2),
                      "mfma_frac_of_peak": round(fl[n] / (ms * 1e-3) / 1e12 / peak_tf, 4)}
     # the kernels one ssd_forward call launches
@@ -428,6 +448,7 @@ def main() -> int:
                           "hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "note": "the conv over the layer's x, B, C channels; not part of the step"},
         "gated_deltanet": gdn,
+        "copy_GB_per_s": round(copy_gbs, 1),
         "effective_TFLOP_per_s": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
     }
