@@ -75,20 +75,16 @@ struct Geo {
   static_assert(MB == 1 || MB == 2, "one or two row blocks per wave");
 };
 
-// bf16 geometry: 8 waves for 128- and 256-token chunks, 4 for 64.  The
-// code also allows more waves than row blocks (PS waves sharing a row block,
-// each taking PBW of its four 16-column blocks), but for 64-token chunks 8
-// waves in that form measured slower (47.2 against 43.5 us on the 4 x
-// 2048-token, 24-head layer) than 4 waves of one row block each.
+// bf16 geometry: 8 waves for 128- and 256-token chunks (one or two row
+// blocks per wave), 4 for 64-token chunks (one each).  (Measured on the
+// small layer: 8 waves that split a 64-token chunk's output columns in two
+// took 47.2 against 43.5 us.)
 template <int T>
 struct GeoB {
   static constexpr int NIB = T / 16;
   static constexpr int NW = T == 64 ? 4 : 8;
   static constexpr int NTHR = 64 * NW;
-  static constexpr int PS = NW > NIB ? NW / NIB : 1;  // column splits of a row block
-  static constexpr int RW = NW / PS;                  // waves per column split
-  static constexpr int MB = NIB / RW;                 // row blocks per wave
-  static constexpr int PBW = 4 / PS;                  // 16-column blocks per wave
+  static constexpr int MB = NIB / NW;                 // row blocks per wave
   static_assert(MB == 1 || MB == 2, "one or two row blocks per wave");
 };
 
@@ -138,7 +134,7 @@ __global__ __launch_bounds__(GeoB<T>::NTHR) void compute_out_bf16(
     const float* __restrict__ Dv, void* __restrict__ y, int L, int H, int G,
     int nc, int items) {
   using Gm = GeoB<T>;
-  constexpr int NTHR = Gm::NTHR, MB = Gm::MB, NIB = Gm::NIB, RW = Gm::RW, PBW = Gm::PBW;
+  constexpr int NTHR = Gm::NTHR, MB = Gm::MB, NIB = Gm::NIB;
   constexpr int KN = N / 32;            // k-steps over the state index
   constexpr int XS = 80;                // X tile row stride (bf16), 64 + 16
   constexpr int SS = N + 8;             // state-half row stride (bf16)
@@ -160,8 +156,6 @@ __global__ __launch_bounds__(GeoB<T>::NTHR) void compute_out_bf16(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
-  // this wave's row-block slot and its 16-column blocks pb0 .. pb0+PBW-1
-  const int rw = wave % RW, pb0 = (wave / RW) * PBW;
   const int hpg = H / G;
   const uint32_t xbytes = (uint32_t)L * H * kHeadDim * 2;
   const uint32_t bcbytes = (uint32_t)L * G * N * 2;
@@ -246,14 +240,14 @@ __global__ __launch_bounds__(GeoB<T>::NTHR) void compute_out_bf16(
     const rsrc_t br = make_rsrc(Bm + (size_t)it.b * L * G * N, bcbytes);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      const int i = 16 * row_block_b<T>(rw, m) + lr;
+      const int i = 16 * row_block_b<T>(wave, m) + lr;
       const uint32_t off = ((uint32_t)(it.c * T + i) * G + it.grp) * (N * 2) + 16 * lq;
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) cf[m][kk] = load_b128(cr, off + 64 * kk);
     }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      const int ib = row_block_b<T>(rw, m);
+      const int ib = row_block_b<T>(wave, m);
 #pragma unroll
       for (int k = 0; k < NIB; ++k) {
         if (k <= ib) {
@@ -296,31 +290,31 @@ __global__ __launch_bounds__(GeoB<T>::NTHR) void compute_out_bf16(
     const int t0 = it.c * T;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      const int ib = row_block_b<T>(rw, m);
+      const int ib = row_block_b<T>(wave, m);
       const int i = 16 * ib + lr;
       // Y^T = S C^T (state split hi + lo), then column i scaled by 2^{g_i}
-      f32x4 yacc[PBW];
+      f32x4 yacc[4];
 #pragma unroll
-      for (int q = 0; q < PBW; ++q) yacc[q] = (f32x4){0, 0, 0, 0};
+      for (int pb = 0; pb < 4; ++pb) yacc[pb] = (f32x4){0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < KN; ++kk) {
 #pragma unroll
-        for (int q = 0; q < PBW; ++q) {
+        for (int pb = 0; pb < 4; ++pb) {
           // the next item's loads, one per pair of matrix instructions
-          if (m == 0 && PBW * kk + q < NLOAD) issue_slot(PBW * kk + q, nxt);
-          const int off = (16 * (pb0 + q) + lr) * SS + 32 * kk + 8 * lq;
-          yacc[q] = mfma_bf16(*(const u32x4*)(sh + off), cf[m][kk], yacc[q]);
-          yacc[q] = mfma_bf16(*(const u32x4*)(sl + off), cf[m][kk], yacc[q]);
+          if (m == 0 && 4 * kk + pb < NLOAD) issue_slot(4 * kk + pb, nxt);
+          const int off = (16 * pb + lr) * SS + 32 * kk + 8 * lq;
+          yacc[pb] = mfma_bf16(*(const u32x4*)(sh + off), cf[m][kk], yacc[pb]);
+          yacc[pb] = mfma_bf16(*(const u32x4*)(sl + off), cf[m][kk], yacc[pb]);
         }
       }
       if (m == 0) {
 #pragma unroll
-        for (int j = PBW * KN; j < NLOAD; ++j) issue_slot(j, nxt);
+        for (int j = 4 * KN; j < NLOAD; ++j) issue_slot(j, nxt);
       }
       const float gi = gs[i];
       const float ei = exp2_hw(gi);
 #pragma unroll
-      for (int q = 0; q < PBW; ++q) yacc[q] *= ei;
+      for (int pb = 0; pb < 4; ++pb) yacc[pb] *= ei;
 
       // Y^T += X^T L'^T over 32-token k-steps s: slots 0..3 carry tokens
       // 32s + 4lq + rr and slots 4..7 tokens 32s + 16 + 4lq + rr.
@@ -370,19 +364,19 @@ __global__ __launch_bounds__(GeoB<T>::NTHR) void compute_out_bf16(
           const u32x4 lh = make_u32x4(lh4), ll = make_u32x4(ll4);
           const uint16_t* xp = xs + (32 * s + 4 * lq + (lr >> 2)) * XS + 4 * (lr & 3);
 #pragma unroll
-          for (int q = 0; q < PBW; ++q) {
-            const u32x2 a0 = lds_read_tr16(xp + 16 * (pb0 + q));
-            const u32x2 a1 = lds_read_tr16(xp + 16 * XS + 16 * (pb0 + q));
+          for (int pb = 0; pb < 4; ++pb) {
+            const u32x2 a0 = lds_read_tr16(xp + 16 * pb);
+            const u32x2 a1 = lds_read_tr16(xp + 16 * XS + 16 * pb);
             const u32x4 xa = (u32x4){a0[0], a0[1], a1[0], a1[1]};
-            yacc[q] = mfma_bf16(xa, lh, yacc[q]);
-            yacc[q] = mfma_bf16(xa, ll, yacc[q]);
+            yacc[pb] = mfma_bf16(xa, lh, yacc[pb]);
+            yacc[pb] = mfma_bf16(xa, ll, yacc[pb]);
           }
         }
       }
       if (t0 + i < L) {
         const size_t off = (((size_t)it.b * L + t0 + i) * H + it.h) * kHeadDim + 4 * lq;
 #pragma unroll
-        for (int q = 0; q < PBW; ++q) store_y<YBF16>(y, off + 16 * (pb0 + q), yacc[q]);
+        for (int pb = 0; pb < 4; ++pb) store_y<YBF16>(y, off + 16 * pb, yacc[pb]);
       }
     }
   }
