@@ -127,9 +127,10 @@ ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt_t,
  * Matmul"]: the jump S_{c+1} = 2^{g_last(c)} S_c + P_c, with P_c =
  * X_c^T (w o B_c) the contribution of chunk c from a zero state, split into
  * a fully parallel part and a short sequential one.  The two calls below,
- * in this order, produce exactly what ssd_fwd_pass_state produces (same
- * states and final_state); ssd_fwd_pass_state itself uses them where they
- * are faster than its one-pass kernel.
+ * in this order, compute the states and final_state ssd_fwd_pass_state
+ * computes (equal up to the order of fp32 roundings); with bf16 inputs
+ * ssd_fwd_pass_state itself takes this form for long chains on few heads,
+ * where it is faster than the one-pass kernel.
  *
  * ssd_chunk_state: every P_c at once, written into the slot of the state it
  * feeds: states[b,h,c+1] = P_c for c < nc-1, and final_state = P_{nc-1}
