@@ -138,6 +138,9 @@ def _check(t: Optional[torch.Tensor], name: str, shape, dtypes,
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.data_ptr() % 16:
+        raise ValueError(f"{name} must start on a 16-byte boundary (a slice of a "
+                         f"larger tensor may not; pass a copy)")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if shape is not None and tuple(t.shape) != tuple(shape):

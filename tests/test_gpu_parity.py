@@ -319,6 +319,10 @@ def test_binding_rejects_bad_arguments(ssd):
     with pytest.raises(TypeError):      # B dtype differs from x
         ssd.forward(dev["x"], dev["dt"], dev["A"], dev["B"].float(), dev["C"],
                     dev["D"], chunk_size=64)
+    dt_off = torch.empty(dev["dt"].numel() + 1, device=DEV)[1:].view(dev["dt"].shape)
+    dt_off.copy_(dev["dt"])
+    with pytest.raises(ValueError):     # contiguous, but 4 bytes past a 16-byte boundary
+        ssd.forward(dev["x"], dt_off, dev["A"], dev["B"], dev["C"], dev["D"], chunk_size=64)
     with pytest.raises(ssd.SsdError) as e:   # chunk size not built
         ssd.forward(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"],
                     dev["D"], chunk_size=32)
