@@ -28,6 +28,8 @@
 // are loaded into registers while the current one is processed, then staged
 // into the other half of a double-buffered LDS tile set (one barrier per
 // chunk).
+#include <atomic>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -309,10 +311,15 @@ int launch_h_kv(const void* k, const void* w, const void* u, const float* g, con
 }
 
 // ------------------------------------------------------------ chunk_fwd_o
-// One workgroup per (b, chunk, head, 64-column block of V); wave w owns the
-// 16 tokens t of block w and computes o^T[v][t] for the block's columns, so
-// each lane's accumulators are four consecutive v of one token (16-byte
-// stores).  Per wave:
+// Work items are (b, chunk, head, 64-column block of V), the column block
+// fastest.  A persistent workgroup takes one contiguous run of items and
+// prefetches: while item i is computed from LDS and registers, item i+1's
+// state block, v_new block, g and (when its (b, chunk, head) differs from
+// item i's) its k tile and q rows are already loading into registers.  The
+// column blocks of one (b, chunk, head) share k and q, so the second block
+// loads neither.  Wave w owns the 16 tokens t of block w and computes
+// o^T[v][t] for the item's columns, so each lane's accumulators are four
+// consecutive v of one token (16-byte stores).  Per wave:
 //   (i)   D = k q^T over K for the key blocks j <= t (rows j, columns t); with
 //         the decay e^{g_t - g_j} and the causal select (j <= t, applied
 //         after the exponent is formed) it is A^T, and a lane holds exactly
@@ -321,16 +328,17 @@ int launch_h_kv(const void* k, const void* w, const void* u, const float* g, con
 //   (ii)  o^T = h^T q^T (the state from LDS as bf16 hi + lo, read with the
 //         transpose read), scaled per token by e^{g_t};
 //   (iii) o^T += v_new^T A^T (v_new from LDS with the transpose read).
-// q stays in registers (each wave reads only its own 16 rows); k, v_new
-// and the state are staged once per workgroup in LDS.  The LDS footprint
-// lets two workgroups share a CU, so one loads while the other computes.
+// q stays in registers (each wave reads only its own 16 rows); k, v_new and
+// the state are staged in LDS.  The LDS footprint lets two workgroups share
+// a CU.
 template <int K, int V, bool OBF16>
 __global__ __launch_bounds__(256) void gdn_fwd_o_kernel(
     const uint16_t* __restrict__ qin, const uint16_t* __restrict__ kin,
     const uint16_t* __restrict__ vnin, const float* __restrict__ hin,
-    const float* __restrict__ g, void* __restrict__ out, float scale, int L, int H, int nt) {
+    const float* __restrict__ g, void* __restrict__ out, float scale, int L, int H, int nt,
+    int items) {
   constexpr int C = kGdnC;
-  constexpr int VB = 64;                       // columns of V per workgroup
+  constexpr int VB = 64;                       // columns of V per item
   constexpr int NVB = VB / 16;
   constexpr int NKK = K / 32;
   constexpr int HS = VB + 16;                  // state tile row stride (bf16)
@@ -350,167 +358,239 @@ __global__ __launch_bounds__(256) void gdn_fwd_o_kernel(
   __shared__ __attribute__((aligned(16))) float gs[C];
 
   constexpr int NVH = V / VB;
-  const int logical = gdn_xcd_remap(blockIdx.x, gridDim.x);
-  const int vh = logical % NVH;
-  const int item = logical / NVH;
-  const int h = item % H;
-  const int c = (item / H) % nt;
-  const int b = item / (H * nt);
+  // this workgroup's run [i0, i1); consecutive runs on one XCD
+  int i0, i1;
+  {
+    const int nwg = gridDim.x;
+    const int wg = gdn_xcd_remap(blockIdx.x, nwg);
+    i0 = (int)((int64_t)wg * items / nwg);
+    i1 = (int)((int64_t)(wg + 1) * items / nwg);
+  }
+  if (i0 >= i1) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
-  const uint32_t t0 = (uint32_t)(c * C);
-
   const uint32_t krow = (uint32_t)(H * K), vrow = (uint32_t)(H * V);
-  const rsrc_t qr = make_rsrc(qin + ((size_t)b * L * H + h) * K, ((uint32_t)(L - 1) * krow + K) * 2u);
-  const rsrc_t kr = make_rsrc(kin + ((size_t)b * L * H + h) * K, ((uint32_t)(L - 1) * krow + K) * 2u);
-  const rsrc_t vr = make_rsrc(vnin + ((size_t)b * L * H + h) * V, ((uint32_t)(L - 1) * vrow + V) * 2u);
-  const rsrc_t gr = make_rsrc(g + (size_t)b * L * H + h, ((uint32_t)(L - 1) * H + 1) * 4u);
-  const float* hsrc = hin + (((size_t)b * H + h) * nt + c) * K * V + vh * VB;
 
-  // All loads of the item first.
-  f32x4 hreg[HU];
-  u32x4 kreg[KU], vreg[VU];
-#pragma unroll
-  for (int i = 0; i < HU; ++i) {
-    const int u = tid + 256 * i, row = u / (VB / 4), c4 = u % (VB / 4);
-    hreg[i] = *(const f32x4*)(hsrc + (size_t)row * V + 4 * c4);
-  }
-#pragma unroll
-  for (int i = 0; i < KU; ++i) {
-    const int u = tid + 256 * i, t = u / (K / 8), c8 = u % (K / 8);
-    kreg[i] = load_b128(kr, ((t0 + t) * krow + 8 * c8) * 2u);
-  }
-#pragma unroll
-  for (int i = 0; i < VU; ++i) {
-    const int u = tid + 256 * i, t = u / (VB / 8), c8 = u % (VB / 8);
-    vreg[i] = load_b128(vr, ((t0 + t) * vrow + vh * VB + 8 * c8) * 2u);
-  }
-  const float gv = load_f32(gr, (tid < C && t0 + tid < (uint32_t)L) ? (t0 + tid) * (uint32_t)H * 4u
-                                                                    : kPastRange);
-  // q: this wave's 16 tokens, in the k-slot map (K = 32kk + 4lq + 0..3 and
-  // 32kk + 16 + 4lq + 0..3), straight into operand registers.
-  const uint32_t tq = t0 + 16 * wave + lr;
-  u32x4 qf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const u32x2 a = load_b64(qr, (tq * krow + 32 * kk + 4 * lq) * 2u);
-    const u32x2 bq = load_b64(qr, (tq * krow + 32 * kk + 16 + 4 * lq) * 2u);
-    qf[kk] = (u32x4){a[0], a[1], bq[0], bq[1]};
-  }
+  struct Item {
+    int b, c, h, vh;
+  };
+  auto decode = [&](int i) {
+    Item it;
+    it.vh = i % NVH;
+    const int r = i / NVH;
+    it.h = r % H;
+    it.c = (r / H) % nt;
+    it.b = r / (H * nt);
+    return it;
+  };
+  // An item loads k and q unless the item before it in the run has the same
+  // (b, chunk, head).
+  auto loads_kq = [&](int i) { return i == i0 || i % NVH == 0; };
 
-  // Stage: the state split into bf16 hi + lo, k and v_new as loaded, g.
+  // One item's raw data.  A dead item (past the run) gets empty buffer
+  // ranges: its loads return zero without touching memory.
+  struct Ld {
+    f32x4 h[HU];
+    u32x4 k[KU], v[VU], q[NKK];
+    float g;
+  };
+  auto issue = [&](int i, bool live, bool kq, Ld& d) {
+    const Item it = decode(i);
+    const uint32_t t0 = (uint32_t)(it.c * C);
+    const rsrc_t hr = make_rsrc(hin + (((size_t)it.b * H + it.h) * nt + it.c) * K * V + it.vh * VB,
+                                live ? ((uint32_t)(K - 1) * V + VB) * 4u : 0u);
 #pragma unroll
-  for (int i = 0; i < HU; ++i) {
-    const int u = tid + 256 * i, row = u / (VB / 4), c4 = u % (VB / 4);
-    uint32_t hh0, hl0, hh1, hl1;
-    split_bf16(hreg[i][0], hreg[i][1], hh0, hl0);
-    split_bf16(hreg[i][2], hreg[i][3], hh1, hl1);
-    *(u32x2*)(hhi + row * HS + 4 * c4) = (u32x2){hh0, hh1};
-    *(u32x2*)(hlo + row * HS + 4 * c4) = (u32x2){hl0, hl1};
-  }
-#pragma unroll
-  for (int i = 0; i < KU; ++i) {
-    const int u = tid + 256 * i, t = u / (K / 8), c8 = u % (K / 8);
-    *(u32x4*)(ks + t * KS + 8 * c8) = kreg[i];
-  }
-#pragma unroll
-  for (int i = 0; i < VU; ++i) {
-    const int u = tid + 256 * i, t = u / (VB / 8), c8 = u % (VB / 8);
-    *(u32x4*)(vs + t * VS + 8 * c8) = vreg[i];
-  }
-  if (tid < C) gs[tid] = gv;
-  __syncthreads();
-
-  const int tl = 16 * wave + lr;               // this lane's token in the chunk
-  const float gt = gs[tl];
-
-  // (ii) inter term: o^T = h^T q^T, then e^{g_t} per token.
-  f32x4 oa[NVB];
-#pragma unroll
-  for (int vb = 0; vb < NVB; ++vb) {
-    oa[vb] = (f32x4){0, 0, 0, 0};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int o0 = (32 * kk + 4 * lq + (lr >> 2)) * HS + 16 * vb + 4 * (lr & 3);
-      const u32x2 a0 = lds_read_tr16(hhi + o0), a1 = lds_read_tr16(hhi + o0 + 16 * HS);
-      const u32x2 c0 = lds_read_tr16(hlo + o0), c1 = lds_read_tr16(hlo + o0 + 16 * HS);
-      oa[vb] = mfma_bf16((u32x4){a0[0], a0[1], a1[0], a1[1]}, qf[kk], oa[vb]);
-      oa[vb] = mfma_bf16((u32x4){c0[0], c0[1], c1[0], c1[1]}, qf[kk], oa[vb]);
+    for (int j = 0; j < HU; ++j) {
+      const int u = tid + 256 * j, row = u / (VB / 4), c4 = u % (VB / 4);
+      d.h[j] = load_f32x4(hr, ((uint32_t)row * V + 4 * c4) * 4u);
     }
-    oa[vb] = exp2_hw(gt * kLog2e) * oa[vb];
-  }
-
-  // (i) A^T blocks for key blocks jb <= wave, then (iii) o^T += v_new^T A^T
-  // in pairs of key blocks (32 keys per matrix step).
+    if (kq) {
+      const rsrc_t kr = make_rsrc(kin + ((size_t)it.b * L * H + it.h) * K,
+                                  live ? ((uint32_t)(L - 1) * krow + K) * 2u : 0u);
 #pragma unroll
-  for (int kp = 0; kp < 2; ++kp) {
-    if (2 * kp > wave) break;
-    f32x4 at[2];
+      for (int j = 0; j < KU; ++j) {
+        const int u = tid + 256 * j, t = u / (K / 8), c8 = u % (K / 8);
+        d.k[j] = load_b128(kr, ((t0 + t) * krow + 8 * c8) * 2u);
+      }
+      // q: this wave's 16 tokens, in the k-slot map (K = 32kk + 4lq + 0..3
+      // and 32kk + 16 + 4lq + 0..3), straight into operand registers
+      const rsrc_t qr = make_rsrc(qin + ((size_t)it.b * L * H + it.h) * K,
+                                  live ? ((uint32_t)(L - 1) * krow + K) * 2u : 0u);
+      const uint32_t tq = t0 + 16 * wave + lr;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int jb = 2 * kp + s2;
-      at[s2] = (f32x4){0, 0, 0, 0};
-      if (jb <= wave) {
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const uint16_t* kp0 = ks + (16 * jb + lr) * KS + 32 * kk + 4 * lq;
-          const u32x2 a = *(const u32x2*)kp0;
-          const u32x2 bb = *(const u32x2*)(kp0 + 16);
-          at[s2] = mfma_bf16((u32x4){a[0], a[1], bb[0], bb[1]}, qf[kk], at[s2]);
-        }
-        const f32x4 gj = *(const f32x4*)(gs + 16 * jb + 4 * lq);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jb + 4 * lq + r;
-          const float e = at[s2][r] * exp2_hw((gt - gj[r]) * kLog2e);
-          at[s2][r] = j <= tl ? e : 0.0f;
-        }
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x2 a = load_b64(qr, (tq * krow + 32 * kk + 4 * lq) * 2u);
+        const u32x2 bq = load_b64(qr, (tq * krow + 32 * kk + 16 + 4 * lq) * 2u);
+        d.q[kk] = (u32x4){a[0], a[1], bq[0], bq[1]};
       }
     }
-    u32x4 bh, bl;
-    split8(at[0], at[1], bh, bl);
+    const rsrc_t vr = make_rsrc(vnin + ((size_t)it.b * L * H + it.h) * V,
+                                live ? ((uint32_t)(L - 1) * vrow + V) * 2u : 0u);
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+      const int u = tid + 256 * j, t = u / (VB / 8), c8 = u % (VB / 8);
+      d.v[j] = load_b128(vr, ((t0 + t) * vrow + it.vh * VB + 8 * c8) * 2u);
+    }
+    const rsrc_t gr = make_rsrc(g + (size_t)it.b * L * H + it.h,
+                                live ? ((uint32_t)(L - 1) * H + 1) * 4u : 0u);
+    d.g = load_f32(gr, (tid < C && t0 + tid < (uint32_t)L) ? (t0 + tid) * (uint32_t)H * 4u
+                                                          : kPastRange);
+  };
+
+  Ld nx;
+  u32x4 qf[NKK];
+  issue(i0, true, true, nx);
+  for (int i = i0; i < i1; ++i) {
+    const Item it = decode(i);
+    const bool kq = loads_kq(i);
+    __syncthreads();  // the previous item's LDS reads are done
+    // Stage: the state split into bf16 hi + lo, k and v_new as loaded, g.
+#pragma unroll
+    for (int j = 0; j < HU; ++j) {
+      const int u = tid + 256 * j, row = u / (VB / 4), c4 = u % (VB / 4);
+      uint32_t hh0, hl0, hh1, hl1;
+      split_bf16(nx.h[j][0], nx.h[j][1], hh0, hl0);
+      split_bf16(nx.h[j][2], nx.h[j][3], hh1, hl1);
+      *(u32x2*)(hhi + row * HS + 4 * c4) = (u32x2){hh0, hh1};
+      *(u32x2*)(hlo + row * HS + 4 * c4) = (u32x2){hl0, hl1};
+    }
+    if (kq) {
+#pragma unroll
+      for (int j = 0; j < KU; ++j) {
+        const int u = tid + 256 * j, t = u / (K / 8), c8 = u % (K / 8);
+        *(u32x4*)(ks + t * KS + 8 * c8) = nx.k[j];
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) qf[kk] = nx.q[kk];
+    }
+#pragma unroll
+    for (int j = 0; j < VU; ++j) {
+      const int u = tid + 256 * j, t = u / (VB / 8), c8 = u % (VB / 8);
+      *(u32x4*)(vs + t * VS + 8 * c8) = nx.v[j];
+    }
+    if (tid < C) gs[tid] = nx.g;
+    // the next item's loads
+    {
+      const bool live = i + 1 < i1;
+      issue(live ? i + 1 : i, live, live && loads_kq(i + 1), nx);
+    }
+    __syncthreads();
+
+    const int tl = 16 * wave + lr;               // this lane's token in the chunk
+    const float gt = gs[tl];
+
+    // (ii) inter term: o^T = h^T q^T, then e^{g_t} per token.
+    f32x4 oa[NVB];
 #pragma unroll
     for (int vb = 0; vb < NVB; ++vb) {
-      const int o0 = (32 * kp + 4 * lq + (lr >> 2)) * VS + 16 * vb + 4 * (lr & 3);
-      const u32x2 e0 = lds_read_tr16(vs + o0), e1 = lds_read_tr16(vs + o0 + 16 * VS);
-      const u32x4 av = {e0[0], e0[1], e1[0], e1[1]};
-      oa[vb] = mfma_bf16(av, bh, oa[vb]);
-      oa[vb] = mfma_bf16(av, bl, oa[vb]);
-    }
-  }
-
-  // o[t][v .. v+3] for v = 64 vh + 16 vb + 4 lq; tokens past the end are
-  // outside the buffer range and dropped.
-  constexpr int OES = OBF16 ? 2 : 4;
-  const rsrc_t orr = make_rsrc((char*)out + ((size_t)b * L * H + h) * V * OES,
-                               ((uint32_t)(L - 1) * vrow + V) * OES);
+      oa[vb] = (f32x4){0, 0, 0, 0};
 #pragma unroll
-  for (int vb = 0; vb < NVB; ++vb) {
-    const f32x4 ov = scale * oa[vb];
-    const uint32_t off = (tq * vrow + vh * VB + 16 * vb + 4 * lq) * OES;
-    if constexpr (OBF16) {
-      __builtin_amdgcn_raw_buffer_store_b64((u32x2){pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])},
-                                            orr, (int)off, 0, 0);
-    } else {
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), orr, (int)off, 0, 0);
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int o0 = (32 * kk + 4 * lq + (lr >> 2)) * HS + 16 * vb + 4 * (lr & 3);
+        const u32x2 a0 = lds_read_tr16(hhi + o0), a1 = lds_read_tr16(hhi + o0 + 16 * HS);
+        const u32x2 c0 = lds_read_tr16(hlo + o0), c1 = lds_read_tr16(hlo + o0 + 16 * HS);
+        oa[vb] = mfma_bf16((u32x4){a0[0], a0[1], a1[0], a1[1]}, qf[kk], oa[vb]);
+        oa[vb] = mfma_bf16((u32x4){c0[0], c0[1], c1[0], c1[1]}, qf[kk], oa[vb]);
+      }
+      oa[vb] = exp2_hw(gt * kLog2e) * oa[vb];
+    }
+
+    // (i) A^T blocks for key blocks jb <= wave, then (iii) o^T += v_new^T A^T
+    // in pairs of key blocks (32 keys per matrix step).
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      if (2 * kp > wave) break;
+      f32x4 at[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int jb = 2 * kp + s2;
+        at[s2] = (f32x4){0, 0, 0, 0};
+        if (jb <= wave) {
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            const uint16_t* kp0 = ks + (16 * jb + lr) * KS + 32 * kk + 4 * lq;
+            const u32x2 a = *(const u32x2*)kp0;
+            const u32x2 bb = *(const u32x2*)(kp0 + 16);
+            at[s2] = mfma_bf16((u32x4){a[0], a[1], bb[0], bb[1]}, qf[kk], at[s2]);
+          }
+          const f32x4 gj = *(const f32x4*)(gs + 16 * jb + 4 * lq);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jb + 4 * lq + r;
+            const float e = at[s2][r] * exp2_hw((gt - gj[r]) * kLog2e);
+            at[s2][r] = j <= tl ? e : 0.0f;
+          }
+        }
+      }
+      u32x4 bh, bl;
+      split8(at[0], at[1], bh, bl);
+#pragma unroll
+      for (int vb = 0; vb < NVB; ++vb) {
+        const int o0 = (32 * kp + 4 * lq + (lr >> 2)) * VS + 16 * vb + 4 * (lr & 3);
+        const u32x2 e0 = lds_read_tr16(vs + o0), e1 = lds_read_tr16(vs + o0 + 16 * VS);
+        const u32x4 av = {e0[0], e0[1], e1[0], e1[1]};
+        oa[vb] = mfma_bf16(av, bh, oa[vb]);
+        oa[vb] = mfma_bf16(av, bl, oa[vb]);
+      }
+    }
+
+    // o[t][v .. v+3] for v = 64 vh + 16 vb + 4 lq; tokens past the end are
+    // outside the buffer range and dropped.
+    constexpr int OES = OBF16 ? 2 : 4;
+    const rsrc_t orr = make_rsrc((char*)out + ((size_t)it.b * L * H + it.h) * V * OES,
+                                 ((uint32_t)(L - 1) * vrow + V) * OES);
+    const uint32_t tq = (uint32_t)(it.c * C) + 16 * wave + lr;
+#pragma unroll
+    for (int vb = 0; vb < NVB; ++vb) {
+      const f32x4 ov = scale * oa[vb];
+      const uint32_t off = (tq * vrow + it.vh * VB + 16 * vb + 4 * lq) * OES;
+      if constexpr (OBF16) {
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){pack_bf16(ov[0], ov[1]), pack_bf16(ov[2], ov[3])},
+                                              orr, (int)off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ov), orr, (int)off, 0, 0);
+      }
     }
   }
+}
+
+// Workgroups resident on the whole device at once for `kernel` (a multiple
+// of 8, so the XCD-aware placement applies): the persistent grid.
+int gdn_resident_slots(const void* kernel, int threads) {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
+    return 0;
+  const int slots = (per < 1 ? 1 : per) * cus;
+  return slots < 8 ? slots : slots / 8 * 8;
+}
+
+template <int K, int V, bool OBF16>
+int launch_o(const void* q, const void* k, const void* vnew, const float* h, const float* g,
+             void* o, float scale, const GdnShape& s, hipStream_t st) {
+  const int nt = (int)s.nchunks();
+  const int items = (int)(s.batch * nt * s.nheads * (V / 64));
+  static std::atomic<int> cached{0};
+  int slots = cached.load(std::memory_order_relaxed);
+  if (slots <= 0) {
+    slots = gdn_resident_slots((const void*)gdn_fwd_o_kernel<K, V, OBF16>, 256);
+    if (slots <= 0) return (int)hipErrorInvalidDevice;
+    cached.store(slots, std::memory_order_relaxed);
+  }
+  const unsigned grid = (unsigned)(items < slots ? items : slots);
+  hipLaunchKernelGGL((gdn_fwd_o_kernel<K, V, OBF16>), dim3(grid), dim3(256), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vnew, h, g, o, scale,
+                     (int)s.seqlen, (int)s.nheads, nt, items);
+  return (int)hipGetLastError();
 }
 
 template <int K, int V>
 int launch_o_kv(const void* q, const void* k, const void* vnew, const float* h, const float* g,
                 void* o, float scale, bool obf16, const GdnShape& s, hipStream_t st) {
-  const int nt = (int)s.nchunks();
-  const unsigned blocks = (unsigned)(s.batch * nt * s.nheads * (V / 64));
-  if (obf16)
-    hipLaunchKernelGGL((gdn_fwd_o_kernel<K, V, true>), dim3(blocks), dim3(256), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vnew, h, g, o,
-                       scale, (int)s.seqlen, (int)s.nheads, nt);
-  else
-    hipLaunchKernelGGL((gdn_fwd_o_kernel<K, V, false>), dim3(blocks), dim3(256), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vnew, h, g, o,
-                       scale, (int)s.seqlen, (int)s.nheads, nt);
-  return (int)hipGetLastError();
+  if (obf16) return launch_o<K, V, true>(q, k, vnew, h, g, o, scale, s, st);
+  return launch_o<K, V, false>(q, k, vnew, h, g, o, scale, s, st);
 }
 
 }  // namespace
