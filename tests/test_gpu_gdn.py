@@ -142,6 +142,10 @@ O_CASES = [
     (1, 64, 2, 64, 128, 1.0),
     (2, 129, 2, 128, 128, 0.0883883),
     (1, 1, 2, 128, 128, 1.0),
+    # more items than resident workgroups: runs of one or two items that start
+    # at either column block of a head (k and q loaded or reused)
+    (5, 640, 10, 128, 128, 1.0),
+    (4, 1100, 12, 64, 64, 0.5),
 ]
 
 
