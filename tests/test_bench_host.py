@@ -1,0 +1,46 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU contract and the
+algorithmic byte counts the roofline divides by.
+
+The byte counts are written out here term by term for the small-model layer
+(batch 4, 2048 tokens, 24 heads of 64, state 128, one group, chunk 64, bf16
+inputs, fp32 y, no initial state): each stage must move its inputs and
+outputs once.
+"""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_algorithmic_bytes_of_the_small_layer():
+    import bench
+    from ssd_workloads import WORKLOADS
+    w = WORKLOADS["small_bf16"]
+    b, L, H, P, N, G, T = 4, 2048, 24, 64, 128, 1, 64
+    assert (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size) == \
+        (b, L, H, P, N, G, T)
+    nc = L // T
+    x = 2 * b * L * H * P                      # bf16 x
+    bc = 2 * b * L * G * N                     # one of B, C (bf16)
+    g_dt = 4 * b * L * H * 2                   # g and dt_t (fp32)
+    states = 4 * b * H * nc * P * N            # every chunk's starting state (fp32)
+    final = 4 * b * H * P * N
+    y = 4 * b * L * H * P                      # fp32 y
+    by, fl = bench.algorithmic(w, 4)
+    # stage 1 reads dt and writes g and dt_t
+    assert by["chunk_cumsum"] == 4 * b * L * H + g_dt == 2359296
+    assert by["fwd_pass_state"] == x + bc + g_dt + states + final == 132644864
+    # stage 3 also reads C and D
+    assert by["compute_out"] == x + 2 * bc + g_dt + states + 4 * H + y == 181928032
+    # the state pass's contraction: one multiply-add per (token, head, p, n)
+    assert fl["fwd_pass_state"] == 2 * b * L * H * P * N
