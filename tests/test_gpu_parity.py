@@ -51,6 +51,12 @@ SMALL = [
     _wl("bf16_T128_N128_1head_tiles_group_per_head", "bf16", 4, 150, 8, 8, 128, 128, True),
     _wl("bf16_T128_N128_single_token", "bf16", 1, 1, 1, 1, 128, 128, True),
     _wl("fp32_T256_N64_single_token", "fp32", 2, 1, 2, 2, 64, 256, True),
+    # decay extremes: A dt from about -0.5 to -70 per token (most exponents
+    # underflow within a few tokens), and from -2e-6 to -1e-3 per token (the
+    # state keeps nearly the whole sequence)
+    _wl("bf16_T128_N128_strong_decay", "bf16", 2, 300, 4, 2, 128, 128, True, 1.0, (2.0, 3.0)),
+    _wl("bf16_T256_N64_weak_decay_init", "bf16", 1, 900, 3, 1, 64, 256, True, -4.0, (-6.0, -5.0)),
+    _wl("fp32_T64_N128_strong_decay", "fp32", 2, 200, 3, 3, 128, 64, False, 1.0, (2.0, 3.0)),
 ]
 
 
