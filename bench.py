@@ -1,27 +1,34 @@
 """Benchmark of the Mamba-2 SSD chunked forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-configs] [--no-cpu-baseline] [--no-side]
 
 A step is one ssd_forward call -- the whole hot path: stage 1 (chunk
 cumsum), stage 2 (state pass), stage 3 (fused output) -- over one batch of
-synthetic input of the named workload (default: the small-model bf16 layer,
-batch 4 x 2048 tokens, 24 heads of 64, state 128, chunk 64).  The wall clock
-over K steps gives tokens/s.  A second timed loop calls the three stage entry
-points (ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_compute_out) -- exactly the
-kernels ssd_forward launches -- each captured in a HIP graph and replayed
-between HIP events on the launch stream, which gives each kernel's mean
-duration for the per-stage lines and the roofline.
+synthetic input of the named workload.  The default workload is the largest
+of the five (wide_fp32: 64 sequences of 1024 tokens, 48 heads, 8 groups,
+state 64, fp32; 4.6 GB of algorithmic traffic per step).  The wall clock
+over K steps gives `value` in tokens/s.
 
-Inputs are resident in HBM before timing.  Steps rotate over several
-independent input/output sets whose total footprint is >= 1 GiB, so no step
-finds its operands in the 256 MB last-level cache from the previous step.
+Per-kernel durations come from HIP graphs: each stage entry point's launches
+(over the rotating input sets) are captured once and the graph is replayed
+between two HIP events on the launch stream, so a duration holds neither
+host launch time nor an event between launches.  They give the per-stage
+lines and the roofline of the dominant kernel: algorithmic bytes per launch
+(the method's inputs and outputs, each moved once) over the mean duration,
+against the MI355X HBM peak of 8 TB/s.
 
-Prints ONE JSON line: tokens/s (whole job), the roofline of the dominant
-kernel from algorithmic bytes and its event-measured duration, and the fp64
-CPU oracle timed on this host as a reported baseline.  Side fields (not part
-of the step): the streaming decode step at the workload's batch and heads,
-the causal conv1d that feeds the layer's SSD, and the Gated DeltaNet
-chunk_fwd_h / chunk_fwd_o kernels on their own layer shape.
+The `configs` map repeats the graph timing (ssd_forward and each stage) for
+all five workloads, so every configuration has a number from this run.
+
+Inputs are resident in HBM before timing.  Steps rotate over independent
+input/output sets whose total footprint is >= 1 GiB, so no step finds its
+operands in the 256 MB last-level cache from the previous step.
+
+Prints ONE JSON line.  Side fields (not part of the step): the streaming
+decode step at the workload's batch and heads, the causal conv1d that feeds
+the layer's SSD, and the Gated DeltaNet chunk_fwd_h / chunk_fwd_o kernels on
+their own layer shape.
 """
 from __future__ import annotations
 
@@ -29,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import statistics
 import sys
 import time
@@ -41,23 +49,29 @@ METRIC = "SSD forward tokens/sec + % of HBM/MFMA roofline, 1×MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_TFLOPS = 2500.0      # dense
 FP32_MFMA_TFLOPS = 157.3
+CONFIG_ORDER = ["tiny_fp32", "small_bf16", "large_bf16", "long_bf16", "wide_fp32"]
 # the kernel sources of each stage (the state pass runs as one kernel or as
 # chunk_state + state_passing, chosen by shape)
 STAGE_SOURCES = {"chunk_cumsum": ["ssd_chunk_cumsum.hip"],
                  "fwd_pass_state": ["ssd_fwd_pass_state.hip", "ssd_state_two_level.hip"],
                  "compute_out": ["ssd_compute_out.hip"]}
+STEP_KERNELS = ["chunk_cumsum", "fwd_pass_state", "compute_out"]
 
 
 def algorithmic(w, y_bytes: int):
     """Bytes each stage must move and FLOPs it must do (no redundancy, no
-    masked upper triangle), per launch over the whole workload."""
+    masked upper triangle), per launch over the whole workload.
+
+    Stage 1 counts dt in and g out (8 bytes per (token, head)); the
+    head-major copy of dt it also writes is a design choice of this
+    implementation and is reported apart (`design_extra_bytes`)."""
     b, L, H, P, N, G, T = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
                            w.ngroups, w.chunk_size)
     e = 2 if w.dtype == "bf16" else 4
     nc = w.nchunks
     init = 1 if w.init_std is not None else 0
     by = {
-        "chunk_cumsum": 12 * b * L * H,
+        "chunk_cumsum": 8 * b * L * H,
         "fwd_pass_state": (e * b * L * H * P + e * b * L * G * N + 8 * b * L * H
                            + 4 * b * H * P * N * init + 4 * b * H * nc * P * N
                            + 4 * b * H * P * N),
@@ -73,6 +87,36 @@ def algorithmic(w, y_bytes: int):
     return by, fl
 
 
+def design_extra_bytes(w) -> dict:
+    """Bytes a stage moves beyond the algorithmic count by design: stage 1's
+    head-major copy of dt (read back by stages 2 and 3 in place of dt)."""
+    return {"chunk_cumsum": 4 * w.batch * w.seqlen * w.nheads}
+
+
+def issued_mfma_flop(w) -> dict:
+    """Matrix-instruction work the kernels issue, from their structure:
+    causal blocks on or below the diagonal in 16-row (and, for bf16 L'X,
+    32-token) steps, and two instructions (bf16 hi + lo) for every computed
+    fp32 operand with bf16 inputs.  C B^T is counted once per (batch, chunk,
+    group)."""
+    b, L, H, P, N, G, T = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                           w.ngroups, w.chunk_size)
+    nc = w.nchunks
+    nib = T // 16
+    if w.dtype == "bf16":
+        cs = 2 * (2 * T * P * N)                                  # C S^T, hi + lo
+        lx = sum(ib // 2 + 1 for ib in range(nib)) * 32 * 16 * P * 2 * 2
+        cb = sum(ib + 1 for ib in range(nib)) * 16 * 16 * N * 2
+        a2 = 2 * (2 * b * L * H * P * N)                          # P^T: w o x hi + lo
+    else:
+        cs = 2 * T * P * N
+        lx = sum(ib + 1 for ib in range(nib)) * 16 * 16 * P * 2
+        cb = sum(ib + 1 for ib in range(nib)) * 16 * 16 * N * 2
+        a2 = 2 * b * L * H * P * N
+    return {"fwd_pass_state": a2,
+            "compute_out": b * nc * H * (cs + lx) + b * nc * G * cb}
+
+
 def source_sha(stage: str) -> str:
     h = hashlib.sha256()
     for name in STAGE_SOURCES[stage]:
@@ -81,40 +125,178 @@ def source_sha(stage: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, stage: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if there is none or the kernel source changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_traffic.json")
+def committed_profile(workload: str, stage: str, kind: str):
+    """A committed counter summary (profiles/<stage>_<workload>_<kind>.json)
+    if it was taken from the current kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_{kind}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_sha") != source_sha(stage):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(w, inp, min_seconds: float = 10.0):
-    """The fp64 oracle on the host cores, over the full workload, repeated
-    until about `min_seconds` of CPU work (at least 3 runs)."""
+    """The fp64 oracle (the parity checker, untuned) on the host cores, over
+    the full workload, repeated until about `min_seconds` of CPU work (at
+    least 2 runs)."""
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
     if threads <= 0:
         threads = len(os.sched_getaffinity(0))
+    used = min(threads, w.batch * w.nheads)      # OpenMP over (batch, head) pairs
     times = []
-    while len(times) < 3 or (sum(times) < min_seconds and len(times) < 1000):
+    while len(times) < 2 or (sum(times) < min_seconds and len(times) < 1000):
         t0 = time.perf_counter()
         oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
                        inp["D"], inp["init_state"], chunk_size=w.chunk_size,
                        nthreads=threads)
         times.append(time.perf_counter() - t0)
     total = sum(times)
-    return {"value": w.tokens * len(times) / total, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+    return {"value": round(w.tokens * len(times) / total, 1), "unit": "tokens/s",
+            "cores": used, "kind": "oracle", "cpu_model": cpu_model(),
+            "threads_requested": threads, "host_cpus": os.cpu_count(),
             "sample": (f"the full {w.name} workload ({w.batch * w.nheads} "
                        f"(batch, head) pairs x {w.seqlen} tokens), fp64 "
                        f"token recurrence, OpenMP over pairs; {len(times)} runs, "
                        f"{total:.1f} s in total (median run {statistics.median(times):.3f} s)")}
+
+
+def graph_time_ms(calls, nrep: int = 3) -> float:
+    """Mean duration of one call: the calls are captured once in a HIP graph,
+    the graph is replayed once untimed and `nrep` times between two HIP
+    events on the current stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in calls:
+            f()
+    g.replay()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(nrep):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (nrep * len(calls))
+    del g
+    return ms
+
+
+class WorkloadRun:
+    """Device input/output sets of one workload and the calls that use them."""
+
+    def __init__(self, ssd, w, y_dtype, dev):
+        import torch
+        from ssd_workloads import make_inputs
+        self.ssd, self.w, self.dev = ssd, w, dev
+        self.inp = make_inputs(w)
+        inp = self.inp
+        tin = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.y_bytes = 2 if y_dtype == torch.bfloat16 else 4
+        self.by, self.fl = algorithmic(w, self.y_bytes)
+        b, L, H, P, N, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk_size
+        nc = w.nchunks
+        set_bytes = self.by["fwd_pass_state"] + self.by["compute_out"]
+        self.nsets = max(1, min(16, -(-(1 << 30) // set_bytes)))
+        d = ssd.SsdDims(b, L, H, P, N, w.ngroups, T)
+        ws_bytes = ssd.workspace_bytes(d)
+        base = {k: torch.from_numpy(inp[k]).to(dev, tin) for k in ("x", "B", "C")}
+        for k in ("dt", "A", "D"):
+            base[k] = torch.from_numpy(inp[k]).to(dev)
+        base["init"] = (None if inp["init_state"] is None
+                        else torch.from_numpy(inp["init_state"]).to(dev))
+
+        def make_set(i):
+            s = dict(base) if i == 0 else {k: (None if v is None else v.clone())
+                                            for k, v in base.items()}
+            s["ws"] = torch.empty(-(-ws_bytes // 4), device=dev)   # ssd_forward's workspace
+            s["g"] = s["ws"][: b * H * L].view(b, H, L)
+            s["dt_t"] = s["ws"][b * H * L: 2 * b * H * L].view(b, H, L)
+            s["states"] = torch.empty(b, H, nc, P, N, device=dev)
+            s["final"] = torch.empty(b, H, P, N, device=dev)
+            s["y"] = torch.empty(b, L, H, P, device=dev, dtype=y_dtype)
+            return s
+        self.sets = [make_set(i) for i in range(self.nsets)]
+
+    def forward(self, i):
+        s = self.sets[i % self.nsets]
+        self.ssd.ssd_forward(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"], s["init"],
+                             s["y"], s["states"], s["final"], s["ws"], self.w.chunk_size)
+
+    def stage(self, name, i):
+        s, T, ssd = self.sets[i % self.nsets], self.w.chunk_size, self.ssd
+        if name == "chunk_cumsum":
+            ssd.ssd_chunk_cumsum(s["dt"], s["A"], s["g"], s["dt_t"], T)
+        elif name == "fwd_pass_state":
+            ssd.ssd_fwd_pass_state(s["x"], s["B"], s["dt_t"], s["g"], s["init"], s["states"],
+                                   s["final"], T)
+        else:
+            ssd.ssd_compute_out(s["x"], s["B"], s["C"], s["dt_t"], s["g"], s["states"],
+                                s["D"], s["y"], T)
+
+    def time_all(self, nlaunch: int) -> dict:
+        """Graph-replay durations (ms) of ssd_forward and of each stage."""
+        for i in range(max(3, self.nsets)):
+            self.forward(i)
+        out = {"ssd_forward": graph_time_ms([lambda i=i: self.forward(i)
+                                             for i in range(nlaunch)])}
+        for n in STEP_KERNELS:
+            out[n] = graph_time_ms([lambda i=i, n=n: self.stage(n, i) for i in range(nlaunch)])
+        return out
+
+    def summary(self, dur: dict) -> dict:
+        """The configs-map entry: tokens/s, per-stage microseconds, HBM
+        fractions and the output stage's matrix-core fractions."""
+        w = self.w
+        peak_tf = BF16_MFMA_TFLOPS if w.dtype == "bf16" else FP32_MFMA_TFLOPS
+        issued = issued_mfma_flop(w)
+        stages = {}
+        for n in STEP_KERNELS:
+            ms = dur[n]
+            gbs = self.by[n] / (ms * 1e-3) / 1e9
+            e = {"us": round(ms * 1e3, 2), "alg_bytes": self.by[n],
+                 "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+            if n in design_extra_bytes(w):
+                extra = design_extra_bytes(w)[n]
+                e["design_extra_bytes"] = extra
+                e["hbm_frac_with_extra"] = round(
+                    (self.by[n] + extra) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            if n in issued:
+                tf_alg = self.fl[n] / (ms * 1e-3) / 1e12
+                tf_iss = issued[n] / (ms * 1e-3) / 1e12
+                e["alg_TFLOP_per_s"] = round(tf_alg, 2)
+                e["issued_TFLOP_per_s"] = round(tf_iss, 2)
+                e["mfma_peak_TFLOP_per_s"] = peak_tf
+                e["mfma_alg_frac"] = round(tf_alg / peak_tf, 4)
+                e["mfma_issued_frac"] = round(tf_iss / peak_tf, 4)
+            stages[n] = e
+        step_ms = dur["ssd_forward"]
+        step_bytes = sum(self.by[n] for n in STEP_KERNELS)
+        return {"shape": {"batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                          "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                          "chunk_size": w.chunk_size, "dtype": w.dtype},
+                "tokens_per_s": round(w.tokens / (step_ms * 1e-3), 1),
+                "step_us": round(step_ms * 1e3, 2),
+                "step_alg_bytes": step_bytes,
+                "step_hbm_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "hbm_floor_us": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+                "stages": stages}
 
 
 def gdn_bench(ssd, c, make, dev, stream, nrep):
@@ -172,168 +354,35 @@ def gdn_bench(ssd, c, make, dev, stream, nrep):
             "note": "w, u synthetic (the WY transform is not on this path); bf16 v_new and o"}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="small_bf16")
-    ap.add_argument("--y-dtype", default="fp32", choices=["fp32", "bf16"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gdn", action="store_true",
-                    help="skip the Gated DeltaNet kernels' timing")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one 1 GiB device copy (HBM counter scale)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
-              "is not supported (the path shards over (batch, head) with no "
-              "communication between GPUs).", file=sys.stderr)
-        return 2
-
-    import numpy as np
+def side_fields(ssd, run, dev, stream, steps, y_dtype, with_gdn):
+    """Decode step, conv1d and Gated DeltaNet timings (not part of the step)."""
     import torch
-
-    import mamba_ssd_chunked_fwd_amd as ssd
-    from ssd_workloads import (GDN_WORKLOADS, WORKLOADS, conv_workload_for,
-                               make_conv_inputs, make_gdn_inputs, make_inputs)
-
-    w = WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    inp = make_inputs(w)
+    from ssd_workloads import (GDN_WORKLOADS, conv_workload_for, make_conv_inputs,
+                               make_gdn_inputs)
+    w, sets, nsets = run.w, run.sets, run.nsets
+    b, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
     tin = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    ty = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
-    b, L, H, P, N, G, T = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
-                           w.ngroups, w.chunk_size)
-    nc = w.nchunks
-    y_bytes = 2 if ty == torch.bfloat16 else 4
-    by, fl = algorithmic(w, y_bytes)
-    set_bytes = by["fwd_pass_state"] + by["compute_out"]
-    nsets = max(1, min(16, -(-(1 << 30) // set_bytes)))
-
-    d = ssd.SsdDims(b, L, H, P, N, G, T)
-    ws_bytes = ssd.workspace_bytes(d)
-
-    def make_set():
-        s = {k: torch.from_numpy(inp[k]).to(dev, tin) for k in ("x", "B", "C")}
-        for k in ("dt", "A", "D"):
-            s[k] = torch.from_numpy(inp[k]).to(dev)
-        s["init"] = (None if inp["init_state"] is None
-                     else torch.from_numpy(inp["init_state"]).to(dev))
-        s["ws"] = torch.empty(-(-ws_bytes // 4), device=dev)  # ssd_forward's workspace
-        s["g"] = s["ws"][: b * H * L].view(b, H, L)
-        s["dt_t"] = s["ws"][b * H * L: 2 * b * H * L].view(b, H, L)
-        s["states"] = torch.empty(b, H, nc, P, N, device=dev)
-        s["final"] = torch.empty(b, H, P, N, device=dev)
-        s["y"] = torch.empty(b, L, H, P, device=dev, dtype=ty)
-        return s
-
-    sets = [make_set() for _ in range(nsets)]
-    stream = torch.cuda.current_stream(dev)
-
-    def forward(s):
-        ssd.ssd_forward(s["x"], s["dt"], s["A"], s["B"], s["C"], s["D"],
-                        s["init"], s["y"], s["states"], s["final"], s["ws"], T)
-
-    # ---- the step: ssd_forward, the whole hot path, as a user calls it
-    for i in range(args.warmup):
-        forward(sets[i % nsets])
-    # the timed steps carry no events between them: nothing but the step's
-    # own launches reaches the stream inside the timed region
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        forward(sets[i % nsets])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # the same step bracketed by HIP events, in a loop of its own
-    nfe = max(20, args.steps // 2)
-    fwd_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nfe)]
-    torch.cuda.synchronize()
-    for i in range(nfe):
-        fwd_ev[i][0].record(stream)
-        forward(sets[i % nsets])
-        fwd_ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in fwd_ev)
-
-    # ---- every entry point on its own, HIP events on the launch stream
-    def stage_calls(s):
-        return [
-            ("chunk_cumsum", lambda: ssd.ssd_chunk_cumsum(s["dt"], s["A"], s["g"],
-                                                          s["dt_t"], T)),
-            ("fwd_pass_state", lambda: ssd.ssd_fwd_pass_state(
-                s["x"], s["B"], s["dt_t"], s["g"], s["init"], s["states"],
-                s["final"], T)),
-            ("compute_out", lambda: ssd.ssd_compute_out(
-                s["x"], s["B"], s["C"], s["dt_t"], s["g"], s["states"], s["D"],
-                s["y"], T)),
-        ]
-    stage_names = [n for n, _ in stage_calls(sets[0])]
-    nst = max(20, args.steps // 2)
-    for i in range(5):
-        for _, f in stage_calls(sets[i % nsets]):
-            f()
-    # Each entry point's nst launches (over the rotating sets, whose inputs
-    # the warm-up steps produced) are captured once in a HIP graph; the graph
-    # is replayed between two HIP events, so the mean launch duration holds
-    # neither host launch time nor an event between launches.  (Eager loops
-    # with one event per launch add about 3 us per launch; the short first
-    # stage is then host-bound.)
-    dur = {}
-    for k, n in enumerate(stage_names):
-        sg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(sg):
-            for i in range(nst):
-                stage_calls(sets[i % nsets])[k][1]()
-        sg.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(3):
-            sg.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dur[n] = e0.elapsed_time(e1) / (3 * nst)
-        del sg
-
-    # ---- the streaming decode step at the same batch and heads: one token
-    #      per sequence from the carried state (read and written in place)
+    # the streaming decode step at the same batch and heads: one token per
+    # sequence from the carried state (read and written in place), replayed
+    # from a HIP graph (a step is shorter than one Python launch)
     dec_states = [torch.randn(b, H, P, N, device=dev) for _ in range(nsets)]
     dec_in = [(s["x"][:, 0].contiguous(), s["dt"][:, 0].contiguous(),
                s["B"][:, 0].contiguous(), s["C"][:, 0].contiguous(),
-               torch.empty(b, H, P, device=dev, dtype=ty)) for s in sets]
-    for i in range(5):
+               torch.empty(b, H, P, device=dev, dtype=y_dtype)) for s in sets]
+
+    def dec(i):
         xt, dtt, Bt, Ct, yt = dec_in[i % nsets]
         ssd.ssd_decode_step(xt, dtt, sets[0]["A"], Bt, Ct, sets[0]["D"],
                             dec_states[i % nsets], yt)
-    # A decode step is a few microseconds of GPU work, less than the host
-    # needs to issue one through Python, so an eager loop would time the
-    # host.  The steps are captured once in a HIP graph and the graph is
-    # replayed between two events (each replay = ndec steps back to back).
-    ndec, nrep_dec = 50, 8
-    dgraph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(dgraph):
-        for i in range(ndec):
-            xt, dtt, Bt, Ct, yt = dec_in[i % nsets]
-            ssd.ssd_decode_step(xt, dtt, sets[0]["A"], Bt, Ct, sets[0]["D"],
-                                dec_states[i % nsets], yt)
-    dgraph.replay()
-    dec_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    dec_ev[0].record(stream)
-    for _ in range(nrep_dec):
-        dgraph.replay()
-    dec_ev[1].record(stream)
-    torch.cuda.synchronize()
-    dec_ms = dec_ev[0].elapsed_time(dec_ev[1]) / (nrep_dec * ndec)
-    del dgraph
+    for i in range(5):
+        dec(i)
+    dec_ms = graph_time_ms([lambda i=i: dec(i) for i in range(50)], nrep=8)
     dec_bytes = (8 * b * H * P * N + (2 if w.dtype == "bf16" else 4) * (b * H * P + 2 * b * G * N)
-                 + 4 * b * H + 8 * H + y_bytes * b * H * P)
+                 + 4 * b * H + 8 * H + run.y_bytes * b * H * P)
+    del dec_states, dec_in
 
-    # ---- the causal depthwise conv1d that feeds this layer's SSD (over the
-    #      x, B and C channels), x and out in the workload's storage type
+    # the causal depthwise conv1d that feeds this layer's SSD (over the x, B
+    # and C channels), x and out in the workload's storage type
     cw = conv_workload_for(w)
     cinp = make_conv_inputs(cw, seed=7)
     cx0 = torch.from_numpy(cinp["x"]).to(dev, tin)
@@ -345,70 +394,127 @@ def main() -> int:
     for i in range(5):
         cx, co = conv_sets[i % nconv]
         ssd.ssd_causal_conv1d(cx, cwt, cbias, co)
-    nconv_steps = max(50, args.steps)
-    conv_ev = [torch.cuda.Event(enable_timing=True) for _ in range(nconv_steps + 1)]
-    torch.cuda.synchronize()
-    conv_ev[0].record(stream)
-    for i in range(nconv_steps):
-        cx, co = conv_sets[i % nconv]
-        ssd.ssd_causal_conv1d(cx, cwt, cbias, co)
-        conv_ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    conv_ms = statistics.mean(conv_ev[i].elapsed_time(conv_ev[i + 1])
-                              for i in range(nconv_steps))
+    conv_ms = graph_time_ms([lambda i=i: ssd.ssd_causal_conv1d(conv_sets[i % nconv][0], cwt,
+                                                                cbias, conv_sets[i % nconv][1])
+                             for i in range(max(10, nconv))])
     conv_bytes = cset_bytes + 4 * cw.dim * (cw.width + 1)
-    del conv_sets
+    del conv_sets, cx0
+    out = {
+        "decode_step": {"ms": round(dec_ms, 5), "tokens_per_s": round(b / (dec_ms * 1e-3), 1),
+                        "alg_bytes": dec_bytes,
+                        "GB_per_s": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "note": "one token for each of the batch's sequences, state in place; "
+                                "steps replayed from a HIP graph"},
+        "causal_conv1d": {"ms": round(conv_ms, 5),
+                          "shape": {"batch": cw.batch, "dim": cw.dim, "seqlen": cw.seqlen,
+                                    "width": cw.width, "dtype": cw.dtype},
+                          "alg_bytes": conv_bytes,
+                          "GB_per_s": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "note": "the conv over the layer's x, B, C channels; not part of "
+                                  "the step; replayed from a HIP graph"},
+    }
+    if with_gdn:
+        out["gated_deltanet"] = gdn_bench(ssd, GDN_WORKLOADS["gdn_layer_bf16"], make_gdn_inputs,
+                                          dev, stream, max(20, steps // 2))
+    return out
 
-    # ---- Gated DeltaNet chunked forward (chunk_fwd_h then chunk_fwd_o) on
-    #      its own layer shape, v_new and o in bf16
-    gdn = gdn_bench(ssd, GDN_WORKLOADS["gdn_layer_bf16"], make_gdn_inputs, dev, stream,
-                    max(20, args.steps // 2)) if not args.no_gdn else None
 
+def copy_rate(dev) -> float:
+    """A 1 GiB device-to-device copy (read + write), timed from a graph of 5
+    copies: the runtime's own streaming rate on this GPU, for context."""
+    import torch
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    ms = graph_time_ms([lambda: cdst.copy_(csrc)] * 5, nrep=1)
+    del csrc, cdst
+    return 2 * (1 << 28) * 4 / (ms * 1e-3) / 1e9
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="wide_fp32")
+    ap.add_argument("--y-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the named workload (no configs map)")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the decode step, conv1d and Gated DeltaNet timings")
+    ap.add_argument("--no-gdn", action="store_true",
+                    help="skip the Gated DeltaNet kernels' timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (HBM counter scale)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
+              "is not supported (the path shards over (batch, head) with no "
+              "communication between GPUs).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import mamba_ssd_chunked_fwd_amd as ssd
+    from ssd_workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ty = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
+    stream = torch.cuda.current_stream(dev)
+    nlaunch = max(10, min(40, args.steps // 2))
+
+    run = WorkloadRun(ssd, w, ty, dev)
+    # ---- the step: ssd_forward, the whole hot path, as a user calls it
+    for i in range(args.warmup):
+        run.forward(i)
+    # the timed steps carry no events between them: nothing but the step's
+    # own launches reaches the stream inside the timed region
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run.forward(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dur = run.time_all(nlaunch)
+    head = run.summary(dur)
+    side = (side_fields(ssd, run, dev, stream, args.steps, ty, not args.no_gdn)
+            if not args.no_side else {})
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
+    copy_gbs = copy_rate(dev)
+    inp, nsets, step_flop = run.inp, run.nsets, sum(run.fl[n] for n in STEP_KERNELS)
+    del run
+    torch.cuda.empty_cache()
 
-    # The practical streaming ceiling of this GPU in the same run: a 1 GiB
-    # device-to-device copy (read + write), timed from a graph of 5 copies.
-    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    cdst = torch.empty_like(csrc)
-    cdst.copy_(csrc)
-    cg = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(cg):
-        for _ in range(5):
-            cdst.copy_(csrc)
-    cg.replay()
-    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    ce[0].record(stream)
-    cg.replay()
-    ce[1].record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * csrc.numel() * 4 * 5 / (ce[0].elapsed_time(ce[1]) * 1e-3) / 1e9
-    del cg, csrc, cdst
+    configs = {}
+    if not args.no_configs:
+        for name in CONFIG_ORDER:
+            if name == w.name:
+                configs[name] = head
+                continue
+            r = WorkloadRun(ssd, WORKLOADS[name], ty, dev)
+            configs[name] = r.summary(r.time_all(nlaunch))
+            del r
+            torch.cuda.empty_cache()
 
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = w.tokens / (wall / args.steps)
-    peak_tf = BF16_MFMA_TFLOPS if w.dtype == "bf16" else FP32_MFMA_TFLOPS
-    stages = {}
-    for n in stage_names:
-        ms = dur[n]
-        gbs = by[n] / (ms * 1e-3) / 1e9
-        stages[n] = {"ms": round(ms, 5), "alg_bytes": by[n], "alg_flop": fl[n],
-                     "GB_per_s": round(gbs, 1),
-                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "frac_of_copy": round(gbs / copy_gbs, 4),
-                     "TFLOP_per_s": round(fl[n] / (ms * 1e-3) / 1e12, 2),
-                     "mfma_frac_of_peak": round(fl[n] / (ms * 1e-3) / 1e12 / peak_tf, 4)}
-    # the kernels one ssd_forward call launches
-    step_kernels = ["chunk_cumsum", "fwd_pass_state", "compute_out"]
-    dom = max(step_kernels, key=lambda n: dur[n])
-    achieved = by[dom] / (dur[dom] * 1e-3) / 1e9
-    traffic = measured_traffic(w.name, dom)
-    step_bytes = sum(by[n] for n in step_kernels)
-    total_flop = sum(fl[n] for n in step_kernels)
+    stages = head["stages"]
+    dom = max(STEP_KERNELS, key=lambda n: stages[n]["us"])
+    achieved = stages[dom]["GB_per_s"]
+    traffic_rec = committed_profile(w.name, dom, "traffic")
+    mfma_rec = committed_profile(w.name, "compute_out", "mfma")
+    if mfma_rec is not None:
+        stages["compute_out"]["mfma_busy_frac_counters"] = mfma_rec.get("mfma_busy_frac")
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -420,38 +526,27 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "f32" if w.dtype == "fp32" else "bf16",
         "data": "synthetic (seeded; shapes and distributions of the workload)",
-        "config": {"workload": w.name, "batch": b, "seqlen": L, "nheads": H,
-                   "headdim": P, "dstate": N, "ngroups": G, "chunk_size": T,
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen,
+                   "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate,
+                   "ngroups": w.ngroups, "chunk_size": w.chunk_size,
                    "x_dtype": w.dtype, "y_dtype": args.y_dtype,
                    "state_dtype": "fp32", "input_sets_rotated": nsets},
         "roofline": {"bound": "hbm", "kernel": dom,
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic},
+                     "traffic": (traffic_rec or {}).get("hbm_bytes_per_launch"),
+                     "alg_bytes_per_launch": stages[dom]["alg_bytes"],
+                     "us_per_launch": stages[dom]["us"]},
         "stages": stages,
-        "ssd_forward_event_ms": round(fwd_ms, 5),
-        "decode_step": {"ms": round(dec_ms, 5), "tokens_per_s": round(b / (dec_ms * 1e-3), 1),
-                        "alg_bytes": dec_bytes,
-                        "GB_per_s": round(dec_bytes / (dec_ms * 1e-3) / 1e9, 1),
-                        "hbm_frac": round(dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "note": "one token for each of the batch's sequences, state in place; "
-                                "steps replayed from a HIP graph; the rotated states "
-                                f"({nsets} x {4 * b * H * P * N / 1e6:.1f} MB) stay in the "
-                                "last-level cache"},
-        "causal_conv1d": {"ms": round(conv_ms, 5),
-                          "shape": {"batch": cw.batch, "dim": cw.dim, "seqlen": cw.seqlen,
-                                    "width": cw.width, "dtype": cw.dtype},
-                          "alg_bytes": conv_bytes,
-                          "GB_per_s": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
-                          "hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                          "note": "the conv over the layer's x, B, C channels; not part of the step"},
-        "gated_deltanet": gdn,
-        "copy_GB_per_s": round(copy_gbs, 1),
-        "effective_TFLOP_per_s": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
-        "hbm_floor_ms": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
+        "ssd_forward_graph_us": head["step_us"],
+        "effective_TFLOP_per_s": round(step_flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "hbm_floor_ms": round(head["hbm_floor_us"] / 1e3, 5),
+        "copy_GB_per_s_context": round(copy_gbs, 1),
+        "configs": configs,
     }
+    out.update(side)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)

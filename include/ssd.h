@@ -82,7 +82,7 @@ typedef struct {
 } ssd_dims;
 
 /* Human-readable name of a status code (static storage; never NULL). */
-const char *ssd_status_string(int status);
+const char *ssd_status_string(ssd_status status);
 
 /* Bytes of device workspace ssd_forward needs: the stage-1 outputs g and
  * dt_t, 8 * batch * nheads * seqlen.  Returns 0 when dims is NULL or
@@ -116,10 +116,12 @@ ssd_status ssd_chunk_cumsum(const float *dt, const float *A, float *g,
  *   dt_t, g [b, H, L] fp32 (from ssd_chunk_cumsum)
  *   init_state [b, H, P, N] fp32 or NULL
  *   states [b, H, nc, P, N] fp32 (written)   final_state [b, H, P, N] or NULL
+ * init_state and final_state may be the same buffer (a sequence continued in
+ * place); no other output may overlap an input.
  */
 ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt_t,
                               const float *g, const float *init_state,
-                              float *states, float *final_state, int in_dtype,
+                              float *states, float *final_state, ssd_dtype in_dtype,
                               const ssd_dims *dims, void *stream);
 
 /*
@@ -143,10 +145,13 @@ ssd_status ssd_fwd_pass_state(const void *x, const void *B, const float *dt_t,
  *   states[b,h,c] = 2^{g_last(c-1)} states[b,h,c-1] + states[b,h,c], c >= 1;
  *   final_state = 2^{g_last(nc-1)} states[b,h,nc-1] + final_state (if not NULL).
  *   g [b, H, L] fp32 from ssd_chunk_cumsum; states, init, final fp32.
+ * In this two-call form final_state carries P_{nc-1} from the first call to
+ * the second, so init_state must not overlap final_state
+ * (SSD_ERR_INVALID_ARGUMENT); ssd_fwd_pass_state has no such restriction.
  */
 ssd_status ssd_chunk_state(const void *x, const void *B, const float *dt_t,
                            const float *g, float *states, float *final_state,
-                           int in_dtype, const ssd_dims *dims, void *stream);
+                           ssd_dtype in_dtype, const ssd_dims *dims, void *stream);
 ssd_status ssd_state_passing(const float *g, const float *init_state,
                              float *states, float *final_state,
                              const ssd_dims *dims, void *stream);
@@ -166,7 +171,7 @@ ssd_status ssd_state_passing(const float *g, const float *init_state,
 ssd_status ssd_compute_out(const void *x, const void *B, const void *C,
                            const float *dt_t, const float *g,
                            const float *states, const float *D, void *y,
-                           int in_dtype, int y_dtype, const ssd_dims *dims,
+                           ssd_dtype in_dtype, ssd_dtype y_dtype, const ssd_dims *dims,
                            void *stream);
 
 /*
@@ -175,13 +180,14 @@ ssd_status ssd_compute_out(const void *x, const void *B, const void *C,
  * bytes, else
  * SSD_ERR_WORKSPACE), then stages 2 and 3, all on `stream`.  Returns y, the
  * per-chunk starting states and (if final_state != NULL) the final state,
- * which a later call can take back as init_state to continue the sequence.
+ * which a later call can take back as init_state to continue the sequence
+ * (init_state and final_state may be the same buffer).
  */
 ssd_status ssd_forward(const void *x, const float *dt, const float *A,
                        const void *B, const void *C, const float *D,
                        const float *init_state, void *y, float *states,
                        float *final_state, void *workspace,
-                       size_t workspace_bytes, int in_dtype, int y_dtype,
+                       size_t workspace_bytes, ssd_dtype in_dtype, ssd_dtype y_dtype,
                        const ssd_dims *dims, void *stream);
 
 /*
@@ -202,7 +208,7 @@ ssd_status ssd_forward(const void *x, const float *dt, const float *A,
  */
 ssd_status ssd_decode_step(const void *x, const float *dt, const float *A,
                            const void *B, const void *C, const float *D,
-                           float *state, void *y, int in_dtype, int y_dtype,
+                           float *state, void *y, ssd_dtype in_dtype, ssd_dtype y_dtype,
                            const ssd_dims *dims, void *stream);
 
 /*
@@ -238,8 +244,8 @@ typedef struct {
  */
 ssd_status ssd_gdn_chunk_fwd_h(const void *k, const void *w, const void *u,
                                const float *g, const float *h0, float *h,
-                               void *v_new, float *final_state, int in_dtype,
-                               int v_dtype, const ssd_gdn_dims *dims,
+                               void *v_new, float *final_state, ssd_dtype in_dtype,
+                               ssd_dtype v_dtype, const ssd_gdn_dims *dims,
                                void *stream);
 
 /*
@@ -257,8 +263,8 @@ ssd_status ssd_gdn_chunk_fwd_h(const void *k, const void *w, const void *u,
  */
 ssd_status ssd_gdn_chunk_fwd_o(const void *q, const void *k, const void *v_new,
                                const float *h, const float *g, void *o,
-                               float scale, int in_dtype, int v_dtype,
-                               int o_dtype, const ssd_gdn_dims *dims,
+                               float scale, ssd_dtype in_dtype, ssd_dtype v_dtype,
+                               ssd_dtype o_dtype, const ssd_gdn_dims *dims,
                                void *stream);
 
 /*
@@ -279,7 +285,7 @@ ssd_status ssd_gdn_chunk_fwd_o(const void *q, const void *k, const void *v_new,
 ssd_status ssd_causal_conv1d(const void *x, const float *weight,
                              const float *bias, void *out, int64_t batch,
                              int64_t dim, int64_t seqlen, int64_t width,
-                             int x_dtype, int out_dtype, void *stream);
+                             ssd_dtype x_dtype, ssd_dtype out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

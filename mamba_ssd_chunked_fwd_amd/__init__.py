@@ -229,7 +229,7 @@ def ssd_chunk_state(x: torch.Tensor, B: torch.Tensor, dt_t: torch.Tensor,
     b, L, H, P, N, nc = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, nchunks(d)
     f32 = (torch.float32,)
     _check(x, "x", None, (torch.float32, torch.bfloat16))
-    _check(B, "B", None, (x.dtype,), dev)
+    _check(B, "B", (b, L, d.ngroups, N), (x.dtype,), dev)
     _check(dt_t, "dt_t", (b, H, L), f32, dev)
     _check(g, "g", (b, H, L), f32, dev)
     _check(states, "states", (b, H, nc, P, N), f32, dev)

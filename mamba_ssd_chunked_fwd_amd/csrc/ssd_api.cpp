@@ -4,6 +4,7 @@
 // then enqueues the stage kernels on the caller's stream.  No allocation, no
 // host synchronisation, no global mutable state.
 #include <climits>
+#include <cstddef>
 #include <cstdint>
 
 #include "ssd.h"
@@ -29,8 +30,10 @@ ssd_status check_dims(const ssd_dims* d, ssd::Shape* out) {
   // counts; keep every launch and every (batch * seqlen) within range.
   const int64_t nc = (d->seqlen + d->chunk_size - 1) / d->chunk_size;
   if (d->batch * d->seqlen > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  // (batch * per_head_blocks <= 2^34 here, so only the last factor needs a
+  // division to stay clear of 64-bit overflow)
   const int64_t per_head_blocks = nc * 4 > 8 ? nc * 4 : 8;
-  if (d->batch * d->nheads * per_head_blocks > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  if (d->batch * per_head_blocks > INT32_MAX / d->nheads) return SSD_ERR_INVALID_ARGUMENT;
   if (d->headdim != 64) return SSD_ERR_UNSUPPORTED;
   // Kernels address each sequence with 32-bit byte offsets (up to one chunk
   // past its end).
@@ -48,7 +51,7 @@ ssd_status check_dims(const ssd_dims* d, ssd::Shape* out) {
   return SSD_OK;
 }
 
-bool ok_dtype(int t) { return t == SSD_F32 || t == SSD_BF16; }
+bool ok_dtype(ssd_dtype t) { return t == SSD_F32 || t == SSD_BF16; }
 
 ssd_status check_gdn_dims(const ssd_gdn_dims* d, ssd::GdnShape* out) {
   if (d == nullptr) return SSD_ERR_INVALID_ARGUMENT;
@@ -57,7 +60,7 @@ ssd_status check_gdn_dims(const ssd_gdn_dims* d, ssd::GdnShape* out) {
     if (e < 1 || e > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
   if (d->batch * d->seqlen > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
   const int64_t nt = (d->seqlen + 63) / 64;
-  if (d->batch * d->nheads * (nt > 8 ? nt : 8) > INT32_MAX) return SSD_ERR_INVALID_ARGUMENT;
+  if (d->batch * (nt > 8 ? nt : 8) > INT32_MAX / d->nheads) return SSD_ERR_INVALID_ARGUMENT;
   if (d->chunk_size != 64) return SSD_ERR_UNSUPPORTED;
   if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128))
     return SSD_ERR_UNSUPPORTED;
@@ -72,19 +75,27 @@ ssd_status check_gdn_dims(const ssd_gdn_dims* d, ssd::GdnShape* out) {
 
 ssd_status from_hip(int err) { return err == 0 ? SSD_OK : SSD_ERR_HIP; }
 
+// Whether two byte ranges of length n starting at a and b (either may be
+// null) share any byte.
+bool overlap(const void* a, const void* b, size_t n) {
+  if (a == nullptr || b == nullptr || n == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + n && y < x + n;
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* ssd_status_string(int status) {
+const char* ssd_status_string(ssd_status status) {
   switch (status) {
     case SSD_OK: return "SSD_OK";
     case SSD_ERR_INVALID_ARGUMENT: return "SSD_ERR_INVALID_ARGUMENT";
     case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
     case SSD_ERR_HIP: return "SSD_ERR_HIP";
-    default: return "SSD_ERR_UNKNOWN";
   }
+  return "SSD_ERR_UNKNOWN";
 }
 
 size_t ssd_forward_workspace_bytes(const ssd_dims* dims) {
@@ -112,7 +123,7 @@ ssd_status ssd_chunk_cumsum(const float* dt, const float* A, float* g,
 
 ssd_status ssd_fwd_pass_state(const void* x, const void* B, const float* dt_t,
                               const float* g, const float* init_state,
-                              float* states, float* final_state, int in_dtype,
+                              float* states, float* final_state, ssd_dtype in_dtype,
                               const ssd_dims* dims, void* stream) {
   ssd::Shape s;
   const ssd_status st = check_dims(dims, &s);
@@ -127,7 +138,7 @@ ssd_status ssd_fwd_pass_state(const void* x, const void* B, const float* dt_t,
 }
 
 ssd_status ssd_chunk_state(const void* x, const void* B, const float* dt_t, const float* g,
-                           float* states, float* final_state, int in_dtype,
+                           float* states, float* final_state, ssd_dtype in_dtype,
                            const ssd_dims* dims, void* stream) {
   ssd::Shape s;
   const ssd_status st = check_dims(dims, &s);
@@ -137,7 +148,7 @@ ssd_status ssd_chunk_state(const void* x, const void* B, const float* dt_t, cons
       !ok_opt(final_state))
     return SSD_ERR_INVALID_ARGUMENT;
   return from_hip(ssd::launch_chunk_state(x, B, dt_t, g, states, final_state,
-                                          in_dtype == SSD_BF16, s, stream));
+                                          in_dtype == SSD_BF16, false, s, stream));
 }
 
 ssd_status ssd_state_passing(const float* g, const float* init_state, float* states,
@@ -147,13 +158,18 @@ ssd_status ssd_state_passing(const float* g, const float* init_state, float* sta
   if (st != SSD_OK) return st;
   if (!ok_ptr(g) || !ok_opt(init_state) || !ok_ptr(states) || !ok_opt(final_state))
     return SSD_ERR_INVALID_ARGUMENT;
-  return from_hip(ssd::launch_state_passing(g, init_state, states, final_state, s, stream));
+  // final_state holds the last chunk's contribution on entry, so it cannot
+  // also be the initial state here.
+  const size_t sbytes = sizeof(float) * (size_t)(s.batch * s.nheads * s.headdim * s.dstate);
+  if (overlap(init_state, final_state, sbytes)) return SSD_ERR_INVALID_ARGUMENT;
+  return from_hip(
+      ssd::launch_state_passing(g, init_state, states, final_state, false, s, stream));
 }
 
 ssd_status ssd_compute_out(const void* x, const void* B, const void* C,
                            const float* dt_t, const float* g,
                            const float* states, const float* D, void* y,
-                           int in_dtype, int y_dtype, const ssd_dims* dims,
+                           ssd_dtype in_dtype, ssd_dtype y_dtype, const ssd_dims* dims,
                            void* stream) {
   ssd::Shape s;
   const ssd_status st = check_dims(dims, &s);
@@ -171,7 +187,7 @@ ssd_status ssd_forward(const void* x, const float* dt, const float* A,
                        const void* B, const void* C, const float* D,
                        const float* init_state, void* y, float* states,
                        float* final_state, void* workspace,
-                       size_t workspace_bytes, int in_dtype, int y_dtype,
+                       size_t workspace_bytes, ssd_dtype in_dtype, ssd_dtype y_dtype,
                        const ssd_dims* dims, void* stream) {
   ssd::Shape s;
   const ssd_status st = check_dims(dims, &s);
@@ -199,7 +215,7 @@ ssd_status ssd_forward(const void* x, const float* dt, const float* A,
 
 ssd_status ssd_decode_step(const void* x, const float* dt, const float* A,
                            const void* B, const void* C, const float* D, float* state,
-                           void* y, int in_dtype, int y_dtype, const ssd_dims* dims,
+                           void* y, ssd_dtype in_dtype, ssd_dtype y_dtype, const ssd_dims* dims,
                            void* stream) {
   if (dims == nullptr) return SSD_ERR_INVALID_ARGUMENT;
   // One token: seqlen and chunk_size are not read; check the rest with
@@ -220,7 +236,7 @@ ssd_status ssd_decode_step(const void* x, const float* dt, const float* A,
 
 ssd_status ssd_gdn_chunk_fwd_h(const void* k, const void* w, const void* u, const float* g,
                                const float* h0, float* h, void* v_new, float* final_state,
-                               int in_dtype, int v_dtype, const ssd_gdn_dims* dims,
+                               ssd_dtype in_dtype, ssd_dtype v_dtype, const ssd_gdn_dims* dims,
                                void* stream) {
   ssd::GdnShape s;
   const ssd_status st = check_gdn_dims(dims, &s);
@@ -235,8 +251,8 @@ ssd_status ssd_gdn_chunk_fwd_h(const void* k, const void* w, const void* u, cons
 }
 
 ssd_status ssd_gdn_chunk_fwd_o(const void* q, const void* k, const void* v_new, const float* h,
-                               const float* g, void* o, float scale, int in_dtype, int v_dtype,
-                               int o_dtype, const ssd_gdn_dims* dims, void* stream) {
+                               const float* g, void* o, float scale, ssd_dtype in_dtype, ssd_dtype v_dtype,
+                               ssd_dtype o_dtype, const ssd_gdn_dims* dims, void* stream) {
   ssd::GdnShape s;
   const ssd_status st = check_gdn_dims(dims, &s);
   if (st != SSD_OK) return st;
@@ -251,7 +267,7 @@ ssd_status ssd_gdn_chunk_fwd_o(const void* q, const void* k, const void* v_new, 
 
 ssd_status ssd_causal_conv1d(const void* x, const float* weight, const float* bias, void* out,
                              int64_t batch, int64_t dim, int64_t seqlen, int64_t width,
-                             int x_dtype, int out_dtype, void* stream) {
+                             ssd_dtype x_dtype, ssd_dtype out_dtype, void* stream) {
   if (batch < 1 || dim < 1 || seqlen < 1 || width < 1) return SSD_ERR_INVALID_ARGUMENT;
   if (!ok_dtype(x_dtype) || !ok_dtype(out_dtype)) return SSD_ERR_INVALID_ARGUMENT;
   if (!ok_ptr(x) || !ok_ptr(weight) || !ok_opt(bias) || !ok_ptr(out))

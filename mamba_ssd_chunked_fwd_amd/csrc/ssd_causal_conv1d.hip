@@ -24,6 +24,7 @@
 // Rows whose byte length is not a multiple of 16 take a plain per-token
 // kernel instead.
 #include "ssd_device.h"
+#include "ssd_host.h"
 #include "ssd_launch.h"
 
 namespace ssd {
@@ -213,6 +214,7 @@ int launch_t(const void* x, const float* weight, const float* bias, void* out, i
 int launch_causal_conv1d(const void* x, const float* weight, const float* bias, void* out,
                          int64_t batch, int64_t dim, int64_t seqlen, int width, bool bf16_in,
                          bool bf16_out, void* stream) {
+  clear_launch_error();
   hipStream_t st = (hipStream_t)stream;
   if (bf16_in)
     return bf16_out ? launch_t<true, true>(x, weight, bias, out, batch, dim, seqlen, width, st)

@@ -21,6 +21,7 @@
 // (16 bytes per lane where the rows allow it).  The stage moves 12 bytes per
 // (token, head) and is HBM-bound.
 #include "ssd_device.h"
+#include "ssd_host.h"
 #include "ssd_launch.h"
 
 namespace ssd {
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(
 
 int launch_chunk_cumsum(const float* dt, const float* A, float* g,
                         float* dt_t, const Shape& s, void* stream) {
+  clear_launch_error();
   const int nc = (int)s.nchunks();
   const int nhq = (int)((s.nheads + kHeadsPerWave - 1) / kHeadsPerWave);
   const int64_t nwaves = s.batch * nc * nhq;

@@ -45,9 +45,8 @@
 // HBM traffic per item: the x tile, the state S_c (4*64*N bytes), dt, g and
 // y; B and C once per (b, c, group) run.  The stage is HBM-bound at every
 // supported shape by algorithmic count.
-#include <atomic>
-
 #include "ssd_device.h"
+#include "ssd_host.h"
 #include "ssd_launch.h"
 
 namespace ssd {
@@ -576,21 +575,6 @@ __global__ __launch_bounds__(Geo<T>::NTHR) void compute_out_f32(
 }
 
 // ------------------------------------------------------------- launching
-// Workgroups resident on the whole device at once for `kernel`: the grid of
-// the persistent kernels.  Computed once per instantiation (a property of
-// the kernel and the device model, not mutable state); a multiple of 8 so
-// the XCD-aware placement applies.
-int resident_slots(const void* kernel, int threads) {
-  int dev = 0, cus = 0, per = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
-    return 0;
-  const int slots = (per < 1 ? 1 : per) * cus;
-  return slots < 8 ? slots : slots / 8 * 8;
-}
-
 template <bool BF16, int T, int N, bool YBF16>
 int launch_t(const void* x, const void* B, const void* C, const float* dt_t,
              const float* g, const float* states, const float* D, void* y,
@@ -601,13 +585,10 @@ int launch_t(const void* x, const void* B, const void* C, const float* dt_t,
   const int items = (int)(s.batch * nc * s.nheads);
   const void* kern = BF16 ? (const void*)compute_out_bf16<T, N, YBF16>
                           : (const void*)compute_out_f32<T, N, YBF16>;
-  static std::atomic<int> cached{0};
-  int slots = cached.load(std::memory_order_relaxed);
-  if (slots <= 0) {
-    slots = resident_slots(kern, NTHR);
-    if (slots <= 0) return (int)hipErrorInvalidDevice;
-    cached.store(slots, std::memory_order_relaxed);
-  }
+  // the persistent grid: as many workgroups as are resident on the device
+  static PerDeviceInt resident;
+  const int slots = resident.get([&](int dev) { return resident_slots(kern, NTHR, dev); });
+  if (slots <= 0) return (int)hipErrorInvalidDevice;
   const unsigned grid = (unsigned)(items < slots ? items : slots);
   if constexpr (BF16) {
     hipLaunchKernelGGL((compute_out_bf16<T, N, YBF16>), dim3(grid), dim3(NTHR), 0, st,
@@ -654,6 +635,7 @@ int launch_compute_out(const void* x, const void* B, const void* C,
                        const float* dt_t, const float* g, const float* states,
                        const float* D, void* y, bool bf16_in, bool bf16_out,
                        const Shape& s, void* stream) {
+  clear_launch_error();
   hipStream_t st = (hipStream_t)stream;
   if (bf16_in) return launch_chunk<true>(x, B, C, dt_t, g, states, D, y, bf16_out, s, st);
   return launch_chunk<false>(x, B, C, dt_t, g, states, D, y, bf16_out, s, st);

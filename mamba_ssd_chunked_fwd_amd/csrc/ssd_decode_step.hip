@@ -21,6 +21,7 @@
 // and C are loaded once.  A row's N/4 units belong to N/4 consecutive lanes
 // of one wave, so the row sum for y is a lane reduction.
 #include "ssd_device.h"
+#include "ssd_host.h"
 #include "ssd_launch.h"
 
 namespace ssd {
@@ -142,6 +143,7 @@ int launch_y(const void* x, const float* dt, const float* A, const void* B, cons
 int launch_decode_step(const void* x, const float* dt, const float* A, const void* B,
                        const void* C, const float* D, float* state, void* y, bool bf16_in,
                        bool bf16_out, const Shape& s, void* stream) {
+  clear_launch_error();
   hipStream_t st = (hipStream_t)stream;
   if (s.dstate == 64) {
     return bf16_in ? launch_y<64, true>(x, dt, A, B, C, D, state, y, bf16_out, s, st)

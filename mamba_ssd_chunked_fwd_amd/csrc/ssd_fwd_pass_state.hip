@@ -38,9 +38,8 @@
 // HBM traffic per (b, h, chunk): x (e*T*64) + B (e*T*N, shared by the heads
 // of a group) + dt, g (8*T) + the stored state (4*64*N); the stored states
 // dominate, so the stage is HBM-bound.
-#include <atomic>
-
 #include "ssd_device.h"
+#include "ssd_host.h"
 #include "ssd_launch.h"
 
 namespace ssd {
@@ -555,17 +554,12 @@ int choose_bf_cfg(const Shape& s, int cus) {
   return most;
 }
 
+// Compute units of the current device (the MI355X count if the query fails;
+// only the tile choice depends on it), cached per device.
 int device_cus() {
-  static std::atomic<int> cached{0};
-  int cus = cached.load(std::memory_order_relaxed);
-  if (cus > 0) return cus;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return 256;  // the MI355X count; only the tile choice depends on it
-  cached.store(cus, std::memory_order_relaxed);
-  return cus;
+  static PerDeviceInt cache;
+  const int cus = cache.get(query_cus);
+  return cus > 0 ? cus : 256;
 }
 
 template <int T, int N, int HB, int RS, int BN, int NBW>
@@ -692,11 +686,15 @@ int launch_fwd_pass_state(const void* x, const void* B, const float* dt_t,
                           const float* g, const float* init_state,
                           float* states, float* final_state, bool bf16_in,
                           const Shape& s, void* stream) {
+  clear_launch_error();
   hipStream_t st = (hipStream_t)stream;
   if (bf16_in && use_two_level(s, device_cus())) {
-    const int r = launch_chunk_state(x, B, dt_t, g, states, final_state, true, s, stream);
+    // P_{nc-1} is parked in the states[0] slot rather than in final_state,
+    // so init_state may be the final_state buffer (a sequence continued in
+    // place), as it may for the one-pass kernels.
+    const int r = launch_chunk_state(x, B, dt_t, g, states, final_state, true, true, s, stream);
     if (r != 0) return r;
-    return launch_state_passing(g, init_state, states, final_state, s, stream);
+    return launch_state_passing(g, init_state, states, final_state, true, s, stream);
   }
   if (bf16_in)
     return launch_chunk<true>(x, B, dt_t, g, init_state, states, final_state, s, st);

@@ -28,9 +28,9 @@
 // are loaded into registers while the current one is processed, then staged
 // into the other half of a double-buffered LDS tile set (one barrier per
 // chunk).
-#include <atomic>
 
 #include "ssd_device.h"
+#include "ssd_host.h"
 #include "ssd_launch.h"
 
 namespace ssd {
@@ -554,31 +554,17 @@ __global__ __launch_bounds__(256) void gdn_fwd_o_kernel(
   }
 }
 
-// Workgroups resident on the whole device at once for `kernel` (a multiple
-// of 8, so the XCD-aware placement applies): the persistent grid.
-int gdn_resident_slots(const void* kernel, int threads) {
-  int dev = 0, cus = 0, per = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess)
-    return 0;
-  const int slots = (per < 1 ? 1 : per) * cus;
-  return slots < 8 ? slots : slots / 8 * 8;
-}
-
 template <int K, int V, bool OBF16>
 int launch_o(const void* q, const void* k, const void* vnew, const float* h, const float* g,
              void* o, float scale, const GdnShape& s, hipStream_t st) {
   const int nt = (int)s.nchunks();
   const int items = (int)(s.batch * nt * s.nheads * (V / 64));
-  static std::atomic<int> cached{0};
-  int slots = cached.load(std::memory_order_relaxed);
-  if (slots <= 0) {
-    slots = gdn_resident_slots((const void*)gdn_fwd_o_kernel<K, V, OBF16>, 256);
-    if (slots <= 0) return (int)hipErrorInvalidDevice;
-    cached.store(slots, std::memory_order_relaxed);
-  }
+  // the persistent grid: as many workgroups as are resident on the device
+  static PerDeviceInt resident;
+  const int slots = resident.get([](int dev) {
+    return resident_slots((const void*)gdn_fwd_o_kernel<K, V, OBF16>, 256, dev);
+  });
+  if (slots <= 0) return (int)hipErrorInvalidDevice;
   const unsigned grid = (unsigned)(items < slots ? items : slots);
   hipLaunchKernelGGL((gdn_fwd_o_kernel<K, V, OBF16>), dim3(grid), dim3(256), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vnew, h, g, o, scale,
@@ -598,6 +584,7 @@ int launch_o_kv(const void* q, const void* k, const void* vnew, const float* h, 
 int launch_gdn_fwd_o(const void* q, const void* k, const void* vnew, const float* h,
                      const float* g, void* o, float scale, bool obf16, const GdnShape& s,
                      void* stream) {
+  clear_launch_error();
   hipStream_t st = (hipStream_t)stream;
   if (s.dk == 64)
     return s.dv == 64 ? launch_o_kv<64, 64>(q, k, vnew, h, g, o, scale, obf16, s, st)
@@ -609,6 +596,7 @@ int launch_gdn_fwd_o(const void* q, const void* k, const void* vnew, const float
 int launch_gdn_fwd_h(const void* k, const void* w, const void* u, const float* g,
                      const float* h0, float* hout, void* vnew, float* fin, bool vbf16,
                      const GdnShape& s, void* stream) {
+  clear_launch_error();
   hipStream_t st = (hipStream_t)stream;
   if (s.dk == 64)
     return s.dv == 64 ? launch_h_kv<64, 64>(k, w, u, g, h0, hout, vnew, fin, vbf16, s, st)

@@ -28,11 +28,14 @@ int launch_compute_out(const void* x, const void* B, const void* C,
 
 // The two-level form of stage 2 (chunk_state writes each chunk's zero-state
 // contribution into the slot of the state it feeds; state_passing turns the
-// slots into the states in place).
+// slots into the states in place).  With park / parked, the last chunk's
+// contribution goes through the states[0] slot instead of final_state, so
+// init_state may alias final_state.
 int launch_chunk_state(const void* x, const void* B, const float* dt_t, const float* g,
-                       float* states, float* fin, bool bf16_in, const Shape& s, void* stream);
+                       float* states, float* fin, bool bf16_in, bool park, const Shape& s,
+                       void* stream);
 int launch_state_passing(const float* g, const float* init, float* states, float* fin,
-                         const Shape& s, void* stream);
+                         bool parked, const Shape& s, void* stream);
 
 int launch_decode_step(const void* x, const float* dt, const float* A, const void* B,
                        const void* C, const float* D, float* state, void* y, bool bf16_in,

@@ -30,6 +30,7 @@
 //   chunks in blocks of D.  The loads do not depend on the carried value,
 //   so the next block's loads are in flight while a block is combined.
 #include "ssd_device.h"
+#include "ssd_host.h"
 #include "ssd_launch.h"
 
 namespace ssd {
@@ -52,7 +53,7 @@ template <int T, int N, int HB>
 __global__ __launch_bounds__(256 * HB) void chunk_state_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
-    float* __restrict__ final_state, int L, int H, int G, int nc) {
+    float* __restrict__ final_state, int L, int H, int G, int nc, int park) {
   constexpr int ST = HB == 1 ? 64 : 32;        // tokens per sub-tile
   constexpr int NSUB = T / ST;
   constexpr int XS = kHeadDim + 16;            // w o x row stride (bf16)
@@ -167,12 +168,14 @@ __global__ __launch_bounds__(256 * HB) void chunk_state_bf16(
     }
   }
 
-  // P_c into the slot of the state it feeds: states[c + 1], or final.
+  // P_c into the slot of the state it feeds: states[c + 1], or final (or,
+  // with `park`, the not yet written states[0]).
   float* dst = nullptr;
   if (c + 1 < nc) {
     dst = states + (((size_t)b * H + h) * nc + c + 1) * kHeadDim * N;
   } else if (final_state) {
-    dst = final_state + ((size_t)b * H + h) * kHeadDim * N;
+    dst = park ? states + ((size_t)b * H + h) * nc * kHeadDim * N
+               : final_state + ((size_t)b * H + h) * kHeadDim * N;
   }
   if (dst) {
     const int p = 16 * wr + lr;
@@ -192,7 +195,7 @@ template <int T, int N>
 __global__ __launch_bounds__(256) void chunk_state_f32(
     const float* __restrict__ x, const float* __restrict__ Bm,
     const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
-    float* __restrict__ final_state, int L, int H, int G, int nc) {
+    float* __restrict__ final_state, int L, int H, int G, int nc, int park) {
   constexpr int NB = N / 16;
   const int item = xcd_item(blockIdx.x, gridDim.x);   // as in the bf16 kernel
   const int h = item % H;
@@ -240,7 +243,8 @@ __global__ __launch_bounds__(256) void chunk_state_f32(
   if (c + 1 < nc) {
     dst = states + (((size_t)b * H + h) * nc + c + 1) * kHeadDim * N;
   } else if (final_state) {
-    dst = final_state + ((size_t)b * H + h) * kHeadDim * N;
+    dst = park ? states + ((size_t)b * H + h) * nc * kHeadDim * N
+               : final_state + ((size_t)b * H + h) * kHeadDim * N;
   }
   if (dst) {
     const int p = 16 * wave + lr;
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(256) void chunk_state_f32(
 template <int N, int D>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     const float* __restrict__ g, const float* __restrict__ init, float* __restrict__ states,
-    float* __restrict__ final_state, int L, int T, int nc) {
+    float* __restrict__ final_state, int L, int T, int nc, int parked) {
   constexpr int UNITS = kHeadDim * N / 4;      // 16-byte units per state
   constexpr int WPB = UNITS / 256;             // workgroups per (b, h)
   const int bh = blockIdx.x / WPB;
@@ -263,6 +267,11 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
   const float* gh = g + (size_t)bh * L;
 
   f32x4 s = init ? *(const f32x4*)(init + bh * sstride + 4 * (size_t)u) : (f32x4){0, 0, 0, 0};
+  // P_{nc-1}: in the final slot, or parked in states[0] (read before the
+  // slot is overwritten; each unit is read and written by its own thread,
+  // so init_state may then be the final_state buffer).
+  f32x4 plast = (f32x4){0, 0, 0, 0};
+  if (parked) plast = *(const f32x4*)st;
   *(f32x4*)st = s;
   // Chunks 1 .. nc-1 in blocks of D, software-pipelined over two register
   // blocks: the loads of block j+1 are issued before block j is combined.
@@ -298,18 +307,19 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
   if (final_state) {
     float* f = final_state + bh * sstride + 4 * (size_t)u;
     const float dec = exp2_hw(gh[min(nc * T, L) - 1]);
-    *(f32x4*)f = dec * s + *(const f32x4*)f;
+    if (!parked) plast = *(const f32x4*)f;
+    *(f32x4*)f = dec * s + plast;
   }
 }
 
 template <int T, int N, int HB>
 int launch_cs_hb(const void* x, const void* B, const float* dt_t, const float* g,
-                 float* states, float* fin, const Shape& s, hipStream_t st) {
+                 float* states, float* fin, bool park, const Shape& s, hipStream_t st) {
   const int nc = (int)s.nchunks();
   const unsigned blocks = (unsigned)(s.batch * nc * (s.nheads / HB));
   hipLaunchKernelGGL((chunk_state_bf16<T, N, HB>), dim3(blocks), dim3(256 * HB), 0, st,
                      (const uint16_t*)x, (const uint16_t*)B, dt_t, g, states, fin,
-                     (int)s.seqlen, (int)s.nheads, (int)s.ngroups, nc);
+                     (int)s.seqlen, (int)s.nheads, (int)s.ngroups, nc, (int)park);
   return (int)hipGetLastError();
 }
 
@@ -321,75 +331,78 @@ int launch_cs_hb(const void* x, const void* B, const float* dt_t, const float* g
 // 197 and 196): four heads need 83 KB of LDS, one workgroup per CU.
 template <int T, int N>
 int launch_cs(const void* x, const void* B, const float* dt_t, const float* g, float* states,
-              float* fin, const Shape& s, hipStream_t st) {
+              float* fin, bool park, const Shape& s, hipStream_t st) {
   const int64_t hpg = s.nheads / s.ngroups;
   const int64_t items = s.batch * s.nchunks() * s.nheads;
   if (hpg % 2 == 0 && items / 2 >= 256)
-    return launch_cs_hb<T, N, 2>(x, B, dt_t, g, states, fin, s, st);
-  return launch_cs_hb<T, N, 1>(x, B, dt_t, g, states, fin, s, st);
+    return launch_cs_hb<T, N, 2>(x, B, dt_t, g, states, fin, park, s, st);
+  return launch_cs_hb<T, N, 1>(x, B, dt_t, g, states, fin, park, s, st);
 }
 
 template <int T, int N>
 int launch_cs_f32(const void* x, const void* B, const float* dt_t, const float* g,
-                  float* states, float* fin, const Shape& s, hipStream_t st) {
+                  float* states, float* fin, bool park, const Shape& s, hipStream_t st) {
   const int nc = (int)s.nchunks();
   const unsigned blocks = (unsigned)(s.batch * nc * s.nheads);
   hipLaunchKernelGGL((chunk_state_f32<T, N>), dim3(blocks), dim3(256), 0, st, (const float*)x,
                      (const float*)B, dt_t, g, states, fin, (int)s.seqlen, (int)s.nheads,
-                     (int)s.ngroups, nc);
+                     (int)s.ngroups, nc, (int)park);
   return (int)hipGetLastError();
 }
 
 template <int N>
-int launch_sp(const float* g, const float* init, float* states, float* fin, const Shape& s,
-              hipStream_t st) {
+int launch_sp(const float* g, const float* init, float* states, float* fin, bool parked,
+              const Shape& s, hipStream_t st) {
   constexpr int UNITS = kHeadDim * N / 4;
   const unsigned blocks = (unsigned)(s.batch * s.nheads * (UNITS / 256));
   // D = 4 chunks per register block (measured on the 65536-token sequence:
   // 183 us against 265, 192 and 193 for D = 2, 8 and 16)
   hipLaunchKernelGGL((state_passing_kernel<N, 4>), dim3(blocks), dim3(256), 0, st, g, init,
-                     states, fin, (int)s.seqlen, (int)s.chunk, (int)s.nchunks());
+                     states, fin, (int)s.seqlen, (int)s.chunk, (int)s.nchunks(), (int)parked);
   return (int)hipGetLastError();
 }
 
 }  // namespace
 
 int launch_chunk_state(const void* x, const void* B, const float* dt_t, const float* g,
-                       float* states, float* fin, bool bf16_in, const Shape& s, void* stream) {
+                       float* states, float* fin, bool bf16_in, bool park, const Shape& s,
+                       void* stream) {
+  clear_launch_error();
   hipStream_t st = (hipStream_t)stream;
   if (!bf16_in) {
     if (s.dstate == 64) {
       switch (s.chunk) {
-        case 64: return launch_cs_f32<64, 64>(x, B, dt_t, g, states, fin, s, st);
-        case 128: return launch_cs_f32<128, 64>(x, B, dt_t, g, states, fin, s, st);
-        default: return launch_cs_f32<256, 64>(x, B, dt_t, g, states, fin, s, st);
+        case 64: return launch_cs_f32<64, 64>(x, B, dt_t, g, states, fin, park, s, st);
+        case 128: return launch_cs_f32<128, 64>(x, B, dt_t, g, states, fin, park, s, st);
+        default: return launch_cs_f32<256, 64>(x, B, dt_t, g, states, fin, park, s, st);
       }
     }
     switch (s.chunk) {
-      case 64: return launch_cs_f32<64, 128>(x, B, dt_t, g, states, fin, s, st);
-      case 128: return launch_cs_f32<128, 128>(x, B, dt_t, g, states, fin, s, st);
-      default: return launch_cs_f32<256, 128>(x, B, dt_t, g, states, fin, s, st);
+      case 64: return launch_cs_f32<64, 128>(x, B, dt_t, g, states, fin, park, s, st);
+      case 128: return launch_cs_f32<128, 128>(x, B, dt_t, g, states, fin, park, s, st);
+      default: return launch_cs_f32<256, 128>(x, B, dt_t, g, states, fin, park, s, st);
     }
   }
   if (s.dstate == 64) {
     switch (s.chunk) {
-      case 64: return launch_cs<64, 64>(x, B, dt_t, g, states, fin, s, st);
-      case 128: return launch_cs<128, 64>(x, B, dt_t, g, states, fin, s, st);
-      default: return launch_cs<256, 64>(x, B, dt_t, g, states, fin, s, st);
+      case 64: return launch_cs<64, 64>(x, B, dt_t, g, states, fin, park, s, st);
+      case 128: return launch_cs<128, 64>(x, B, dt_t, g, states, fin, park, s, st);
+      default: return launch_cs<256, 64>(x, B, dt_t, g, states, fin, park, s, st);
     }
   }
   switch (s.chunk) {
-    case 64: return launch_cs<64, 128>(x, B, dt_t, g, states, fin, s, st);
-    case 128: return launch_cs<128, 128>(x, B, dt_t, g, states, fin, s, st);
-    default: return launch_cs<256, 128>(x, B, dt_t, g, states, fin, s, st);
+    case 64: return launch_cs<64, 128>(x, B, dt_t, g, states, fin, park, s, st);
+    case 128: return launch_cs<128, 128>(x, B, dt_t, g, states, fin, park, s, st);
+    default: return launch_cs<256, 128>(x, B, dt_t, g, states, fin, park, s, st);
   }
 }
 
 int launch_state_passing(const float* g, const float* init, float* states, float* fin,
-                         const Shape& s, void* stream) {
+                         bool parked, const Shape& s, void* stream) {
+  clear_launch_error();
   hipStream_t st = (hipStream_t)stream;
-  return s.dstate == 64 ? launch_sp<64>(g, init, states, fin, s, st)
-                        : launch_sp<128>(g, init, states, fin, s, st);
+  return s.dstate == 64 ? launch_sp<64>(g, init, states, fin, parked, s, st)
+                        : launch_sp<128>(g, init, states, fin, parked, s, st);
 }
 
 }  // namespace ssd

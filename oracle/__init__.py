@@ -21,22 +21,48 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
-_LIB = os.path.join(_HERE, "libssd_oracle.so")
+# SSD_ORACLE_SANITIZE=1 selects a build with AddressSanitizer and
+# UndefinedBehaviorSanitizer (host code only; the process must preload the
+# sanitizer runtimes, see sanitizer_env()).
+SANITIZE = os.environ.get("SSD_ORACLE_SANITIZE", "") == "1"
+_LIB = os.path.join(_HERE, "libssd_oracle_san.so" if SANITIZE else "libssd_oracle.so")
+SANITIZER_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                   "-fno-omit-frame-pointer", "-g"]
 _lock = threading.Lock()
 _lib = None
 
 
-def build(force: bool = False) -> str:
-    """Compile ssd_oracle.c into libssd_oracle.so with gcc (-O2, OpenMP)."""
-    if (not force and os.path.exists(_LIB)
-            and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC)):
-        return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+def build(force: bool = False, sanitize: bool = SANITIZE) -> str:
+    """Compile ssd_oracle.c into a shared library with gcc (-O2, OpenMP);
+    with `sanitize`, instrumented with ASan and UBSan (-O1)."""
+    lib = os.path.join(_HERE, "libssd_oracle_san.so" if sanitize else "libssd_oracle.so")
+    if (not force and os.path.exists(lib)
+            and os.path.getmtime(lib) >= os.path.getmtime(_SRC)):
+        return lib
+    tmp = lib + ".tmp%d" % os.getpid()
+    opt = ["-O1", *SANITIZER_FLAGS] if sanitize else ["-O2"]
+    cmd = ["gcc", *opt, "-fopenmp", "-fPIC", "-shared", "-std=c99",
            "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def sanitizer_env(base=None) -> dict:
+    """Environment for a process that loads the sanitized oracle: the gcc
+    ASan and UBSan runtimes preloaded, leak checking off (the Python
+    interpreter itself holds memory until exit)."""
+    env = dict(os.environ if base is None else base)
+    libs = []
+    for name in ("libasan.so", "libubsan.so"):
+        p = subprocess.run(["gcc", f"-print-file-name={name}"], capture_output=True,
+                           text=True, check=True).stdout.strip()
+        libs.append(os.path.realpath(p))
+    env["LD_PRELOAD"] = ":".join(libs)
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    env["SSD_ORACLE_SANITIZE"] = "1"
+    return env
 
 
 def _load():

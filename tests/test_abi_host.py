@@ -170,6 +170,11 @@ def test_two_level_entry_points_validate():
     for name in ("g", "st"):
         assert sp(d, **{name: None}) == INV, name
     assert sp(d, init=MISALIGNED) == INV and sp(d, fin=MISALIGNED) == INV
+    # final_state carries P_{nc-1} between the two calls: it may not overlap
+    # the initial state (whole or partial overlap)
+    assert sp(d, init=FAKE, fin=FAKE) == INV
+    assert sp(d, init=ctypes.c_void_p(FAKE.value + 4096), fin=FAKE) == INV
+    assert sp(d, init=FAKE, fin=ctypes.c_void_p(FAKE.value + 16)) == INV
 
 
 def test_gdn_entry_points_validate():

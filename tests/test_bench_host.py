@@ -37,10 +37,34 @@ def test_algorithmic_bytes_of_the_small_layer():
     final = 4 * b * H * P * N
     y = 4 * b * L * H * P                      # fp32 y
     by, fl = bench.algorithmic(w, 4)
-    # stage 1 reads dt and writes g and dt_t
-    assert by["chunk_cumsum"] == 4 * b * L * H + g_dt == 2359296
+    # stage 1 reads dt and writes g; its head-major copy of dt is counted
+    # apart, as a design choice
+    assert by["chunk_cumsum"] == 4 * b * L * H + 4 * b * L * H == 1572864
+    assert bench.design_extra_bytes(w)["chunk_cumsum"] == 4 * b * L * H
     assert by["fwd_pass_state"] == x + bc + g_dt + states + final == 132644864
     # stage 3 also reads C and D
     assert by["compute_out"] == x + 2 * bc + g_dt + states + 4 * H + y == 181928032
     # the state pass's contraction: one multiply-add per (token, head, p, n)
     assert fl["fwd_pass_state"] == 2 * b * L * H * P * N
+
+
+def test_issued_matrix_work_of_the_output_stage():
+    """Issued matrix-instruction work of stage 3, from the kernels' block
+    structure, for the wide fp32 and the large bf16 layers: never below
+    the algorithmic count, and the bf16 form doubles every product with a
+    computed operand (hi + lo)."""
+    import bench
+    from ssd_workloads import WORKLOADS
+    for name in ("wide_fp32", "large_bf16", "small_bf16", "long_bf16"):
+        w = WORKLOADS[name]
+        by, fl = bench.algorithmic(w, 4)
+        iss = bench.issued_mfma_flop(w)
+        assert iss["compute_out"] >= fl["compute_out"], name
+        assert iss["fwd_pass_state"] == (2 if w.dtype == "bf16" else 1) * fl["fwd_pass_state"]
+    # wide fp32: T = 64, 4 row blocks; C S^T 2 T P N per (b, c, h); L'X 10
+    # of 16 blocks; C B^T 10 of 16 blocks once per (b, c, group)
+    w = WORKLOADS["wide_fp32"]
+    b, H, G, P, N, nc = 64, 48, 8, 64, 64, 16
+    per_item = 2 * 64 * P * N + 10 * 16 * 16 * P * 2
+    assert bench.issued_mfma_flop(w)["compute_out"] == \
+        b * nc * H * per_item + b * nc * G * 10 * 16 * 16 * N * 2

@@ -3,14 +3,16 @@
 Small cases compare every output element; they span several tiles, a ragged
 last chunk, grouped B/C and both input types.  The named workloads run at
 full size, in the same launch configuration the benchmark times, and compare
-sampled (batch, head) pairs that the oracle computes one by one.
+every element too, in batches of (batch, head) pairs that the oracle
+computes one batch at a time.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import (assert_close, device_inputs, g_tolerance, log)
+from gpu_util import (assert_close, compare_all_pairs, device_inputs, g_tolerance, log,
+                      pairs_per_batch)
 from ssd_workloads import WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -146,43 +148,33 @@ def test_cumsum_exact_inputs(ssd):
 NAMED = ["tiny_fp32", "small_bf16", "large_bf16", "wide_fp32", "long_bf16"]
 
 
-def _sample_pairs(w, k, seed):
-    n = w.batch * w.nheads
-    rng = np.random.default_rng(seed)
-    picks = {0, n - 1} | set(int(v) for v in rng.integers(0, n, size=k))
-    return sorted(picks)
-
-
 @pytest.mark.parametrize("name", NAMED)
 def test_named_workload_full_size(ssd, name):
+    """Every element of y, states and final at the workload's full size, in
+    the launch configuration the benchmark times, against the oracle (pairs
+    of (batch, head) in batches to bound host memory)."""
     w = WORKLOADS[name]
     log(f"[full] {name}: b={w.batch} L={w.seqlen} H={w.nheads} N={w.dstate} "
         f"G={w.ngroups} T={w.chunk_size} {w.dtype}")
     inp = make_inputs(w)
     dev = device_inputs(inp, w.dtype)
     y, states, final = _run_forward(ssd, dev, w.chunk_size)
-    if name == "tiny_fp32":
-        ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"],
-                             inp["C"], inp["D"], inp["init_state"],
-                             chunk_size=w.chunk_size)
-        assert_close(_np(y), ref["y"], w.dtype, "y")
-        assert_close(_np(states), ref["states"], w.dtype, "states")
-        assert_close(_np(final), ref["final"], w.dtype, "final")
-        return
-    pairs = _sample_pairs(w, 3, seed=len(name))
-    log(f"  sampled (b*H + h) pairs: {pairs}")
-    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
-                         inp["D"], inp["init_state"], chunk_size=w.chunk_size,
-                         pairs=pairs)
-    H = w.nheads
-    ys = np.stack([_np(y[p // H, :, p % H]) for p in pairs])
-    ss = np.stack([_np(states[p // H, p % H]) for p in pairs])
-    fs = np.stack([_np(final[p // H, p % H]) for p in pairs])
-    assert_close(ss, ref["states"], w.dtype, "states (sampled pairs)")
-    assert_close(fs, ref["final"], w.dtype, "final (sampled pairs)")
-    assert_close(ys, ref["y"], w.dtype, "y (sampled pairs)")
-    # properties that hold over every element
-    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(states).all())
+    b, L, H, P, N, nc = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.nchunks
+    # pair-major views of the device outputs: pair = b * H + h
+    yp = y.permute(0, 2, 1, 3).reshape(b * H, L, P)
+    sp = states.reshape(b * H, nc, P, N)
+    fp = final.reshape(b * H, P, N)
+
+    def ref(p0, p1):
+        return oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                              inp["D"], inp["init_state"], chunk_size=w.chunk_size,
+                              pairs=list(range(p0, p1)))
+
+    def got(p0, p1):
+        return {"y": _np(yp[p0:p1]), "states": _np(sp[p0:p1]), "final": _np(fp[p0:p1])}
+
+    compare_all_pairs(ref, got, b * H, pairs_per_batch(w), w.dtype,
+                      ("states", "final", "y"))
     if inp["init_state"] is None:
         assert bool((states[:, :, 0] == 0).all())
     else:

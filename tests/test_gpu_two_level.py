@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_close, device_inputs, log
+from gpu_util import assert_close, compare_all_pairs, device_inputs, log
 from ssd_workloads import WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -168,19 +168,52 @@ def test_state_passing_alone(ssd):
     assert_close(_np(fin), ref["final"], "fp32", "final")
 
 
-def test_two_level_long_sampled(ssd):
-    """The long workload (65536 tokens, 512 chunks) on sampled pairs."""
+def test_two_level_long_full(ssd):
+    """The long workload (65536 tokens, 512 chunks): every element of the
+    states and the final state."""
     w = WORKLOADS["long_bf16"]
     inp = make_inputs(w)
     log(f"[two-level] full size {w.name}")
     dev = device_inputs(inp, "bf16")
     g, dtt = _cumsum(ssd, dev, w)
     states, fin = _two_level(ssd, dev, w, g, dtt)
-    pairs = [0, 13, 31]
+    npairs = w.batch * w.nheads
+    sp = states.reshape(npairs, w.nchunks, 64, w.dstate)
+    fp = fin.reshape(npairs, 64, w.dstate)
+
+    def ref(p0, p1):
+        return oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                              inp["init_state"], chunk_size=w.chunk_size,
+                              pairs=list(range(p0, p1)), want_y=False)
+
+    def got(p0, p1):
+        return {"states": _np(sp[p0:p1]), "final": _np(fp[p0:p1])}
+
+    compare_all_pairs(ref, got, npairs, 16, "bf16", ("states", "final"))
+
+
+@pytest.mark.parametrize("L,T", [(16384, 128), (8192, 64)])
+def test_fwd_pass_state_init_aliases_final(ssd, L, T):
+    """init_state and final_state as one buffer (a sequence continued in
+    place) give the same states and final state as separate buffers: 128
+    chunks of 128 tokens on 4 heads take the two-level form, 128 chunks of
+    64 the one-pass kernel."""
+    w = _wl(1, L, 4, 1, 128, T, True)
+    inp = make_inputs(w, seed=101)
+    log(f"[alias] {w}")
+    dev = device_inputs(inp, "bf16")
+    g, dtt = _cumsum(ssd, dev, w)
+    b, H, nc = w.batch, w.nheads, w.nchunks
+    s1 = torch.empty(b, H, nc, 64, 128, device=DEV)
+    f1 = torch.empty(b, H, 64, 128, device=DEV)
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dtt, g, dev["init_state"], s1, f1, T)
+    s2 = torch.empty_like(s1)
+    both = dev["init_state"].clone()
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dtt, g, both, s2, both, T)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(f1, both)
     ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
-                         inp["init_state"], chunk_size=w.chunk_size, pairs=pairs,
-                         want_y=False)
-    got_s = _np(states).reshape(-1, w.nchunks, 64, w.dstate)[pairs]
-    got_f = _np(fin).reshape(-1, 64, w.dstate)[pairs]
-    assert_close(got_s, ref["states"], "bf16", "states (sampled)")
-    assert_close(got_f, ref["final"], "bf16", "final (sampled)")
+                         inp["init_state"], chunk_size=T, want_y=False)
+    assert_close(_np(s2), ref["states"], "bf16", "states (aliased)")
+    assert_close(_np(both), ref["final"], "bf16", "final (aliased)")
