@@ -191,6 +191,27 @@ ssd_status ssd_forward(const void *x, const float *dt, const float *A,
                        const ssd_dims *dims, void *stream);
 
 /*
+ * ssd_forward without allocation: for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments and results as
+ * ssd_forward minus the workspace; g and dt_t (8 * batch * nheads * seqlen
+ * bytes) go to a scratch array the library holds on each GPU it runs on,
+ * SSD_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU for the life of the process.
+ * Shapes that need more return SSD_ERR_WORKSPACE before any HIP call; use
+ * ssd_forward with a workspace for those.  The call allocates nothing and
+ * calls no allocating routine.  All calls on one GPU share its array, so
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race: order them on one stream.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ssd_status ssd_forward_noalloc(const void *x, const float *dt, const float *A,
+                               const void *B, const void *C, const float *D,
+                               const float *init_state, void *y, float *states,
+                               float *final_state, ssd_dtype in_dtype,
+                               ssd_dtype y_dtype, const ssd_dims *dims,
+                               void *stream);
+
+/*
  * The streaming decode step [P1 "The Mamba-2 Recurrence"; P1 "Why Would a
  * Trading Firm Care About Mamba-2 Kernels?" (at inference the fixed-size
  * state is carried forward and updated per new event); P1 "Kernel 2" (the

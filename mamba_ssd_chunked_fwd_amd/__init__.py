@@ -7,7 +7,7 @@ the current HIP stream.  PyTorch supplies device memory and streams.
 
 Entry points (same names as the C ABI):
   ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_chunk_state, ssd_state_passing,
-  ssd_compute_out, ssd_forward,
+  ssd_compute_out, ssd_forward, ssd_forward_noalloc,
   ssd_decode_step, ssd_causal_conv1d, ssd_gdn_chunk_fwd_h, ssd_gdn_chunk_fwd_o
 and the allocating convenience wrapper ``forward``.
 
@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
     lib.ssd_compute_out.restype = i
     lib.ssd_forward.argtypes = [vp] * 11 + [sz, i, i, dims, vp]
     lib.ssd_forward.restype = i
+    lib.ssd_forward_noalloc.argtypes = [vp] * 10 + [i, i, dims, vp]
+    lib.ssd_forward_noalloc.restype = i
     lib.ssd_decode_step.argtypes = [vp] * 8 + [i, i, dims, vp]
     lib.ssd_decode_step.restype = i
     i64 = ctypes.c_int64
@@ -318,6 +320,41 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
         _ptr(init_state), _ptr(y), _ptr(states), _ptr(final_state),
         _ptr(workspace), nbytes, _dtype_code(x.dtype), _dtype_code(y.dtype),
         ctypes.byref(d), _stream(dev)), "ssd_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def ssd_forward_noalloc(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,
+                        B: torch.Tensor, C: torch.Tensor, D: torch.Tensor,
+                        init_state: Optional[torch.Tensor], y: torch.Tensor,
+                        states: torch.Tensor, final_state: Optional[torch.Tensor],
+                        chunk_size: int) -> None:
+    """``ssd_forward`` without a workspace: g and dt_t live in the library's
+    per-GPU scratch array (NOALLOC_SCRATCH_BYTES), so the call allocates
+    nothing.  Calls that overlap in time on one GPU race on that array."""
+    d = make_dims(x, B, chunk_size)
+    dev = x.device
+    ins = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _check(x, "x", None, ins)
+    bc = (d.batch, d.seqlen, d.ngroups, d.dstate)
+    _check(B, "B", bc, (x.dtype,), dev)
+    _check(C, "C", bc, (x.dtype,), dev)
+    _check(dt, "dt", (d.batch, d.seqlen, d.nheads), f32, dev)
+    _check(A, "A", (d.nheads,), f32, dev)
+    _check(D, "D", (d.nheads,), f32, dev)
+    st_shape = (d.batch, d.nheads, d.headdim, d.dstate)
+    _check(init_state, "init_state", st_shape, f32, dev, optional=True)
+    _check(y, "y", tuple(x.shape), ins, dev)
+    _check(states, "states", (d.batch, d.nheads, nchunks(d), d.headdim,
+                              d.dstate), f32, dev)
+    _check(final_state, "final_state", st_shape, f32, dev, optional=True)
+    _raise(_lib.ssd_forward_noalloc(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(init_state), _ptr(y), _ptr(states), _ptr(final_state),
+        _dtype_code(x.dtype), _dtype_code(y.dtype), ctypes.byref(d), _stream(dev)),
+        "ssd_forward_noalloc")
 
 
 def ssd_decode_step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,

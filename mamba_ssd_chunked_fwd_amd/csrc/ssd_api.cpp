@@ -213,6 +213,24 @@ ssd_status ssd_forward(const void* x, const float* dt, const float* A,
   return from_hip(err);
 }
 
+ssd_status ssd_forward_noalloc(const void* x, const float* dt, const float* A, const void* B,
+                               const void* C, const float* D, const float* init_state, void* y,
+                               float* states, float* final_state, ssd_dtype in_dtype,
+                               ssd_dtype y_dtype, const ssd_dims* dims, void* stream) {
+  ssd::Shape s;
+  const ssd_status st = check_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype) || !ok_dtype(y_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(x) || !ok_ptr(dt) || !ok_ptr(A) || !ok_ptr(B) || !ok_ptr(C) ||
+      !ok_ptr(D) || !ok_ptr(y) || !ok_ptr(states) || !ok_opt(init_state) ||
+      !ok_opt(final_state))
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (ssd_forward_workspace_bytes(dims) > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+  return from_hip(ssd::launch_forward_noalloc(x, dt, A, B, C, D, init_state, y, states,
+                                              final_state, in_dtype == SSD_BF16,
+                                              y_dtype == SSD_BF16, s, stream));
+}
+
 ssd_status ssd_decode_step(const void* x, const float* dt, const float* A,
                            const void* B, const void* C, const float* D, float* state,
                            void* y, ssd_dtype in_dtype, ssd_dtype y_dtype, const ssd_dims* dims,

@@ -6,7 +6,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ssd.h"
+
 namespace ssd {
+
+// Size of the per-device scratch array behind ssd_forward_noalloc (holds g
+// and dt_t: 8 bytes per (batch, token, head)).
+constexpr size_t kNoallocScratchBytes = SSD_NOALLOC_SCRATCH_BYTES;
 
 struct Shape {
   int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
@@ -36,6 +42,13 @@ int launch_chunk_state(const void* x, const void* B, const float* dt_t, const fl
                        void* stream);
 int launch_state_passing(const float* g, const float* init, float* states, float* fin,
                          bool parked, const Shape& s, void* stream);
+
+// ssd_forward with g and dt_t in the library's per-device scratch array;
+// the shape must need at most kNoallocScratchBytes of it.
+int launch_forward_noalloc(const void* x, const float* dt, const float* A, const void* B,
+                           const void* C, const float* D, const float* init_state, void* y,
+                           float* states, float* final_state, bool bf16_in, bool bf16_out,
+                           const Shape& s, void* stream);
 
 int launch_decode_step(const void* x, const float* dt, const float* A, const void* B,
                        const void* C, const float* D, float* state, void* y, bool bf16_in,

@@ -120,6 +120,30 @@ void test_forward() {
   stub::reset();
 }
 
+void test_forward_noalloc() {
+  auto call = [](const ssd_dims* d, ssd_dtype in = SSD_BF16) {
+    return ssd_forward_noalloc(P(1), (const float*)P(2), (const float*)P(3), P(4), P(5),
+                               (const float*)P(6), nullptr, P(7), (float*)P(8), nullptr, in,
+                               SSD_F32, d, nullptr);
+  };
+  stub::reset();
+  const ssd_dims d = dims(2, 300, 4, 64, 128, 2, 128);
+  CHECK(call(&d) == SSD_OK);
+  CHECK(stub::ncalls == 1 && std::strcmp(stub::calls[0].name, "forward_noalloc") == 0);
+  CHECK(stub::calls[0].shape.seqlen == 300 && stub::calls[0].flag[0]);
+  // g and dt_t must fit the per-GPU scratch array: 8 * b * H * L bytes
+  const int64_t fit = (int64_t)(SSD_NOALLOC_SCRATCH_BYTES / 8 / 64);   // b * L with H = 64
+  const ssd_dims at = dims(1, fit, 64, 64, 64, 1, 64);
+  const ssd_dims over = dims(1, fit + 1, 64, 64, 64, 1, 64);
+  CHECK(ssd_forward_workspace_bytes(&at) == SSD_NOALLOC_SCRATCH_BYTES);
+  CHECK(call(&at) == SSD_OK);
+  CHECK(call(&over) == SSD_ERR_WORKSPACE);
+  CHECK(call(&d, (ssd_dtype)3) == SSD_ERR_INVALID_ARGUMENT);
+  CHECK(call(nullptr) == SSD_ERR_INVALID_ARGUMENT);
+  CHECK(stub::ncalls == 2);
+  stub::reset();
+}
+
 void test_stage_entry_points() {
   const ssd_dims d = dims();
   stub::reset();
@@ -215,6 +239,7 @@ int main() {
   test_status_strings();
   test_dims_checks();
   test_forward();
+  test_forward_noalloc();
   test_stage_entry_points();
   test_two_level();
   test_side_entry_points();

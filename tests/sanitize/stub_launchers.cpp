@@ -57,6 +57,11 @@ int launch_state_passing(const float* g, const float* init, float* states, float
                          const Shape& s, void*) {
   return stub::record("state_passing", &s, g, init, states, parked, false);
 }
+int launch_forward_noalloc(const void* x, const float*, const float*, const void*, const void*,
+                           const float*, const float*, void* y, float* states, float*,
+                           bool bf16_in, bool bf16_out, const Shape& s, void*) {
+  return stub::record("forward_noalloc", &s, x, y, states, bf16_in, bf16_out);
+}
 int launch_decode_step(const void* x, const float*, const float*, const void*, const void*,
                        const float*, float* state, void* y, bool bf16_in, bool bf16_out,
                        const Shape& s, void*) {

@@ -42,7 +42,7 @@ def test_every_declared_function_is_exported():
                           "ssd_compute_out", "ssd_forward", "ssd_decode_step",
                           "ssd_causal_conv1d", "ssd_gdn_chunk_fwd_h",
                           "ssd_gdn_chunk_fwd_o", "ssd_chunk_state",
-                          "ssd_state_passing"}
+                          "ssd_state_passing", "ssd_forward_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -250,3 +250,22 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         ssd.forward(x, torch.zeros(1, 64, 2), torch.zeros(2), B, B,
                     torch.zeros(2), chunk_size=64)
+
+
+def test_forward_noalloc_validates():
+    """Rejections happen on the host before any HIP call; shapes whose g and
+    dt_t exceed the per-GPU scratch array get SSD_ERR_WORKSPACE."""
+    def call(d, **o):
+        return lib.ssd_forward_noalloc(
+            o.get("x", FAKE), FAKE, FAKE, FAKE, FAKE, FAKE, o.get("init", None), FAKE, FAKE,
+            o.get("fin", None), o.get("ind", ssd.SSD_BF16), ssd.SSD_F32,
+            ctypes.byref(d) if d is not None else None, None)
+    assert call(None) == INV
+    assert call(dims(), x=None) == INV and call(dims(), x=MISALIGNED) == INV
+    assert call(dims(), ind=4) == INV
+    assert call(dims(headdim=32)) == UNS
+    fit = ssd.NOALLOC_SCRATCH_BYTES // 8 // 64          # tokens with 64 heads
+    assert ssd.workspace_bytes(dims(batch=1, seqlen=fit, nheads=64, ngroups=1)) == \
+        ssd.NOALLOC_SCRATCH_BYTES
+    assert call(dims(batch=1, seqlen=fit + 1, nheads=64, ngroups=1)) == WS
+    assert call(dims(batch=2, seqlen=fit, nheads=64, ngroups=1)) == WS
