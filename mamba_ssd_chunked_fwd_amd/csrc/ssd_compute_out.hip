@@ -381,6 +381,300 @@ __global__ __launch_bounds__(GeoB<T>::NTHR) void compute_out_bf16(
   }
 }
 
+// ------------------------------------------------ fp32 via split bf16
+// fp32 inputs on the bf16 matrix instructions: every operand is split into
+// three bf16 terms, exactly (hi + mid + lo), and each product keeps its six
+// terms of relative size 2^-16 or more (hh, hm, mh, hl, mm, lh), which is
+// fp32 accuracy at 6 x 16 cycles per 32-step of k instead of 8 x 32 with the
+// fp32 instruction.  Same geometry, item order, prefetch and operand layouts
+// as compute_out_bf16: the x tile and the state are staged in LDS as three
+// bf16 planes each, C and B fragments are split in registers, and L' is
+// split where it is formed.
+template <int T, int N, bool YBF16>
+__global__ __launch_bounds__(GeoB<T>::NTHR) void compute_out_f32s(
+    const float* __restrict__ x, const float* __restrict__ Bm,
+    const float* __restrict__ Cm, const float* __restrict__ dt_t,
+    const float* __restrict__ g, const float* __restrict__ states,
+    const float* __restrict__ Dv, void* __restrict__ y, int L, int H, int G,
+    int nc, int items) {
+  using Gm = GeoB<T>;
+  constexpr int NTHR = Gm::NTHR, MB = Gm::MB, NIB = Gm::NIB;
+  constexpr int KN = N / 32;            // k-steps over the state index
+  constexpr int XS = 80;                // x plane row stride (bf16), 64 + 16
+  constexpr int SS = N + 8;             // state plane row stride (bf16)
+  constexpr int XU = T * 16 / NTHR;     // 16-byte fp32 x units per thread
+  constexpr int SU = 16 * N / NTHR;     // 16-byte state units per thread
+  constexpr int NE = MB == 1 ? NIB : NIB + 2;
+  static_assert(XU >= 1 && SU >= 1 && 2 * T <= NTHR, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[3][T * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t ss[3][64 * SS];
+  __shared__ float gs[T], ds[T];
+  __shared__ __attribute__((aligned(16))) float cw[Gm::NW][32];
+
+  int k0, k1;
+  item_range(items, k0, k1);
+  if (k0 >= k1) return;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int hpg = H / G;
+  const uint32_t xbytes = (uint32_t)L * H * kHeadDim * 4;
+  const uint32_t bcbytes = (uint32_t)L * G * N * 4;
+  const rsrc_t drs = make_rsrc(Dv, (uint32_t)H * 4);
+
+  struct Regs {
+    f32x4 x[XU];
+    f32x4 s[SU];
+    float gd, dh;
+  };
+  Regs ra, rb;
+  constexpr int NLOAD = XU + SU + 2;
+  struct Src {
+    rsrc_t xr, sr, gdr;
+    uint32_t xo[XU], gdo;
+    int h;
+  };
+  auto prepare = [&](int k, Src& sc) {
+    const bool live = k < k1;
+    const Item it = decode_item(live ? k : k0, H, nc, hpg);
+    sc.xr = make_rsrc(x + (size_t)it.b * L * H * kHeadDim, live ? xbytes : 0u);
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int e = tid + NTHR * u, row = e >> 4, c4 = e & 15;
+      sc.xo[u] = ((uint32_t)(it.c * T + row) * H + it.h) * (kHeadDim * 4) + 16 * c4;
+    }
+    sc.sr = make_rsrc(states + (((size_t)it.b * H + it.h) * nc + it.c) * kHeadDim * N,
+                      live ? kHeadDim * N * 4u : 0u);
+    const size_t row = ((size_t)it.b * H + it.h) * L;
+    const bool wave_g = __builtin_amdgcn_readfirstlane(tid >> 6) < T / 64;
+    sc.gdr = make_rsrc((wave_g ? g : dt_t) + row, live ? (uint32_t)L * 4 : 0u);
+    sc.gdo = tid < 2 * T ? 4 * (uint32_t)(it.c * T + (tid % T)) : kPastRange;
+    sc.h = it.h;
+  };
+  auto issue_slot = [&](int j, const Src& sc, Regs& r) {
+    if (j < XU) {
+      r.x[j] = load_f32x4(sc.xr, sc.xo[j]);
+    } else if (j < XU + SU) {
+      r.s[j - XU] = load_f32x4(sc.sr, 16 * (tid + NTHR * (j - XU)));
+    } else if (j == XU + SU) {
+      r.gd = load_f32(sc.gdr, sc.gdo);
+    } else {
+      r.dh = load_f32(drs, 4 * sc.h);
+    }
+  };
+  auto commit = [&](const Regs& r) {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) {
+      const int e = tid + NTHR * u, row = e >> 4, c4 = e & 15;
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3_bf16(r.x[u][0], r.x[u][1], h0, m0, l0);
+      split3_bf16(r.x[u][2], r.x[u][3], h1, m1, l1);
+      const int o = row * XS + 4 * c4;
+      *(u32x2*)(xs[0] + o) = (u32x2){h0, h1};
+      *(u32x2*)(xs[1] + o) = (u32x2){m0, m1};
+      *(u32x2*)(xs[2] + o) = (u32x2){l0, l1};
+    }
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int e = tid + NTHR * u, row = e / (N / 4), col = 4 * (e % (N / 4));
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3_bf16(r.s[u][0], r.s[u][1], h0, m0, l0);
+      split3_bf16(r.s[u][2], r.s[u][3], h1, m1, l1);
+      const int o = row * SS + col;
+      *(u32x2*)(ss[0] + o) = (u32x2){h0, h1};
+      *(u32x2*)(ss[1] + o) = (u32x2){m0, m1};
+      *(u32x2*)(ss[2] + o) = (u32x2){l0, l1};
+    }
+    if (tid < T) {
+      gs[tid] = r.gd;
+    } else if (tid < 2 * T) {
+      ds[tid - T] = r.gd;
+    }
+  };
+  // the six products of a split pair: acc += a * b to fp32 accuracy
+  auto mfma6 = [](const u32x4 (&a)[3], const u32x4 (&b)[3], f32x4 acc) {
+    acc = mfma_bf16(a[0], b[0], acc);
+    acc = mfma_bf16(a[0], b[1], acc);
+    acc = mfma_bf16(a[1], b[0], acc);
+    acc = mfma_bf16(a[0], b[2], acc);
+    acc = mfma_bf16(a[1], b[1], acc);
+    acc = mfma_bf16(a[2], b[0], acc);
+    return acc;
+  };
+  // eight consecutive fp32 values split into three bf16 fragments
+  auto split8 = [](const f32x4& v0, const f32x4& v1, u32x4 (&f)[3]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t h, m, l;
+      split3_bf16(v0[2 * q], v0[2 * q + 1], h, m, l);
+      f[0][q] = h; f[1][q] = m; f[2][q] = l;
+      split3_bf16(v1[2 * q], v1[2 * q + 1], h, m, l);
+      f[0][2 + q] = h; f[1][2 + q] = m; f[2][2 + q] = l;
+    }
+  };
+
+  // ---- C fragments (k = state index 32kk + 8lq + e, three planes) and
+  //      C B^T blocks, cb[entry][rr] = (C B^T)[i][16 jb + 4 lq + rr]
+  u32x4 cf[MB][KN][3];
+  f32x4 cb[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) cb[e] = (f32x4){0, 0, 0, 0};
+  auto form_cb = [&](const Item& it) {
+    const rsrc_t cr = make_rsrc(Cm + (size_t)it.b * L * G * N, bcbytes);
+    const rsrc_t br = make_rsrc(Bm + (size_t)it.b * L * G * N, bcbytes);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int i = 16 * row_block_b<T>(wave, m) + lr;
+      const uint32_t off = ((uint32_t)(it.c * T + i) * G + it.grp) * (N * 4) + 32 * lq;
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk)
+        split8(load_f32x4(cr, off + 128 * kk), load_f32x4(cr, off + 128 * kk + 16), cf[m][kk]);
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int ib = row_block_b<T>(wave, m);
+#pragma unroll
+      for (int k = 0; k < NIB; ++k) {
+        if (k <= ib) {
+          const uint32_t off =
+              ((uint32_t)(it.c * T + 16 * k + lr) * G + it.grp) * (N * 4) + 32 * lq;
+          f32x4 acc = (f32x4){0, 0, 0, 0};
+#pragma unroll
+          for (int kk = 0; kk < KN; ++kk) {
+            u32x4 bf[3];
+            split8(load_f32x4(br, off + 128 * kk), load_f32x4(br, off + 128 * kk + 16), bf);
+            acc = mfma6(bf, cf[m][kk], acc);
+          }
+          if (m == 0) {
+            if (k < NE) cb[k] = acc;
+          } else {
+            if (NE - 1 - k >= 0) cb[NE - 1 - k] = acc;
+          }
+        }
+      }
+    }
+  };
+
+  // Two items of prefetch: the loads of items k0 and k0 + 1 go out first;
+  // item k is committed from its register set, which then takes the loads
+  // of item k + 2 while item k is computed.
+  {
+    Src sc;
+    prepare(k0, sc);
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) issue_slot(j, sc, ra);
+    prepare(k0 + 1, sc);
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) issue_slot(j, sc, rb);
+  }
+  int key = -1;
+  auto body = [&](int k, Regs& r) {
+    const Item it = decode_item(k, H, nc, hpg);
+    const int nkey = (it.b * nc + it.c) * G + it.grp;
+    if (nkey != key) {
+      form_cb(it);
+      key = nkey;
+    }
+    __syncthreads();  // the previous item's LDS reads are done
+    commit(r);
+    const float Dh = r.dh;
+    Src nxt;
+    prepare(k + 2, nxt);
+    __syncthreads();
+
+    const int t0 = it.c * T;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int ib = row_block_b<T>(wave, m);
+      const int i = 16 * ib + lr;
+      // Y^T = S C^T (both split), then column i scaled by 2^{g_i}
+      f32x4 yacc[4];
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) yacc[pb] = (f32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk) {
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) {
+          if (m == 0 && 4 * kk + pb < NLOAD) issue_slot(4 * kk + pb, nxt, r);
+          const int off = (16 * pb + lr) * SS + 32 * kk + 8 * lq;
+          const u32x4 sa[3] = {*(const u32x4*)(ss[0] + off), *(const u32x4*)(ss[1] + off),
+                               *(const u32x4*)(ss[2] + off)};
+          yacc[pb] = mfma6(sa, cf[m][kk], yacc[pb]);
+        }
+      }
+      if (m == 0) {
+#pragma unroll
+        for (int j = 4 * KN; j < NLOAD; ++j) issue_slot(j, nxt, r);
+      }
+      const float gi = gs[i];
+      const float ei = exp2_hw(gi);
+#pragma unroll
+      for (int pb = 0; pb < 4; ++pb) yacc[pb] *= ei;
+
+      // Y^T += X^T L'^T over 32-token k-steps, the decay factored below the
+      // diagonal exactly as in compute_out_bf16
+      const bool row_in = t0 + i < L;
+#pragma unroll
+      for (int s = 0; s < NE / 2; ++s) {
+        if (2 * s <= ib) {
+          const int e0 = m == 0 ? 2 * s : NE - 1 - 2 * s;
+          const int e1 = m == 0 ? 2 * s + 1 : NE - 2 - 2 * s;
+          float v[8];
+          if (2 * s + 2 <= ib) {
+            const float ge = gs[32 * s + 31];
+            const int jl = 32 * s + (lane & 31);
+            const float cl = exp2_hw(ge - gs[jl]) * ds[jl];
+            if (lane < 32) cw[wave][lane] = cl;
+            const float ai = row_in ? exp2_hw(gi - ge) : 0.0f;
+            const f32x4 c0 = *(const f32x4*)(&cw[wave][4 * lq]);
+            const f32x4 c1 = *(const f32x4*)(&cw[wave][16 + 4 * lq]);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              v[rr] = cb[e0][rr] * (c0[rr] * ai);
+              v[4 + rr] = cb[e1][rr] * (c1[rr] * ai);
+            }
+          } else {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const f32x4 cbv = half ? cb[e1] : cb[e0];
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int j = 32 * s + 16 * half + 4 * lq + rr;
+                float w = cbv[rr] * exp2_hw(gi - gs[j]) * ds[j];
+                if (j == i) w += Dh;
+                v[4 * half + rr] = j <= i ? w : 0.0f;
+              }
+            }
+          }
+          u32x4 lf[3];
+          split8((f32x4){v[0], v[1], v[2], v[3]}, (f32x4){v[4], v[5], v[6], v[7]}, lf);
+          const int xo = (32 * s + 4 * lq + (lr >> 2)) * XS + 4 * (lr & 3);
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb) {
+            u32x4 xa[3];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+              const u32x2 a0 = lds_read_tr16(xs[q] + xo + 16 * pb);
+              const u32x2 a1 = lds_read_tr16(xs[q] + xo + 16 * XS + 16 * pb);
+              xa[q] = (u32x4){a0[0], a0[1], a1[0], a1[1]};
+            }
+            yacc[pb] = mfma6(xa, lf, yacc[pb]);
+          }
+        }
+      }
+      if (t0 + i < L) {
+        const size_t off = (((size_t)it.b * L + t0 + i) * H + it.h) * kHeadDim + 4 * lq;
+#pragma unroll
+        for (int pb = 0; pb < 4; ++pb) store_y<YBF16>(y, off + 16 * pb, yacc[pb]);
+      }
+    }
+  };
+  for (int k = k0; k < k1; k += 2) {
+    body(k, ra);
+    if (k + 1 < k1) body(k + 1, rb);
+  }
+}
+
 // ---------------------------------------------------------------- fp32 path
 // k-map over the state index n for v_mfma_f32_16x16x4_f32: step (u, v)
 // gives lane group lq the index 16u + 4lq + v; over tokens j: step (jb, rr)
@@ -583,17 +877,27 @@ int launch_t(const void* x, const void* B, const void* C, const float* dt_t,
   const int nc = (int)s.nchunks();
   const int L = (int)s.seqlen, H = (int)s.nheads, G = (int)s.ngroups;
   const int items = (int)(s.batch * nc * s.nheads);
-  const void* kern = BF16 ? (const void*)compute_out_bf16<T, N, YBF16>
-                          : (const void*)compute_out_f32<T, N, YBF16>;
+  // fp32 inputs: the split-bf16 kernel for chunks of 64 and 128 tokens (its
+  // three x planes of 256 tokens would not fit the LDS beside the state)
+  constexpr bool SPLIT = !BF16 && T <= 128;
+  constexpr int NTHR_K = SPLIT ? GeoB<T>::NTHR : NTHR;
+  const void* kern;
+  if constexpr (BF16) kern = (const void*)compute_out_bf16<T, N, YBF16>;
+  else if constexpr (SPLIT) kern = (const void*)compute_out_f32s<T, N, YBF16>;
+  else kern = (const void*)compute_out_f32<T, N, YBF16>;
   // the persistent grid: as many workgroups as are resident on the device
   static PerDeviceInt resident;
-  const int slots = resident.get([&](int dev) { return resident_slots(kern, NTHR, dev); });
+  const int slots = resident.get([&](int dev) { return resident_slots(kern, NTHR_K, dev); });
   if (slots <= 0) return (int)hipErrorInvalidDevice;
   const unsigned grid = (unsigned)(items < slots ? items : slots);
   if constexpr (BF16) {
     hipLaunchKernelGGL((compute_out_bf16<T, N, YBF16>), dim3(grid), dim3(NTHR), 0, st,
                        (const uint16_t*)x, (const uint16_t*)B, (const uint16_t*)C, dt_t, g,
                        states, D, y, L, H, G, nc, items);
+  } else if constexpr (SPLIT) {
+    hipLaunchKernelGGL((compute_out_f32s<T, N, YBF16>), dim3(grid), dim3(NTHR_K), 0, st,
+                       (const float*)x, (const float*)B, (const float*)C, dt_t, g, states,
+                       D, y, L, H, G, nc, items);
   } else {
     hipLaunchKernelGGL((compute_out_f32<T, N, YBF16>), dim3(grid), dim3(NTHR), 0, st,
                        (const float*)x, (const float*)B, (const float*)C, dt_t, g, states,

@@ -96,6 +96,22 @@ __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi,
   lo = pack_bf16(a - bf16_lo(hi), b - bf16_hi(hi));
 }
 
+// Three-term bf16 split of fp32 values, exact: v = hi + mid + lo.  hi is v
+// rounded to bf16; v - hi is exact in fp32 and keeps at most 16 significant
+// bits, mid takes the top 8 of them, and the remaining at most 8 bits fit lo
+// exactly.  (Values near the bottom of the fp32 range, where bf16 goes
+// subnormal, are the exception; their products are far below fp32
+// resolution of any sum they join.)  The product of two split values, kept
+// to its six terms of relative size 2^-16 or more, is exact to about 2^-23:
+// fp32 accuracy from bf16 matrix instructions.
+__device__ __forceinline__ void split3_bf16(float a, float b, uint32_t& hi, uint32_t& mid,
+                                            uint32_t& lo) {
+  hi = pack_bf16(a, b);
+  const float ra = a - bf16_lo(hi), rb = b - bf16_hi(hi);
+  mid = pack_bf16(ra, rb);
+  lo = pack_bf16(ra - bf16_lo(mid), rb - bf16_hi(mid));
+}
+
 __device__ __forceinline__ u32x4 make_u32x4(const uint32_t (&a)[4]) {
   return (u32x4){a[0], a[1], a[2], a[3]};
 }

@@ -59,6 +59,14 @@ SMALL = [
     _wl("bf16_T128_N128_strong_decay", "bf16", 2, 300, 4, 2, 128, 128, True, 1.0, (2.0, 3.0)),
     _wl("bf16_T256_N64_weak_decay_init", "bf16", 1, 900, 3, 1, 64, 256, True, -4.0, (-6.0, -5.0)),
     _wl("fp32_T64_N128_strong_decay", "fp32", 2, 200, 3, 3, 128, 64, False, 1.0, (2.0, 3.0)),
+    # fp32 shapes with enough (batch, head) pairs for the state-pass kernel
+    # whose workgroups share B among 3 or 2 heads of a group
+    _wl("fp32_T64_N64_3head_shared_B_ragged_init", "fp32", 128, 70, 6, 2, 64, 64, True,
+        -1.0, (-1.0, 2.0)),
+    _wl("fp32_T128_N128_2head_shared_B", "fp32", 128, 300, 4, 2, 128, 128, False),
+    _wl("fp32_T256_N128_3head_shared_B_ragged", "fp32", 86, 260, 9, 3, 128, 256, True),
+    _wl("fp32_T64_N64_3head_shared_B_one_chunk", "fp32", 64, 64, 12, 2, 64, 64, False,
+        -1.0, (-1.0, 2.0)),
 ]
 
 
