@@ -93,28 +93,39 @@ def design_extra_bytes(w) -> dict:
     return {"chunk_cumsum": 4 * w.batch * w.seqlen * w.nheads}
 
 
+def mfma_kind(w) -> dict:
+    """The matrix instruction each stage issues: bf16 (16x16x32) or fp32
+    (16x16x4).  fp32 inputs run stage 3 on bf16 instructions (three-term
+    splits) for chunks of up to 128 tokens."""
+    out_bf16 = w.dtype == "bf16" or w.chunk_size <= 128
+    return {"fwd_pass_state": "bf16" if w.dtype == "bf16" else "fp32",
+            "compute_out": "bf16" if out_bf16 else "fp32"}
+
+
 def issued_mfma_flop(w) -> dict:
     """Matrix-instruction work the kernels issue, from their structure:
-    causal blocks on or below the diagonal in 16-row (and, for bf16 L'X,
-    32-token) steps, and two instructions (bf16 hi + lo) for every computed
-    fp32 operand with bf16 inputs.  C B^T is counted once per (batch, chunk,
-    group)."""
+    causal blocks on or below the diagonal in 16-row (and, on bf16
+    instructions, 32-token) steps; with bf16 inputs, two instructions (hi +
+    lo) for every product with a computed fp32 operand; with fp32 inputs on
+    bf16 instructions, six per product (three-term splits of both
+    operands).  C B^T is counted once per (batch, chunk, group)."""
     b, L, H, P, N, G, T = (w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
                            w.ngroups, w.chunk_size)
     nc = w.nchunks
     nib = T // 16
+    lx32 = sum(ib // 2 + 1 for ib in range(nib)) * 32 * 16 * P * 2   # 32-token k-steps
+    lx16 = sum(ib + 1 for ib in range(nib)) * 16 * 16 * P * 2        # 16-token blocks
+    cb = sum(ib + 1 for ib in range(nib)) * 16 * 16 * N * 2
     if w.dtype == "bf16":
-        cs = 2 * (2 * T * P * N)                                  # C S^T, hi + lo
-        lx = sum(ib // 2 + 1 for ib in range(nib)) * 32 * 16 * P * 2 * 2
-        cb = sum(ib + 1 for ib in range(nib)) * 16 * 16 * N * 2
+        out = b * nc * H * (2 * 2 * T * P * N + 2 * lx32) + b * nc * G * cb
         a2 = 2 * (2 * b * L * H * P * N)                          # P^T: w o x hi + lo
-    else:
-        cs = 2 * T * P * N
-        lx = sum(ib + 1 for ib in range(nib)) * 16 * 16 * P * 2
-        cb = sum(ib + 1 for ib in range(nib)) * 16 * 16 * N * 2
+    elif mfma_kind(w)["compute_out"] == "bf16":
+        out = 6 * (b * nc * H * (2 * T * P * N + lx32) + b * nc * G * cb)
         a2 = 2 * b * L * H * P * N
-    return {"fwd_pass_state": a2,
-            "compute_out": b * nc * H * (cs + lx) + b * nc * G * cb}
+    else:
+        out = b * nc * H * (2 * T * P * N + lx16) + b * nc * G * cb
+        a2 = 2 * b * L * H * P * N
+    return {"fwd_pass_state": a2, "compute_out": out}
 
 
 def source_sha(stage: str) -> str:
@@ -264,7 +275,7 @@ class WorkloadRun:
         """The configs-map entry: tokens/s, per-stage microseconds, HBM
         fractions and the output stage's matrix-core fractions."""
         w = self.w
-        peak_tf = BF16_MFMA_TFLOPS if w.dtype == "bf16" else FP32_MFMA_TFLOPS
+        kind = mfma_kind(w)
         issued = issued_mfma_flop(w)
         stages = {}
         for n in STEP_KERNELS:
@@ -278,13 +289,18 @@ class WorkloadRun:
                 e["hbm_frac_with_extra"] = round(
                     (self.by[n] + extra) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
             if n in issued:
+                peak_tf = BF16_MFMA_TFLOPS if kind[n] == "bf16" else FP32_MFMA_TFLOPS
                 tf_alg = self.fl[n] / (ms * 1e-3) / 1e12
                 tf_iss = issued[n] / (ms * 1e-3) / 1e12
                 e["alg_TFLOP_per_s"] = round(tf_alg, 2)
                 e["issued_TFLOP_per_s"] = round(tf_iss, 2)
+                e["mfma_instruction"] = kind[n]
                 e["mfma_peak_TFLOP_per_s"] = peak_tf
                 e["mfma_alg_frac"] = round(tf_alg / peak_tf, 4)
                 e["mfma_issued_frac"] = round(tf_iss / peak_tf, 4)
+                rec = committed_profile(w.name, n, "mfma") if n == "compute_out" else None
+                if rec is not None:
+                    e["mfma_busy_frac_counters"] = round(rec["mfma_busy_frac"], 4)
             stages[n] = e
         step_ms = dur["ssd_forward"]
         step_bytes = sum(self.by[n] for n in STEP_KERNELS)
@@ -512,9 +528,6 @@ def main() -> int:
     dom = max(STEP_KERNELS, key=lambda n: stages[n]["us"])
     achieved = stages[dom]["GB_per_s"]
     traffic_rec = committed_profile(w.name, dom, "traffic")
-    mfma_rec = committed_profile(w.name, "compute_out", "mfma")
-    if mfma_rec is not None:
-        stages["compute_out"]["mfma_busy_frac_counters"] = mfma_rec.get("mfma_busy_frac")
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),

@@ -61,10 +61,13 @@ def test_issued_matrix_work_of_the_output_stage():
         iss = bench.issued_mfma_flop(w)
         assert iss["compute_out"] >= fl["compute_out"], name
         assert iss["fwd_pass_state"] == (2 if w.dtype == "bf16" else 1) * fl["fwd_pass_state"]
-    # wide fp32: T = 64, 4 row blocks; C S^T 2 T P N per (b, c, h); L'X 10
-    # of 16 blocks; C B^T 10 of 16 blocks once per (b, c, group)
+    # wide fp32 on bf16 instructions (three-term splits, six products):
+    # T = 64, 4 row blocks; C S^T 2 T P N per (b, c, h); L'X in 32-token
+    # steps, 1 + 1 + 2 + 2 of them over the row blocks; C B^T 10 of 16 blocks
+    # once per (b, c, group)
     w = WORKLOADS["wide_fp32"]
+    assert bench.mfma_kind(w) == {"fwd_pass_state": "fp32", "compute_out": "bf16"}
     b, H, G, P, N, nc = 64, 48, 8, 64, 64, 16
-    per_item = 2 * 64 * P * N + 10 * 16 * 16 * P * 2
+    per_item = 2 * 64 * P * N + 6 * 32 * 16 * P * 2
     assert bench.issued_mfma_flop(w)["compute_out"] == \
-        b * nc * H * per_item + b * nc * G * 10 * 16 * 16 * N * 2
+        6 * (b * nc * H * per_item + b * nc * G * 10 * 16 * 16 * N * 2)
