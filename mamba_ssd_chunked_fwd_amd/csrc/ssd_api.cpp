@@ -205,11 +205,8 @@ ssd_status ssd_forward(const void* x, const float* dt, const float* A,
   const bool bf16 = in_dtype == SSD_BF16;
   int err = ssd::launch_chunk_cumsum(dt, A, g, dt_t, s, stream);
   if (err == 0)
-    err = ssd::launch_fwd_pass_state(x, B, dt_t, g, init_state, states,
-                                     final_state, bf16, s, stream);
-  if (err == 0)
-    err = ssd::launch_compute_out(x, B, C, dt_t, g, states, D, y, bf16,
-                                  y_dtype == SSD_BF16, s, stream);
+    err = ssd::launch_state_and_out(x, B, C, dt_t, g, D, init_state, states, final_state, y,
+                                    bf16, y_dtype == SSD_BF16, s, stream);
   return from_hip(err);
 }
 

@@ -55,10 +55,8 @@ int launch_forward_noalloc(const void* x, const float* dt, const float* A, const
   float* dt_t = g + n;
   int err = launch_chunk_cumsum(dt, A, g, dt_t, s, stream);
   if (err == 0)
-    err = launch_fwd_pass_state(x, B, dt_t, g, init_state, states, final_state, bf16_in, s,
-                                stream);
-  if (err == 0)
-    err = launch_compute_out(x, B, C, dt_t, g, states, D, y, bf16_in, bf16_out, s, stream);
+    err = launch_state_and_out(x, B, C, dt_t, g, D, init_state, states, final_state, y, bf16_in,
+                               bf16_out, s, stream);
   return err;
 }
 

@@ -32,6 +32,15 @@ int launch_compute_out(const void* x, const void* B, const void* C,
                        const float* D, void* y, bool bf16_in, bool bf16_out,
                        const Shape& s, void* stream);
 
+// Stages 2 and 3 of ssd_forward: the fused single-pass kernel where it
+// applies (fp32 inputs, 64-token chunks, N = 64, at least one (b, head pair)
+// per compute unit), otherwise launch_fwd_pass_state then
+// launch_compute_out.  Outputs are the same either way.
+int launch_state_and_out(const void* x, const void* B, const void* C, const float* dt_t,
+                         const float* g, const float* D, const float* init_state, float* states,
+                         float* final_state, void* y, bool bf16_in, bool bf16_out,
+                         const Shape& s, void* stream);
+
 // The two-level form of stage 2 (chunk_state writes each chunk's zero-state
 // contribution into the slot of the state it feeds; state_passing turns the
 // slots into the states in place).  With park / parked, the last chunk's

@@ -98,18 +98,17 @@ void test_forward() {
         SSD_ERR_INVALID_ARGUMENT);
   CHECK(fwd(nullptr, P(20), need) == SSD_ERR_INVALID_ARGUMENT);
   CHECK(stub::ncalls == 0);
-  // a valid call: the three stages in order, g and dt_t split from the
+  // a valid call: stage 1, then stages 2 and 3, g and dt_t split from the
   // workspace, the dtype flags passed through
   float* ws = (float*)P(20);
   CHECK(fwd(&d, ws, need, SSD_BF16, SSD_BF16, (const float*)P(9), (float*)P(9)) == SSD_OK);
-  CHECK(stub::ncalls == 3);
+  CHECK(stub::ncalls == 2);
   CHECK(std::strcmp(stub::calls[0].name, "chunk_cumsum") == 0);
-  CHECK(std::strcmp(stub::calls[1].name, "fwd_pass_state") == 0);
-  CHECK(std::strcmp(stub::calls[2].name, "compute_out") == 0);
+  CHECK(std::strcmp(stub::calls[1].name, "state_and_out") == 0);
   CHECK(stub::calls[0].p[1] == ws && stub::calls[0].p[2] == ws + 2 * 4 * 300);
-  CHECK(stub::calls[1].p[1] == ws && stub::calls[1].flag[0]);
-  CHECK(stub::calls[2].p[0] == ws + 2 * 4 * 300 && stub::calls[2].flag[0] &&
-        stub::calls[2].flag[1]);
+  CHECK(stub::calls[1].p[0] == ws + 2 * 4 * 300 && stub::calls[1].p[1] == ws &&
+        stub::calls[1].p[2] == P(8));
+  CHECK(stub::calls[1].flag[0] && stub::calls[1].flag[1]);
   CHECK(stub::calls[1].shape.seqlen == 300 && stub::calls[1].shape.chunk == 128 &&
         stub::calls[1].shape.nchunks() == 3 && stub::calls[1].shape.ngroups == 2);
   // a failing launch stops the sequence and maps to SSD_ERR_HIP

@@ -49,6 +49,11 @@ int launch_compute_out(const void* x, const void*, const void*, const float* dt_
   (void)x;
   return stub::record("compute_out", &s, dt_t, g, y, bf16_in, bf16_out);
 }
+int launch_state_and_out(const void*, const void*, const void*, const float* dt_t,
+                         const float* g, const float*, const float*, float* states, float*,
+                         void*, bool bf16_in, bool bf16_out, const Shape& s, void*) {
+  return stub::record("state_and_out", &s, dt_t, g, states, bf16_in, bf16_out);
+}
 int launch_chunk_state(const void* x, const void*, const float*, const float*, float* states,
                        float* fin, bool bf16_in, bool park, const Shape& s, void*) {
   return stub::record("chunk_state", &s, x, states, fin, bf16_in, park);

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+from closed_forms import rel_err
 from gpu_util import (assert_close, compare_all_pairs, device_inputs, g_tolerance, log,
                       pairs_per_batch)
 from ssd_workloads import WORKLOADS, Workload, make_inputs
@@ -67,6 +68,16 @@ SMALL = [
     _wl("fp32_T256_N128_3head_shared_B_ragged", "fp32", 86, 260, 9, 3, 128, 256, True),
     _wl("fp32_T64_N64_3head_shared_B_one_chunk", "fp32", 64, 64, 12, 2, 64, 64, False,
         -1.0, (-1.0, 2.0)),
+    # fp32, 64-token chunks, N 64, at least one (batch, head pair) per compute
+    # unit: ssd_forward runs stages 2 and 3 as one fused pass (two heads per
+    # workgroup where the group size is even, one where it is odd)
+    _wl("fp32_T64_N64_fused_pairs_ragged_init", "fp32", 48, 300, 12, 2, 64, 64, True,
+        -1.0, (-1.0, 2.0)),
+    _wl("fp32_T64_N64_fused_single_heads", "fp32", 32, 200, 9, 3, 64, 64, False,
+        -1.0, (-1.0, 2.0)),
+    _wl("fp32_T64_N64_fused_two_pairs_per_workgroup_init", "fp32", 128, 130, 8, 1, 64, 64, True),
+    _wl("fp32_T64_N64_fused_weak_decay_short", "fp32", 96, 40, 6, 3, 64, 64, True,
+        -4.0, (-6.0, -5.0)),
 ]
 
 
@@ -303,6 +314,91 @@ def test_forward_equals_stage_calls(ssd):
     ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dt_t, g, s2, dev["D"], y2, T)
     torch.cuda.synchronize()
     assert torch.equal(s2, states) and torch.equal(f2, final) and torch.equal(y2, y)
+
+
+def _fused_case(seed, init=True, dt_shift=-1.0, a=(-1.0, 2.0), H=14, G=7):
+    # 40 x 14 heads in groups of 2: 280 (batch, head pair) workgroups
+    w = _wl("fused_check", "fp32", 40, 250, H, G, 64, 64, init, dt_shift, a)
+    return w, make_inputs(w, seed=seed)
+
+
+# fused pass against the two-kernel path on the same g: both sum the same
+# fp32 products in different orders (measured 2e-6 and below)
+FUSED_VS_STAGES_TOL = 2e-5
+
+
+@pytest.mark.parametrize("regime", ["moderate_decay_pairs", "extreme_decay_single_heads"])
+def test_fused_forward_matches_stage_calls(ssd, regime):
+    """The fused pass of ssd_forward and the separate stage-2 and stage-3
+    kernels agree to fp32 rounding (they sum in different orders).
+
+    The extreme regime (A dt from about -10 to -26 per token) makes |g| reach
+    thousands within a chunk, where fp32 keeps g to an absolute 2^-24 |g|:
+    the stage-1 rounding then moves decay factors by about 1e-4 relative on
+    either path, which is why this regime is compared path to path, with the
+    final state (a sum the last tokens dominate) against the oracle."""
+    if regime == "moderate_decay_pairs":
+        w, inp = _fused_case(31)
+    else:
+        w, inp = _fused_case(34, init=False, dt_shift=1.0, a=(2.0, 3.0), H=9, G=3)
+    log(f"[fused] {regime} {w}")
+    dev = device_inputs(inp, "fp32")
+    T = w.chunk_size
+    y, states, final = _run_forward(ssd, dev, T)
+    b, L, H = w.batch, w.seqlen, w.nheads
+    g = torch.empty(b, H, L, device=DEV)
+    dt_t = torch.empty(b, H, L, device=DEV)
+    s2 = torch.empty_like(states)
+    f2 = torch.empty_like(final)
+    y2 = torch.empty_like(y)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, dt_t, T)
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dt_t, g, dev["init_state"], s2, f2, T)
+    ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dt_t, g, s2, dev["D"], y2, T)
+    torch.cuda.synchronize()
+    for what, a, b_ in (("states", states, s2), ("final", final, f2), ("y", y, y2)):
+        assert bool(torch.isfinite(a).all())
+        e = rel_err(_np(a), _np(b_))
+        log(f"  {what}: fused vs stages rel(RMS-floored)={e:.3e}")
+        assert e <= FUSED_VS_STAGES_TOL, (what, e)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=T, want_y=False)
+    assert_close(_np(final), ref["final"], "fp32", "final (fused)")
+
+
+def test_fused_forward_init_aliases_final(ssd):
+    """ssd_forward on the fused path with init_state and final_state as one
+    buffer gives what separate buffers give."""
+    w, inp = _fused_case(32)
+    dev = device_inputs(inp, "fp32")
+    T = w.chunk_size
+    b, L, H, nc = w.batch, w.seqlen, w.nheads, w.nchunks
+    ws = torch.empty(ssd.workspace_bytes(ssd.make_dims(dev["x"], dev["B"], T)),
+                     dtype=torch.uint8, device=DEV)
+    outs = []
+    for alias in (False, True):
+        y = torch.empty_like(dev["x"])
+        st = torch.empty(b, H, nc, 64, 64, device=DEV)
+        init = dev["init_state"].clone()
+        fin = init if alias else torch.empty_like(init)
+        ssd.ssd_forward(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], init,
+                        y, st, fin, ws, T)
+        torch.cuda.synchronize()
+        outs.append((y, st, fin))
+    for a, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a, b_)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                         inp["init_state"], chunk_size=T)
+    assert_close(_np(outs[1][2]), ref["final"], "fp32", "final (aliased)")
+
+
+def test_fused_forward_bf16_output(ssd):
+    w, inp = _fused_case(33, init=False)
+    dev = device_inputs(inp, "fp32")
+    y, _, _ = _run_forward(ssd, dev, w.chunk_size, y_dtype=torch.bfloat16)
+    assert y.dtype == torch.bfloat16
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["init_state"], chunk_size=w.chunk_size)
+    assert_close(_np(y), ref["y"], "fp32", "bf16 y (fused)", y_bf16=True)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
