@@ -87,13 +87,33 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) {
   return __uint_as_float(w & 0xFFFF0000u);
 }
 
+// c - h_lo and c - h_hi for the two bf16 halves of h, as fp32, with the bf16
+// dot product (v_dot2c_f32_bf16, c + h . m with m = (-1, 0) or (0, -1)): one
+// instruction instead of an unpack and a subtraction, and exact wherever the
+// difference is representable in fp32, as it is in the splits below.  The
+// multiplier pairs are held in scalar registers: the compiler would encode
+// (-1, 0) as the inline constant -1.0, which the hardware reads as the fp32
+// bit pattern, i.e. the pair (0, -1), and the first half would come out wrong.
+__device__ __forceinline__ float sub_bf16_lo(float c, uint32_t h) {
+  uint32_t m = 0x0000BF80u;   // (-1, 0)
+  asm("" : "+s"(m));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h),
+                                         __builtin_bit_cast(bf16x2, m), c, false);
+}
+__device__ __forceinline__ float sub_bf16_hi(float c, uint32_t h) {
+  uint32_t m = 0xBF800000u;   // (0, -1)
+  asm("" : "+s"(m));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h),
+                                         __builtin_bit_cast(bf16x2, m), c, false);
+}
+
 // Two-term bf16 split of fp32 values: v ~= hi + lo with |v - hi - lo| about
 // 2^-17 |v|.  A product with an exact bf16 operand then costs two bf16 matrix
 // instructions and keeps ~16 mantissa bits, which the fp32 accumulate keeps.
 __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi,
                                            uint32_t& lo) {
   hi = pack_bf16(a, b);
-  lo = pack_bf16(a - bf16_lo(hi), b - bf16_hi(hi));
+  lo = pack_bf16(sub_bf16_lo(a, hi), sub_bf16_hi(b, hi));
 }
 
 // Three-term bf16 split of fp32 values, exact: v = hi + mid + lo.  hi is v
@@ -107,9 +127,9 @@ __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi,
 __device__ __forceinline__ void split3_bf16(float a, float b, uint32_t& hi, uint32_t& mid,
                                             uint32_t& lo) {
   hi = pack_bf16(a, b);
-  const float ra = a - bf16_lo(hi), rb = b - bf16_hi(hi);
+  const float ra = sub_bf16_lo(a, hi), rb = sub_bf16_hi(b, hi);
   mid = pack_bf16(ra, rb);
-  lo = pack_bf16(ra - bf16_lo(mid), rb - bf16_hi(mid));
+  lo = pack_bf16(sub_bf16_lo(ra, mid), sub_bf16_hi(rb, mid));
 }
 
 __device__ __forceinline__ u32x4 make_u32x4(const uint32_t (&a)[4]) {
