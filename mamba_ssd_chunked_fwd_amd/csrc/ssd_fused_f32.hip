@@ -16,28 +16,24 @@
 //
 // MI355X design (fp32 values on bf16 matrix instructions, three-term exact
 // splits and six products per pair as in compute_out_f32s: fp32 accuracy).
-// * One workgroup of 8 waves per (b, pair of heads of one group); the
-//   workgroups are persistent and take pairs with a stride of the grid size,
-//   so at any moment the workgroups of one XCD work on consecutive pairs --
-//   the heads of a group -- and share B and C in that XCD's L2.  The LDS
-//   (90 KB) admits one workgroup per CU, so the 8 waves are two per SIMD:
-//   one output wave and one state wave, whose matrix, vector and LDS work
-//   interleave.
-// * A work step is (pair, chunk, head).  Its x tile, g, dt, D_h (and at the
-//   pair's first head, the chunk's B tile and this lane's C rows) are loaded
-//   two steps ahead into one of two register sets.
-// * LDS per step: x as three bf16 planes [token][p], B as three planes
-//   [token][n] (once per chunk), S_c as three planes [p][n] for the output.
-// * Output: wave w < 4 owns query rows 16w..16w+15 exactly as
-//   compute_out_f32s (C B^T blocks in accumulators become the L' operand in
-//   registers).
-// * State: wave 4 + w owns state rows p = 16w..16w+15 of each head, held
-//   transposed in accumulators: lane (r, q) of block nb holds S[16w + r]
-//   [16 nb + 4q + 0..3], the layout both a 16-byte store of S_c and its
-//   bf16 planes want.  The update's operands are B^T (transposed LDS reads of
-//   the B planes) and X' = w o x, where the x fragment of the output's LDS
-//   reads is rebuilt in fp32 (the three planes sum to x exactly), scaled by
-//   w_t = dt_t 2^{g_last - g_t} <= dt_t and split again.
+// Two kernels, both with persistent workgroups that take (b, head pair)
+// work items with a stride of the grid size, so that at any moment the
+// workgroups of one XCD work on consecutive pairs -- the heads of a group --
+// and share B and C in that XCD's L2; both prefetch a step's operands two
+// steps ahead into one of two register sets, and both run 8 waves (two per
+// SIMD) because their LDS admits one workgroup per CU.
+// * fused_pair_f32 (groups of an even number of heads): both heads of a pair
+//   at once, every wave owning 16 state rows of one head; see its comment.
+// * fused_state_out_f32 (odd group sizes: one head per work item): four
+//   waves compute the output by query rows as compute_out_f32s does, four
+//   carry the state rows; x, B and S_c pass through LDS as bf16 planes.
+//   The state waves hold S transposed in accumulators: lane (r, q) of block
+//   nb holds S[16w + r][16 nb + 4q + 0..3], the layout both a 16-byte store
+//   of S_c and its bf16 planes want.  The update's operands are B^T
+//   (transposed LDS reads of the B planes) and X' = w o x, where the x
+//   fragment of the output's LDS reads is rebuilt in fp32 (the three planes
+//   sum to x exactly), scaled by w_t = dt_t 2^{g_last - g_t} <= dt_t and
+//   split again.
 #include "ssd_device.h"
 #include "ssd_host.h"
 #include "ssd_launch.h"
@@ -445,19 +441,404 @@ __global__ __launch_bounds__(kThreads) void fused_state_out_f32(
   }
 }
 
+// Head-pair form (8 waves, two per SIMD), for groups of an even number of
+// heads: both heads of a pair at once, waves 4q..4q+3 on head q, wave 4q + w
+// owning rows p = 16w..16w+15 of that head's state and of its Y^T[p][i]
+// over every token i of the chunk, so the waves carry equal work.
+// * The state stays in accumulators, S[p][16 nb + 4 lq + rr] in lane (p, lq),
+//   and feeds C S^T directly: its k slots follow that layout, n = 32 kk +
+//   16 (e / 4) + 4 lq + e % 4, and C is staged with its columns in that
+//   order.
+// * x never passes through LDS: each lane loads the 16 (token, p) values its
+//   fragments carry (token 32 s + 16 (e / 4) + 4 lq + e % 4, column p),
+//   splits them for X^T L'^T and scales them by w_t for the state update.
+// * B and C are staged once per chunk for both heads.  Each of the ten lower
+//   16x16 blocks of C B^T is formed once, by one wave (two for waves 0 and 1,
+//   one for the others), which turns it into L' of both heads in LDS.
+// * Addresses: every per-step part is uniform and goes into the buffer
+//   descriptors (scalar arithmetic); the lanes' offsets are loop-invariant.
+//   The ranges end at the sequence, so rows past its end read zero and their
+//   stores are dropped.
+template <bool YBF16>
+__global__ __launch_bounds__(512) void fused_pair_f32(
+    const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ Cm,
+    const float* __restrict__ dt_t, const float* __restrict__ g, const float* __restrict__ Dv,
+    const float* __restrict__ init, float* __restrict__ states, float* __restrict__ final_state,
+    void* __restrict__ y, int L, int H, int G, int nc, int pairs) {
+  constexpr int NT = 512;
+  constexpr int T = 64, N = 64, NIB = 4, KN = N / 32;
+  constexpr int BS = 80;                 // B plane row stride (bf16)
+  constexpr int CS = N + 8;              // C plane row stride (bf16), columns in k-slot order
+  constexpr int LS = T + 8;              // L' plane row stride (bf16), columns in k-slot order
+  constexpr int BU = T * 16 / NT;        // 16-byte units of the B and C tiles per thread
+  constexpr int XV = 16;                 // x values per lane
+  constexpr uint32_t kYB = YBF16 ? 2 : 4;
+  constexpr uint32_t kStateBytes = kHeadDim * N * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t bp[3][T * BS];
+  __shared__ __attribute__((aligned(16))) uint16_t cp[3][T * CS];
+  __shared__ __attribute__((aligned(16))) uint16_t lp[2][3][T * LS];
+  __shared__ __attribute__((aligned(16))) float gs[2][T], ds[2][T];
+
+  const int nwg = gridDim.x;
+  int wg = blockIdx.x;
+  if (nwg % 8 == 0) wg = (wg % 8) * (nwg / 8) + wg / 8;
+  if (wg >= pairs) return;
+  const int mine = (pairs - 1 - wg) / nwg + 1;
+  const int nsteps = mine * nc;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = wave >> 2, w = wave & 3;     // head of the pair, row block
+  const int lr = lane & 15, lq = lane >> 4;
+  const int hpg = H / G, npr = H / 2;
+  const uint32_t xrow = (uint32_t)H * kHeadDim * 4;   // bytes per token of x
+  const uint32_t brow = (uint32_t)G * N * 4;          // bytes per token of B and C
+  const rsrc_t drs = make_rsrc(Dv, (uint32_t)H * 4);
+  const int p = 16 * w + lr;                  // this lane's state row (operand row)
+
+  // loop-invariant lane offsets (bytes) from each step's descriptor bases
+  const uint32_t xo_lane = 4 * (uint32_t)p + 4 * (uint32_t)lq * xrow;
+  uint32_t bo_lane[BU];
+#pragma unroll
+  for (int u = 0; u < BU; ++u) {
+    const int e = tid + NT * u;
+    bo_lane[u] = (uint32_t)(e >> 4) * brow + 16 * (e & 15);
+  }
+  const uint32_t gd_lane = 4 * (uint32_t)(tid & 63);
+  const uint32_t so_lane = ((uint32_t)p * N + 4 * lq) * 4;
+
+  auto kpos = [](int c) { return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3); };
+  // uniform part of the token of x value v (v = 8 s + e): 32 s + 16 (e / 4) + e % 4
+  auto xtok_u = [](int v) { return 32 * (v >> 3) + 16 * ((v >> 2) & 1) + (v & 3); };
+
+  // this wave's blocks (ib, jb) of C B^T: waves 0-3 (3, 3-w), waves 4-6
+  // (2, 6-w), wave 7 (1, 0); waves 0 and 1 also (w, w)
+  const int nblk = wave < 2 ? 2 : 1;
+  auto blk_i = [&](int sl) { return sl == 1 ? wave : (wave < 4 ? 3 : (wave < 7 ? 2 : 1)); };
+  auto blk_j = [&](int sl) {
+    return sl == 1 ? wave : (wave < 4 ? 3 - wave : (wave < 7 ? 6 - wave : 0));
+  };
+
+  // Work steps are (pair, chunk), chunks fastest.  A cursor walks them in
+  // order, dividing only when it moves to the next pair.
+  struct StepP {
+    int b, c, h0, grp;
+    bool live;
+  };
+  struct Cursor {
+    int k, c, it;
+    StepP st;
+  };
+  auto at_pair = [&](Cursor& cu) {
+    cu.st.b = cu.it / npr;
+    cu.st.h0 = (cu.it - cu.st.b * npr) * 2;
+    cu.st.grp = cu.st.h0 / hpg;
+  };
+  auto advance = [&](Cursor& cu) {
+    ++cu.k;
+    if (++cu.c == nc) {
+      cu.c = 0;
+      cu.it += nwg;
+      if (cu.k < nsteps) at_pair(cu);
+    }
+    cu.st.c = cu.c;
+    cu.st.live = cu.k < nsteps;
+  };
+
+  struct Regs {
+    float xv[XV];
+    f32x4 bt[BU], ct[BU];
+    float gd, dh[2];
+    StepP st;       // the step these registers were loaded for
+  };
+  constexpr int NLOAD = XV + 2 * BU + 3;
+  struct Src {
+    rsrc_t xr, br, crr, gdr;
+    int h0;
+  };
+  auto prepare = [&](const StepP& st, Src& sc) {
+    const int t0 = st.c * T, h = st.h0 + hq;
+    const uint32_t rows = (uint32_t)(L - t0);
+    sc.xr = make_rsrc(x + (((size_t)st.b * L + t0) * H + h) * kHeadDim,
+                      st.live ? (rows * H - h) * (kHeadDim * 4) : 0u);
+    const size_t bcb = (((size_t)st.b * L + t0) * G + st.grp) * N;
+    const uint32_t bcr = st.live ? (rows * G - st.grp) * (N * 4) : 0u;
+    sc.br = make_rsrc(Bm + bcb, bcr);
+    sc.crr = make_rsrc(Cm + bcb, bcr);
+    // g and dt of both heads: waves 0-1 head 0, waves 2-3 head 1, even waves g
+    const int gh = wave >> 1, gk = wave & 1;
+    sc.gdr = make_rsrc((gk ? dt_t : g) + ((size_t)st.b * H + st.h0 + gh) * L + t0,
+                       st.live && wave < 4 ? rows * 4 : 0u);
+    sc.h0 = st.h0;
+  };
+  auto issue_slot = [&](int j, const Src& sc, Regs& r) {
+    if (j < XV) {
+      r.xv[j] = load_f32(sc.xr, xo_lane + (uint32_t)xtok_u(j) * xrow);
+    } else if (j < XV + BU) {
+      r.bt[j - XV] = load_f32x4(sc.br, bo_lane[j - XV]);
+    } else if (j < XV + 2 * BU) {
+      r.ct[j - XV - BU] = load_f32x4(sc.crr, bo_lane[j - XV - BU]);
+    } else if (j == XV + 2 * BU) {
+      r.gd = load_f32(sc.gdr, gd_lane);
+    } else {
+      const int q = j - XV - 2 * BU - 1;
+      r.dh[q] = load_f32(drs, 4 * (sc.h0 + q));
+    }
+  };
+  auto store3 = [](uint16_t* p0, uint16_t* p1, uint16_t* p2, int o, const f32x4& v) {
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3_bf16(v[0], v[1], h0, m0, l0);
+    split3_bf16(v[2], v[3], h1, m1, l1);
+    *(u32x2*)(p0 + o) = (u32x2){h0, h1};
+    *(u32x2*)(p1 + o) = (u32x2){m0, m1};
+    *(u32x2*)(p2 + o) = (u32x2){l0, l1};
+  };
+
+  f32x4 sacc[N / 16];   // S[p][16 nb + 4 lq + rr] of this wave's head
+  f32x4 cbr[2];         // (B C^T)[16 jb + 4 lq + rr][16 ib + lr] of this wave's blocks
+
+  // L' blocks that stay zero: (ib 0, jb 1) and (ib 2, jb 3), read as the
+  // upper halves of 32-token k-steps on the diagonal
+  for (int e = tid; e < 2 * 2 * 16 * 16; e += NT) {
+    const int hh = e >> 9, blk = (e >> 8) & 1, r = (e >> 4) & 15, c = e & 15;
+    const int i = blk == 0 ? r : 32 + r, j = blk == 0 ? 16 + c : 48 + c;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) lp[hh][q][i * LS + kpos(j)] = 0;
+  }
+
+  Regs ra, rb;
+  Cursor cur;
+  cur.k = 0;
+  cur.c = 0;
+  cur.it = wg;
+  at_pair(cur);
+  cur.st.c = 0;
+  cur.st.live = true;
+  {
+    Src sc;
+    prepare(cur.st, sc);
+    ra.st = cur.st;
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) issue_slot(j, sc, ra);
+    advance(cur);
+    prepare(cur.st, sc);
+    rb.st = cur.st;
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) issue_slot(j, sc, rb);
+    advance(cur);
+  }
+
+  auto body = [&](Regs& r) {
+    const StepP st = r.st;
+    const int h = st.h0 + hq;
+    const int t0 = st.c * T;
+    const int nt = min(T, L - t0);
+    const size_t hrow = (size_t)st.b * H + h;
+    const rsrc_t sres = make_rsrc(states + (hrow * nc + st.c) * (kHeadDim * N), kStateBytes);
+    if (st.c == 0) {
+      // no initial state: an empty range, every load reads zero
+      const rsrc_t ires = init ? make_rsrc(init + hrow * (kHeadDim * N), kStateBytes)
+                               : make_rsrc(states, 0u);
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb) sacc[nb] = load_f32x4(ires, so_lane + 64 * nb);
+    }
+    __syncthreads();  // the previous step's LDS reads are done
+
+    // ---- commit: B and C planes, g and dt of both heads, S_c to the states;
+    //      this lane's x values split into the X^T fragments
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int e = tid + NT * u, row = e >> 4, c4 = e & 15;
+      store3(bp[0], bp[1], bp[2], row * BS + 4 * c4, r.bt[u]);
+      store3(cp[0], cp[1], cp[2], row * CS + kpos(4 * c4), r.ct[u]);
+    }
+    if (wave < 4) ((wave & 1) ? ds : gs)[wave >> 1][lane] = r.gd;
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[nb]), sres,
+                                             so_lane + 64 * nb, 0, 0);
+    u32x4 xa[2][3];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      split8((f32x4){r.xv[8 * s], r.xv[8 * s + 1], r.xv[8 * s + 2], r.xv[8 * s + 3]},
+             (f32x4){r.xv[8 * s + 4], r.xv[8 * s + 5], r.xv[8 * s + 6], r.xv[8 * s + 7]},
+             xa[s]);
+    const float Dh[2] = {r.dh[0], r.dh[1]};
+    Src nxt;
+    prepare(cur.st, nxt);
+    r.st = cur.st;
+    advance(cur);
+    __syncthreads();
+
+    // ---- this wave's blocks of C B^T (A = B rows j, B = C rows i, k slots
+    //      in accumulator order) and from them L' of both heads -> LDS
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (sl < nblk) {
+        const int ib = blk_i(sl), jb = blk_j(sl);
+        f32x4 acc = (f32x4){0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk) {
+          const int ob = (16 * jb + lr) * BS + 32 * kk + 4 * lq;
+          u32x4 bf[3], cf[3];
+#pragma unroll
+          for (int q = 0; q < 3; ++q) {
+            const u32x2 b0 = *(const u32x2*)(bp[q] + ob);
+            const u32x2 b1 = *(const u32x2*)(bp[q] + ob + 16);
+            bf[q] = (u32x4){b0[0], b0[1], b1[0], b1[1]};
+            cf[q] = *(const u32x4*)(cp[q] + (16 * ib + lr) * CS + 32 * kk + 8 * lq);
+          }
+          acc = mfma6(bf, cf, acc);
+        }
+        cbr[sl] = acc;
+      }
+    }
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (sl < nblk) {
+        const int ib = blk_i(sl), jb = blk_j(sl);
+        const int i = 16 * ib + lr, j0 = 16 * jb + 4 * lq;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float gi = gs[hh][i];
+          const f32x4 gj = *(const f32x4*)(&gs[hh][j0]);
+          const f32x4 dj = *(const f32x4*)(&ds[hh][j0]);
+          f32x4 v;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int j = j0 + rr;
+            float wv = cbr[sl][rr] * (exp2_hw(gi - gj[rr]) * dj[rr]);
+            if (j == i) wv += Dh[hh];
+            v[rr] = j <= i ? wv : 0.0f;
+          }
+          store3(lp[hh][0], lp[hh][1], lp[hh][2], i * LS + kpos(j0), v);
+        }
+      }
+    }
+
+    // ---- Y^T = S C^T, A = S from the accumulators (split), B = C rows
+    f32x4 yacc[NIB];
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) yacc[ib] = (f32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk) {
+      u32x4 sf[3];
+      split8(sacc[2 * kk], sacc[2 * kk + 1], sf);
+#pragma unroll
+      for (int ib = 0; ib < NIB; ++ib) {
+        const int j = XV + 4 * kk + ib;
+        if (j < NLOAD) issue_slot(j, nxt, r);
+        const int oc = (16 * ib + lr) * CS + 32 * kk + 8 * lq;
+        const u32x4 cf[3] = {*(const u32x4*)(cp[0] + oc), *(const u32x4*)(cp[1] + oc),
+                             *(const u32x4*)(cp[2] + oc)};
+        yacc[ib] = mfma6(sf, cf, yacc[ib]);
+      }
+    }
+    const float* gsh = gs[hq];
+    const float* dsh = ds[hq];
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) yacc[ib] *= exp2_hw(gsh[16 * ib + lr]);
+
+    // ---- state: S <- 2^{g_last} S + B^T X', X' = w o x on this lane's tokens
+    const float glast = gsh[nt - 1];
+    const float dec = exp2_hw(glast);
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) sacc[nb] *= dec;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f32x4 g0 = *(const f32x4*)(&gsh[32 * s + 4 * lq]);
+      const f32x4 g1 = *(const f32x4*)(&gsh[32 * s + 16 + 4 * lq]);
+      const f32x4 d0 = *(const f32x4*)(&dsh[32 * s + 4 * lq]);
+      const f32x4 d1 = *(const f32x4*)(&dsh[32 * s + 16 + 4 * lq]);
+      f32x4 x0, x1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x0[e] = r.xv[8 * s + e] * (d0[e] * exp2_hw(glast - g0[e]));
+        x1[e] = r.xv[8 * s + 4 + e] * (d1[e] * exp2_hw(glast - g1[e]));
+      }
+      u32x4 xp[3];
+      split8(x0, x1, xp);
+      const int bo = (32 * s + 4 * lq + (lr >> 2)) * BS + 4 * (lr & 3);
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb) {
+        u32x4 bt[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          const u32x2 a0 = lds_read_tr16(bp[q] + bo + 16 * nb);
+          const u32x2 a1 = lds_read_tr16(bp[q] + bo + 16 * BS + 16 * nb);
+          bt[q] = (u32x4){a0[0], a0[1], a1[0], a1[1]};
+        }
+        sacc[nb] = mfma6(bt, xp, sacc[nb]);
+      }
+    }
+    // x of the step two ahead, now that this step's x is consumed
+#pragma unroll
+    for (int j = 0; j < XV; ++j) issue_slot(j, nxt, r);
+    if (st.c == nc - 1 && final_state) {
+      const rsrc_t fres = make_rsrc(final_state + hrow * (kHeadDim * N), kStateBytes);
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[nb]), fres,
+                                               so_lane + 64 * nb, 0, 0);
+    }
+    __syncthreads();  // every wave's L' blocks are in LDS
+
+    // ---- Y^T += X^T L'^T over the 32-token k-steps on or below the
+    //      diagonal; rows past the end of the sequence fall outside the range
+    const rsrc_t yres =
+        make_rsrc((char*)y + (((size_t)st.b * L + t0) * H + h) * kHeadDim * kYB,
+                  ((uint32_t)(L - t0) * H - h) * kHeadDim * kYB);
+    uint16_t(*lph)[T * LS] = lp[hq];
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (2 * s <= ib) {
+          const int ol = (16 * ib + lr) * LS + 32 * s + 8 * lq;
+          const u32x4 lf[3] = {*(const u32x4*)(lph[0] + ol), *(const u32x4*)(lph[1] + ol),
+                               *(const u32x4*)(lph[2] + ol)};
+          yacc[ib] = mfma6(xa[s], lf, yacc[ib]);
+        }
+      }
+      const uint32_t yo = ((uint32_t)(16 * ib + lr) * H * kHeadDim + p - lr + 4 * lq) * kYB;
+      if constexpr (YBF16) {
+        __builtin_amdgcn_raw_buffer_store_b64(
+            (u32x2){pack_bf16(yacc[ib][0], yacc[ib][1]), pack_bf16(yacc[ib][2], yacc[ib][3])},
+            yres, yo, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yacc[ib]), yres, yo, 0,
+                                               0);
+      }
+    }
+  };
+
+  for (int k = 0; k < nsteps; k += 2) {
+    body(ra);
+    if (k + 1 < nsteps) body(rb);
+  }
+}
+
 template <int HB, bool YBF16>
 int launch_hb(const float* x, const float* B, const float* C, const float* dt_t, const float* g,
               const float* D, const float* init, float* states, float* fin, void* y,
               const Shape& s, hipStream_t st) {
-  const void* kern = (const void*)fused_state_out_f32<HB, YBF16>;
+  // two heads per pair: the head-pair kernel; one: the output/state-wave kernel
+  const void* kern = HB == 2 ? (const void*)fused_pair_f32<YBF16>
+                             : (const void*)fused_state_out_f32<HB, YBF16>;
+  const int threads = HB == 2 ? 512 : kThreads;
   static PerDeviceInt resident;
-  const int slots = resident.get([&](int dev) { return resident_slots(kern, kThreads, dev); });
+  const int slots = resident.get([&](int dev) { return resident_slots(kern, threads, dev); });
   if (slots <= 0) return (int)hipErrorInvalidDevice;
   const int pairs = (int)(s.batch * s.nheads / HB);
   const unsigned grid = (unsigned)(pairs < slots ? pairs : slots);
-  hipLaunchKernelGGL((fused_state_out_f32<HB, YBF16>), dim3(grid), dim3(kThreads), 0, st, x, B,
-                     C, dt_t, g, D, init, states, fin, y, (int)s.seqlen, (int)s.nheads,
-                     (int)s.ngroups, (int)s.nchunks(), pairs);
+  if (HB == 2)
+    hipLaunchKernelGGL((fused_pair_f32<YBF16>), dim3(grid), dim3(threads), 0, st, x, B, C, dt_t,
+                       g, D, init, states, fin, y, (int)s.seqlen, (int)s.nheads, (int)s.ngroups,
+                       (int)s.nchunks(), pairs);
+  else
+    hipLaunchKernelGGL((fused_state_out_f32<HB, YBF16>), dim3(grid), dim3(threads), 0, st, x,
+                       B, C, dt_t, g, D, init, states, fin, y, (int)s.seqlen, (int)s.nheads,
+                       (int)s.ngroups, (int)s.nchunks(), pairs);
   return (int)hipGetLastError();
 }
 
