@@ -476,6 +476,7 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
   constexpr uint32_t kStateBytes = kHeadDim * N * 4;
   __shared__ __attribute__((aligned(16))) uint16_t bp[3][T * BS];
   __shared__ __attribute__((aligned(16))) uint16_t cp[3][T * CS];
+  __shared__ __attribute__((aligned(16))) uint16_t bq[3][T * CS];   // B, columns in k-slot order
   __shared__ __attribute__((aligned(16))) uint16_t lp[2][3][T * LS];
   __shared__ __attribute__((aligned(16))) float gs[2][T], ds[2][T];
 
@@ -650,6 +651,7 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     for (int u = 0; u < BU; ++u) {
       const int e = tid + NT * u, row = e >> 4, c4 = e & 15;
       store3(bp[0], bp[1], bp[2], row * BS + 4 * c4, r.bt[u]);
+      store3(bq[0], bq[1], bq[2], row * CS + kpos(4 * c4), r.bt[u]);
       store3(cp[0], cp[1], cp[2], row * CS + kpos(4 * c4), r.ct[u]);
     }
     if (wave < 4) ((wave & 1) ? ds : gs)[wave >> 1][lane] = r.gd;
@@ -679,14 +681,13 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
         f32x4 acc = (f32x4){0, 0, 0, 0};
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk) {
-          const int ob = (16 * jb + lr) * BS + 32 * kk + 4 * lq;
+          const int ob = (16 * jb + lr) * CS + 32 * kk + 8 * lq;
+          const int oc = (16 * ib + lr) * CS + 32 * kk + 8 * lq;
           u32x4 bf[3], cf[3];
 #pragma unroll
           for (int q = 0; q < 3; ++q) {
-            const u32x2 b0 = *(const u32x2*)(bp[q] + ob);
-            const u32x2 b1 = *(const u32x2*)(bp[q] + ob + 16);
-            bf[q] = (u32x4){b0[0], b0[1], b1[0], b1[1]};
-            cf[q] = *(const u32x4*)(cp[q] + (16 * ib + lr) * CS + 32 * kk + 8 * lq);
+            bf[q] = *(const u32x4*)(bq[q] + ob);
+            cf[q] = *(const u32x4*)(cp[q] + oc);
           }
           acc = mfma6(bf, cf, acc);
         }
