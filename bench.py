@@ -5,7 +5,10 @@
 
 A step is one ssd_forward call -- the whole hot path: stage 1 (chunk
 cumsum), stage 2 (state pass), stage 3 (fused output) -- over one batch of
-synthetic input of the named workload.  The default workload is the largest
+synthetic input of the named workload.  For fp32 inputs with 64-token chunks,
+N = 64 and at least one (batch, head pair) per CU, ssd_forward runs stages 2
+and 3 as one kernel (ssd_state_and_out); the step's kernels are then stage 1
+and that one, and the two-kernel path is timed beside it for reference.  The default workload is the largest
 of the five (wide_fp32: 64 sequences of 1024 tokens, 48 heads, 8 groups,
 state 64, fp32; 4.6 GB of algorithmic traffic per step).  The wall clock
 over K steps gives `value` in tokens/s.
@@ -54,8 +57,25 @@ CONFIG_ORDER = ["tiny_fp32", "small_bf16", "large_bf16", "long_bf16", "wide_fp32
 # chunk_state + state_passing, chosen by shape)
 STAGE_SOURCES = {"chunk_cumsum": ["ssd_chunk_cumsum.hip"],
                  "fwd_pass_state": ["ssd_fwd_pass_state.hip", "ssd_state_two_level.hip"],
-                 "compute_out": ["ssd_compute_out.hip"]}
-STEP_KERNELS = ["chunk_cumsum", "fwd_pass_state", "compute_out"]
+                 "compute_out": ["ssd_compute_out.hip"],
+                 "state_and_out": ["ssd_fused_f32.hip"]}
+THREE_STAGES = ["chunk_cumsum", "fwd_pass_state", "compute_out"]
+FUSED_STAGES = ["chunk_cumsum", "state_and_out"]
+
+
+def heads_per_pair(w) -> int:
+    return 2 if (w.nheads // w.ngroups) % 2 == 0 else 1
+
+
+def fused(w, cus: int = 256) -> bool:
+    """Whether ssd_forward runs stages 2 and 3 as one kernel for this
+    workload (the library's own rule)."""
+    return (w.dtype == "fp32" and w.chunk_size == 64 and w.dstate == 64
+            and w.batch * w.nheads // heads_per_pair(w) >= cus)
+
+
+def step_kernels(w, cus: int = 256) -> list:
+    return FUSED_STAGES if fused(w, cus) else THREE_STAGES
 
 
 def algorithmic(w, y_bytes: int):
@@ -77,6 +97,11 @@ def algorithmic(w, y_bytes: int):
                            + 4 * b * H * P * N),
         "compute_out": (e * b * L * H * P + 2 * e * b * L * G * N + 8 * b * L * H
                         + 4 * b * H * nc * P * N + 4 * H + y_bytes * b * L * H * P),
+        # stages 2 and 3 in one pass: x, B, C, dt_t and g read once, the
+        # states written and never read back
+        "state_and_out": (e * b * L * H * P + 2 * e * b * L * G * N + 8 * b * L * H
+                          + 4 * b * H * P * N * init + 4 * b * H * nc * P * N
+                          + 4 * b * H * P * N + 4 * H + y_bytes * b * L * H * P),
     }
     fl = {
         "chunk_cumsum": 2 * b * L * H,
@@ -84,6 +109,7 @@ def algorithmic(w, y_bytes: int):
         "compute_out": (2 * b * L * H * P * N + b * nc * H * T * (T + 1) * P
                         + b * nc * G * T * (T + 1) * N),
     }
+    fl["state_and_out"] = fl["fwd_pass_state"] + fl["compute_out"]
     return by, fl
 
 
@@ -99,7 +125,8 @@ def mfma_kind(w) -> dict:
     splits) for chunks of up to 128 tokens."""
     out_bf16 = w.dtype == "bf16" or w.chunk_size <= 128
     return {"fwd_pass_state": "bf16" if w.dtype == "bf16" else "fp32",
-            "compute_out": "bf16" if out_bf16 else "fp32"}
+            "compute_out": "bf16" if out_bf16 else "fp32",
+            "state_and_out": "bf16"}
 
 
 def issued_mfma_flop(w) -> dict:
@@ -125,7 +152,12 @@ def issued_mfma_flop(w) -> dict:
     else:
         out = b * nc * H * (2 * T * P * N + lx16) + b * nc * G * cb
         a2 = 2 * b * L * H * P * N
-    return {"fwd_pass_state": a2, "compute_out": out}
+    # the fused pass (fp32 on bf16 instructions, six per product): C S^T,
+    # X^T L'^T and the state update per (batch, chunk, head), C B^T once per
+    # (batch, chunk, work item of heads_per_pair heads)
+    fused_issued = 6 * (b * nc * H * (2 * 2 * T * P * N + lx32)
+                        + b * nc * (H // heads_per_pair(w)) * cb)
+    return {"fwd_pass_state": a2, "compute_out": out, "state_and_out": fused_issued}
 
 
 def source_sha(stage: str) -> str:
@@ -223,6 +255,7 @@ class WorkloadRun:
         self.by, self.fl = algorithmic(w, self.y_bytes)
         b, L, H, P, N, T = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk_size
         nc = w.nchunks
+        self.kernels = step_kernels(w, torch.cuda.get_device_properties(dev).multi_processor_count)
         set_bytes = self.by["fwd_pass_state"] + self.by["compute_out"]
         self.nsets = max(1, min(16, -(-(1 << 30) // set_bytes)))
         d = ssd.SsdDims(b, L, H, P, N, w.ngroups, T)
@@ -257,17 +290,22 @@ class WorkloadRun:
         elif name == "fwd_pass_state":
             ssd.ssd_fwd_pass_state(s["x"], s["B"], s["dt_t"], s["g"], s["init"], s["states"],
                                    s["final"], T)
+        elif name == "state_and_out":
+            ssd.ssd_state_and_out(s["x"], s["B"], s["C"], s["dt_t"], s["g"], s["D"], s["init"],
+                                  s["y"], s["states"], s["final"], T)
         else:
             ssd.ssd_compute_out(s["x"], s["B"], s["C"], s["dt_t"], s["g"], s["states"],
                                 s["D"], s["y"], T)
 
     def time_all(self, nlaunch: int) -> dict:
-        """Graph-replay durations (ms) of ssd_forward and of each stage."""
+        """Graph-replay durations (ms) of ssd_forward, of each of its
+        kernels and, where stages 2 and 3 run fused, of the two-kernel path."""
         for i in range(max(3, self.nsets)):
             self.forward(i)
         out = {"ssd_forward": graph_time_ms([lambda i=i: self.forward(i)
                                              for i in range(nlaunch)])}
-        for n in STEP_KERNELS:
+        names = list(dict.fromkeys(self.kernels + THREE_STAGES))
+        for n in names:
             out[n] = graph_time_ms([lambda i=i, n=n: self.stage(n, i) for i in range(nlaunch)])
         return out
 
@@ -278,7 +316,7 @@ class WorkloadRun:
         kind = mfma_kind(w)
         issued = issued_mfma_flop(w)
         stages = {}
-        for n in STEP_KERNELS:
+        for n in self.kernels:
             ms = dur[n]
             gbs = self.by[n] / (ms * 1e-3) / 1e9
             e = {"us": round(ms * 1e3, 2), "alg_bytes": self.by[n],
@@ -298,12 +336,17 @@ class WorkloadRun:
                 e["mfma_peak_TFLOP_per_s"] = peak_tf
                 e["mfma_alg_frac"] = round(tf_alg / peak_tf, 4)
                 e["mfma_issued_frac"] = round(tf_iss / peak_tf, 4)
-                rec = committed_profile(w.name, n, "mfma") if n == "compute_out" else None
+                rec = (committed_profile(w.name, n, "mfma")
+                       if n in ("compute_out", "state_and_out") else None)
                 if rec is not None:
                     e["mfma_busy_frac_counters"] = round(rec["mfma_busy_frac"], 4)
             stages[n] = e
         step_ms = dur["ssd_forward"]
-        step_bytes = sum(self.by[n] for n in STEP_KERNELS)
+        step_bytes = sum(self.by[n] for n in self.kernels)
+        extra = {}
+        if "state_and_out" in self.kernels:
+            extra["two_kernel_path_us"] = {n: round(dur[n] * 1e3, 2)
+                                           for n in ("fwd_pass_state", "compute_out")}
         return {"shape": {"batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                           "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                           "chunk_size": w.chunk_size, "dtype": w.dtype},
@@ -312,7 +355,8 @@ class WorkloadRun:
                 "step_alg_bytes": step_bytes,
                 "step_hbm_frac": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "hbm_floor_us": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
-                "stages": stages}
+                "step_kernels": self.kernels,
+                "stages": stages, **extra}
 
 
 def gdn_bench(ssd, c, make, dev, stream, nrep):
@@ -507,7 +551,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     copy_gbs = copy_rate(dev)
-    inp, nsets, step_flop = run.inp, run.nsets, sum(run.fl[n] for n in STEP_KERNELS)
+    inp, nsets, step_flop = run.inp, run.nsets, sum(run.fl[n] for n in run.kernels)
+    kernels = run.kernels
     del run
     torch.cuda.empty_cache()
 
@@ -525,7 +570,7 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = w.tokens / (wall / args.steps)
     stages = head["stages"]
-    dom = max(STEP_KERNELS, key=lambda n: stages[n]["us"])
+    dom = max(kernels, key=lambda n: stages[n]["us"])
     achieved = stages[dom]["GB_per_s"]
     traffic_rec = committed_profile(w.name, dom, "traffic")
     out = {
@@ -553,6 +598,8 @@ def main() -> int:
                      "alg_bytes_per_launch": stages[dom]["alg_bytes"],
                      "us_per_launch": stages[dom]["us"]},
         "stages": stages,
+        **({"two_kernel_path_us": head["two_kernel_path_us"]}
+           if "two_kernel_path_us" in head else {}),
         "ssd_forward_graph_us": head["step_us"],
         "effective_TFLOP_per_s": round(step_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "hbm_floor_ms": round(head["hbm_floor_us"] / 1e3, 5),

@@ -175,6 +175,26 @@ ssd_status ssd_compute_out(const void *x, const void *B, const void *C,
                            void *stream);
 
 /*
+ * Stages 2 and 3 in one call: ssd_fwd_pass_state then ssd_compute_out on the
+ * same arguments, with the same results (equal up to the order of fp32
+ * roundings).  For fp32 inputs, 64-token chunks and dstate 64, when the
+ * batch holds at least one (b, head pair) per compute unit, the two run as
+ * one kernel that carries each head's state from chunk to chunk in
+ * registers, so x is read once and the states are written but not read back
+ * (the pages' two kernels, fused; [P1 "Kernel 2"; P1 "Kernel 3"]).
+ *   x, B, C, dt_t, g, D as for the two stages; init_state [b, H, P, N] fp32
+ *   or NULL; states [b, H, nc, P, N] fp32 (written); final_state [b, H, P, N]
+ *   fp32 or NULL; y [b, L, H, P] in y_dtype (written).
+ * init_state and final_state may be the same buffer; no other output may
+ * overlap an input.
+ */
+ssd_status ssd_state_and_out(const void *x, const void *B, const void *C,
+                             const float *dt_t, const float *g, const float *D,
+                             const float *init_state, void *y, float *states,
+                             float *final_state, ssd_dtype in_dtype, ssd_dtype y_dtype,
+                             const ssd_dims *dims, void *stream);
+
+/*
  * The whole forward [P1 "From the Math to Three Kernels"]: stage 1 (g, dt_t)
  * into the caller's workspace (at least ssd_forward_workspace_bytes(dims)
  * bytes, else

@@ -7,7 +7,7 @@ the current HIP stream.  PyTorch supplies device memory and streams.
 
 Entry points (same names as the C ABI):
   ssd_chunk_cumsum, ssd_fwd_pass_state, ssd_chunk_state, ssd_state_passing,
-  ssd_compute_out, ssd_forward, ssd_forward_noalloc,
+  ssd_compute_out, ssd_state_and_out, ssd_forward, ssd_forward_noalloc,
   ssd_decode_step, ssd_causal_conv1d, ssd_gdn_chunk_fwd_h, ssd_gdn_chunk_fwd_o
 and the allocating convenience wrapper ``forward``.
 
@@ -77,6 +77,8 @@ def _load() -> ctypes.CDLL:
     lib.ssd_state_passing.restype = i
     lib.ssd_compute_out.argtypes = [vp] * 8 + [i, i, dims, vp]
     lib.ssd_compute_out.restype = i
+    lib.ssd_state_and_out.argtypes = [vp] * 10 + [i, i, dims, vp]
+    lib.ssd_state_and_out.restype = i
     lib.ssd_forward.argtypes = [vp] * 11 + [sz, i, i, dims, vp]
     lib.ssd_forward.restype = i
     lib.ssd_forward_noalloc.argtypes = [vp] * 10 + [i, i, dims, vp]
@@ -287,6 +289,36 @@ def ssd_compute_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         _ptr(x), _ptr(B), _ptr(C), _ptr(dt_t), _ptr(g), _ptr(states), _ptr(D),
         _ptr(y), _dtype_code(x.dtype), _dtype_code(y.dtype), ctypes.byref(d),
         _stream(dev)), "ssd_compute_out")
+
+
+def ssd_state_and_out(x: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                      dt_t: torch.Tensor, g: torch.Tensor, D: torch.Tensor,
+                      init_state: Optional[torch.Tensor], y: torch.Tensor,
+                      states: torch.Tensor, final_state: Optional[torch.Tensor],
+                      chunk_size: int) -> None:
+    """Stages 2 and 3 in one call (the fused single pass where it applies):
+    states, final_state and y from stage 1's g and dt_t."""
+    d = make_dims(x, B, chunk_size)
+    dev = x.device
+    ins = (torch.float32, torch.bfloat16)
+    f32 = (torch.float32,)
+    _check(x, "x", None, ins)
+    bc = (d.batch, d.seqlen, d.ngroups, d.dstate)
+    _check(B, "B", bc, (x.dtype,), dev)
+    _check(C, "C", bc, (x.dtype,), dev)
+    _check(dt_t, "dt_t", (d.batch, d.nheads, d.seqlen), f32, dev)
+    _check(g, "g", (d.batch, d.nheads, d.seqlen), f32, dev)
+    _check(D, "D", (d.nheads,), f32, dev)
+    st_shape = (d.batch, d.nheads, d.headdim, d.dstate)
+    _check(init_state, "init_state", st_shape, f32, dev, optional=True)
+    _check(y, "y", tuple(x.shape), ins, dev)
+    _check(states, "states", (d.batch, d.nheads, nchunks(d), d.headdim,
+                              d.dstate), f32, dev)
+    _check(final_state, "final_state", st_shape, f32, dev, optional=True)
+    _raise(_lib.ssd_state_and_out(
+        _ptr(x), _ptr(B), _ptr(C), _ptr(dt_t), _ptr(g), _ptr(D), _ptr(init_state),
+        _ptr(y), _ptr(states), _ptr(final_state), _dtype_code(x.dtype),
+        _dtype_code(y.dtype), ctypes.byref(d), _stream(dev)), "ssd_state_and_out")
 
 
 def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor,

@@ -183,6 +183,24 @@ ssd_status ssd_compute_out(const void* x, const void* B, const void* C,
                                           y_dtype == SSD_BF16, s, stream));
 }
 
+ssd_status ssd_state_and_out(const void* x, const void* B, const void* C,
+                             const float* dt_t, const float* g, const float* D,
+                             const float* init_state, void* y, float* states,
+                             float* final_state, ssd_dtype in_dtype, ssd_dtype y_dtype,
+                             const ssd_dims* dims, void* stream) {
+  ssd::Shape s;
+  const ssd_status st = check_dims(dims, &s);
+  if (st != SSD_OK) return st;
+  if (!ok_dtype(in_dtype) || !ok_dtype(y_dtype)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!ok_ptr(x) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(dt_t) || !ok_ptr(g) ||
+      !ok_ptr(D) || !ok_ptr(y) || !ok_ptr(states) || !ok_opt(init_state) ||
+      !ok_opt(final_state))
+    return SSD_ERR_INVALID_ARGUMENT;
+  return from_hip(ssd::launch_state_and_out(x, B, C, dt_t, g, D, init_state, states,
+                                            final_state, y, in_dtype == SSD_BF16,
+                                            y_dtype == SSD_BF16, s, stream));
+}
+
 ssd_status ssd_forward(const void* x, const float* dt, const float* A,
                        const void* B, const void* C, const float* D,
                        const float* init_state, void* y, float* states,

@@ -166,6 +166,25 @@ void test_stage_entry_points() {
                         (const float*)P(6), nullptr, P(8), SSD_F32, SSD_BF16, &d,
                         nullptr) == SSD_ERR_INVALID_ARGUMENT);
   CHECK(stub::ncalls == 3);
+  // stages 2 and 3 in one call: optional init/final, dtype flags through
+  CHECK(ssd_state_and_out(P(1), P(2), P(3), (const float*)P(4), (const float*)P(5),
+                          (const float*)P(6), nullptr, P(7), (float*)P(8), nullptr, SSD_F32,
+                          SSD_BF16, &d, nullptr) == SSD_OK);
+  CHECK(stub::ncalls == 4 && std::strcmp(stub::calls[3].name, "state_and_out") == 0);
+  CHECK(stub::calls[3].p[0] == P(4) && stub::calls[3].p[1] == P(5) &&
+        stub::calls[3].p[2] == P(8));
+  CHECK(!stub::calls[3].flag[0] && stub::calls[3].flag[1]);
+  CHECK(ssd_state_and_out(P(1), P(2), P(3), (const float*)P(4), (const float*)P(5),
+                          (const float*)P(6), (const float*)MIS(9), P(7), (float*)P(8),
+                          nullptr, SSD_F32, SSD_F32, &d,
+                          nullptr) == SSD_ERR_INVALID_ARGUMENT);
+  CHECK(ssd_state_and_out(P(1), P(2), P(3), (const float*)P(4), nullptr,
+                          (const float*)P(6), nullptr, P(7), (float*)P(8), nullptr, SSD_F32,
+                          SSD_F32, &d, nullptr) == SSD_ERR_INVALID_ARGUMENT);
+  CHECK(ssd_state_and_out(P(1), P(2), P(3), (const float*)P(4), (const float*)P(5),
+                          (const float*)P(6), nullptr, P(7), (float*)P(8), nullptr,
+                          (ssd_dtype)7, SSD_F32, &d, nullptr) == SSD_ERR_INVALID_ARGUMENT);
+  CHECK(stub::ncalls == 4);
 }
 
 void test_two_level() {

@@ -42,7 +42,8 @@ def test_every_declared_function_is_exported():
                           "ssd_compute_out", "ssd_forward", "ssd_decode_step",
                           "ssd_causal_conv1d", "ssd_gdn_chunk_fwd_h",
                           "ssd_gdn_chunk_fwd_o", "ssd_chunk_state",
-                          "ssd_state_passing", "ssd_forward_noalloc"}
+                          "ssd_state_passing", "ssd_forward_noalloc",
+                          "ssd_state_and_out"}
     out = subprocess.run(["nm", "-D", "--defined-only", ssd.LIB_PATH],
                          capture_output=True, text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
@@ -241,6 +242,16 @@ def test_stage_entry_points_validate():
     assert lib.ssd_compute_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                ssd.SSD_BF16, ssd.SSD_F32,
                                ctypes.byref(dims(nheads=6, ngroups=4)), None) == INV
+    # stages 2 and 3 in one call: x, B, C, dt_t, g, D, init, y, states, final
+    assert lib.ssd_state_and_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+                                 ssd.SSD_F32, ssd.SSD_F32, ctypes.byref(d), None) == INV
+    assert lib.ssd_state_and_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE,
+                                 None, ssd.SSD_F32, ssd.SSD_F32, ctypes.byref(d), None) == INV
+    assert lib.ssd_state_and_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                                 ssd.SSD_F32, 2, ctypes.byref(d), None) == INV
+    assert lib.ssd_state_and_out(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None,
+                                 ssd.SSD_F32, ssd.SSD_F32,
+                                 ctypes.byref(dims(chunk_size=96)), None) == UNS
 
 
 def test_binding_rejects_cpu_tensors():

@@ -66,8 +66,34 @@ def test_issued_matrix_work_of_the_output_stage():
     # steps, 1 + 1 + 2 + 2 of them over the row blocks; C B^T 10 of 16 blocks
     # once per (b, c, group)
     w = WORKLOADS["wide_fp32"]
-    assert bench.mfma_kind(w) == {"fwd_pass_state": "fp32", "compute_out": "bf16"}
+    assert bench.mfma_kind(w) == {"fwd_pass_state": "fp32", "compute_out": "bf16",
+                                  "state_and_out": "bf16"}
     b, H, G, P, N, nc = 64, 48, 8, 64, 64, 16
     per_item = 2 * 64 * P * N + 6 * 32 * 16 * P * 2
     assert bench.issued_mfma_flop(w)["compute_out"] == \
         6 * (b * nc * H * per_item + b * nc * G * 10 * 16 * 16 * N * 2)
+
+
+def test_fused_pass_accounting_of_the_wide_layer():
+    """The wide fp32 layer runs stages 2 and 3 as one kernel: its bytes are
+    x, B, C, g and dt_t read once, the states, final state and y written;
+    its issued work is C S^T, X^T L'^T and the state update per (b, c, h)
+    and C B^T once per (b, c, pair of heads), six bf16 products each."""
+    import bench
+    from ssd_workloads import WORKLOADS
+    w = WORKLOADS["wide_fp32"]
+    assert bench.step_kernels(w) == ["chunk_cumsum", "state_and_out"]
+    for name in ("tiny_fp32", "small_bf16", "large_bf16", "long_bf16"):
+        assert bench.step_kernels(WORKLOADS[name]) == \
+            ["chunk_cumsum", "fwd_pass_state", "compute_out"], name
+    b, L, H, P, N, G, T = 64, 1024, 48, 64, 64, 8, 64
+    nc = L // T
+    by, fl = bench.algorithmic(w, 4)
+    x = 4 * b * L * H * P
+    bc = 4 * b * L * G * N
+    assert by["state_and_out"] == (x + 2 * bc + 8 * b * L * H + 4 * b * H * nc * P * N
+                                   + 4 * b * H * P * N + 4 * H + 4 * b * L * H * P)
+    assert fl["state_and_out"] == fl["fwd_pass_state"] + fl["compute_out"]
+    per_head = 2 * (2 * T * P * N) + 6 * 32 * 16 * P * 2
+    assert bench.issued_mfma_flop(w)["state_and_out"] == \
+        6 * (b * nc * H * per_head + b * nc * (H // 2) * 10 * 16 * 16 * N * 2)

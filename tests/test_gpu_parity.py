@@ -365,6 +365,38 @@ def test_fused_forward_matches_stage_calls(ssd, regime):
     assert_close(_np(final), ref["final"], "fp32", "final (fused)")
 
 
+@pytest.mark.parametrize("case", ["fused_fp32", "two_kernel_bf16"])
+def test_state_and_out_entry_point(ssd, case):
+    """ssd_state_and_out on stage 1's outputs gives exactly what ssd_forward
+    gives (same kernels), on a shape that takes the fused pass and on one
+    that takes the two stage kernels (there also exactly the separate
+    stage-2 and stage-3 calls)."""
+    if case == "fused_fp32":
+        w, inp = _fused_case(35)
+        dtype = "fp32"
+    else:
+        w, inp = _small_inputs(seed=36, L=257, T=128)
+        dtype = "bf16"
+    dev = device_inputs(inp, dtype)
+    T = w.chunk_size
+    y, states, final = _run_forward(ssd, dev, T)
+    b, L, H = w.batch, w.seqlen, w.nheads
+    g = torch.empty(b, H, L, device=DEV)
+    dt_t = torch.empty(b, H, L, device=DEV)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, dt_t, T)
+    y2, s2, f2 = torch.empty_like(y), torch.empty_like(states), torch.empty_like(final)
+    ssd.ssd_state_and_out(dev["x"], dev["B"], dev["C"], dt_t, g, dev["D"], dev["init_state"],
+                          y2, s2, f2, T)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y) and torch.equal(s2, states) and torch.equal(f2, final)
+    if case == "two_kernel_bf16":
+        s3, f3, y3 = torch.empty_like(states), torch.empty_like(final), torch.empty_like(y)
+        ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dt_t, g, dev["init_state"], s3, f3, T)
+        ssd.ssd_compute_out(dev["x"], dev["B"], dev["C"], dt_t, g, s3, dev["D"], y3, T)
+        torch.cuda.synchronize()
+        assert torch.equal(s3, s2) and torch.equal(f3, f2) and torch.equal(y3, y2)
+
+
 def test_fused_forward_init_aliases_final(ssd):
     """ssd_forward on the fused path with init_state and final_state as one
     buffer gives what separate buffers give."""
