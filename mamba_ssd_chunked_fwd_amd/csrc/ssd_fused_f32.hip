@@ -479,6 +479,7 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
   __shared__ __attribute__((aligned(16))) uint16_t bq[3][T * CS];   // B, columns in k-slot order
   __shared__ __attribute__((aligned(16))) uint16_t lp[2][3][T * LS];
   __shared__ __attribute__((aligned(16))) float gs[2][T], ds[2][T];
+  __shared__ __attribute__((aligned(16))) float ws[2][T];   // w_t = dt_t 2^{g_last - g_t}
 
   const int nwg = gridDim.x;
   int wg = blockIdx.x;
@@ -549,12 +550,12 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
   struct Regs {
     float xv[XV];
     f32x4 bt[BU], ct[BU];
-    float gd, dh[2];
-    StepP st;       // the step these registers were loaded for
+    float gv, dv, dh[2];   // g and dt (waves 0 and 2: heads 0 and 1), D_h of both heads
+    StepP st;              // the step these registers were loaded for
   };
-  constexpr int NLOAD = XV + 2 * BU + 3;
+  constexpr int NLOAD = XV + 2 * BU + 4;
   struct Src {
-    rsrc_t xr, br, crr, gdr;
+    rsrc_t xr, br, crr, gr, dr;
     int h0;
   };
   auto prepare = [&](const StepP& st, Src& sc) {
@@ -566,10 +567,11 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     const uint32_t bcr = st.live ? (rows * G - st.grp) * (N * 4) : 0u;
     sc.br = make_rsrc(Bm + bcb, bcr);
     sc.crr = make_rsrc(Cm + bcb, bcr);
-    // g and dt of both heads: waves 0-1 head 0, waves 2-3 head 1, even waves g
-    const int gh = wave >> 1, gk = wave & 1;
-    sc.gdr = make_rsrc((gk ? dt_t : g) + ((size_t)st.b * H + st.h0 + gh) * L + t0,
-                       st.live && wave < 4 ? rows * 4 : 0u);
+    // g and dt of both heads: wave 0 head 0, wave 2 head 1
+    const size_t gro = ((size_t)st.b * H + st.h0 + (wave >> 1)) * L + t0;
+    const uint32_t grr = st.live && (wave == 0 || wave == 2) ? rows * 4 : 0u;
+    sc.gr = make_rsrc(g + gro, grr);
+    sc.dr = make_rsrc(dt_t + gro, grr);
     sc.h0 = st.h0;
   };
   auto issue_slot = [&](int j, const Src& sc, Regs& r) {
@@ -580,9 +582,11 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     } else if (j < XV + 2 * BU) {
       r.ct[j - XV - BU] = load_f32x4(sc.crr, bo_lane[j - XV - BU]);
     } else if (j == XV + 2 * BU) {
-      r.gd = load_f32(sc.gdr, gd_lane);
+      r.gv = load_f32(sc.gr, gd_lane);
+    } else if (j == XV + 2 * BU + 1) {
+      r.dv = load_f32(sc.dr, gd_lane);
     } else {
-      const int q = j - XV - 2 * BU - 1;
+      const int q = j - XV - 2 * BU - 2;
       r.dh[q] = load_f32(drs, 4 * (sc.h0 + q));
     }
   };
@@ -629,13 +633,14 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     advance(cur);
   }
 
-  auto body = [&](Regs& r) {
+  // Staging of a step from its registers: B and C planes, g and dt of both
+  // heads, and S_c (the state entering the chunk, after the previous
+  // chunk's update or from init_state) to the states.  It runs in the
+  // previous step's last phase, which reads only the L' planes, so it
+  // overlaps the other waves' X^T L'^T.
+  auto commit = [&](const Regs& r) {
     const StepP st = r.st;
-    const int h = st.h0 + hq;
-    const int t0 = st.c * T;
-    const int nt = min(T, L - t0);
-    const size_t hrow = (size_t)st.b * H + h;
-    const rsrc_t sres = make_rsrc(states + (hrow * nc + st.c) * (kHeadDim * N), kStateBytes);
+    const size_t hrow = (size_t)st.b * H + st.h0 + hq;
     if (st.c == 0) {
       // no initial state: an empty range, every load reads zero
       const rsrc_t ires = init ? make_rsrc(init + hrow * (kHeadDim * N), kStateBytes)
@@ -643,22 +648,48 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb) sacc[nb] = load_f32x4(ires, so_lane + 64 * nb);
     }
-    __syncthreads();  // the previous step's LDS reads are done
-
-    // ---- commit: B and C planes, g and dt of both heads, S_c to the states;
-    //      this lane's x values split into the X^T fragments
 #pragma unroll
     for (int u = 0; u < BU; ++u) {
       const int e = tid + NT * u, row = e >> 4, c4 = e & 15;
-      store3(bp[0], bp[1], bp[2], row * BS + 4 * c4, r.bt[u]);
-      store3(bq[0], bq[1], bq[2], row * CS + kpos(4 * c4), r.bt[u]);
-      store3(cp[0], cp[1], cp[2], row * CS + kpos(4 * c4), r.ct[u]);
+      uint32_t h0, m0, l0, h1, m1, l1;
+      split3_bf16(r.bt[u][0], r.bt[u][1], h0, m0, l0);
+      split3_bf16(r.bt[u][2], r.bt[u][3], h1, m1, l1);
+      const int ob = row * BS + 4 * c4, oq = row * CS + kpos(4 * c4);
+      *(u32x2*)(bp[0] + ob) = (u32x2){h0, h1};
+      *(u32x2*)(bp[1] + ob) = (u32x2){m0, m1};
+      *(u32x2*)(bp[2] + ob) = (u32x2){l0, l1};
+      *(u32x2*)(bq[0] + oq) = (u32x2){h0, h1};
+      *(u32x2*)(bq[1] + oq) = (u32x2){m0, m1};
+      *(u32x2*)(bq[2] + oq) = (u32x2){l0, l1};
+      store3(cp[0], cp[1], cp[2], oq, r.ct[u]);
     }
-    if (wave < 4) ((wave & 1) ? ds : gs)[wave >> 1][lane] = r.gd;
+    if (wave == 0 || wave == 2) {
+      // g, dt and the state-update weight w of one head: lane = token;
+      // tokens past the end read g = dt = 0, so w = 0
+      const int hh = wave >> 1;
+      const int nt = min(T, L - st.c * T);
+      const int gl = __builtin_amdgcn_readlane(__float_as_int(r.gv), nt - 1);
+      gs[hh][lane] = r.gv;
+      ds[hh][lane] = r.dv;
+      ws[hh][lane] = r.dv * exp2_hw(__int_as_float(gl) - r.gv);
+    }
+    const rsrc_t sres = make_rsrc(states + (hrow * nc + st.c) * (kHeadDim * N), kStateBytes);
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[nb]), sres,
                                              so_lane + 64 * nb, 0, 0);
+  };
+  commit(ra);
+  __syncthreads();
+
+  // step k from the registers r (staged already); rn holds step k + 1
+  auto body = [&](Regs& r, const Regs& rn, bool has_next) {
+    const StepP st = r.st;
+    const int h = st.h0 + hq;
+    const int t0 = st.c * T;
+    const int nt = min(T, L - t0);
+    const size_t hrow = (size_t)st.b * H + h;
+    // this lane's x values split into the X^T fragments
     u32x4 xa[2][3];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -670,7 +701,6 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     prepare(cur.st, nxt);
     r.st = cur.st;
     advance(cur);
-    __syncthreads();
 
     // ---- this wave's blocks of C B^T (A = B rows j, B = C rows i, k slots
     //      in accumulator order) and from them L' of both heads -> LDS
@@ -736,7 +766,7 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
       }
     }
     const float* gsh = gs[hq];
-    const float* dsh = ds[hq];
+    const float* wsh = ws[hq];
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) yacc[ib] *= exp2_hw(gsh[16 * ib + lr]);
 
@@ -747,15 +777,13 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     for (int nb = 0; nb < N / 16; ++nb) sacc[nb] *= dec;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const f32x4 g0 = *(const f32x4*)(&gsh[32 * s + 4 * lq]);
-      const f32x4 g1 = *(const f32x4*)(&gsh[32 * s + 16 + 4 * lq]);
-      const f32x4 d0 = *(const f32x4*)(&dsh[32 * s + 4 * lq]);
-      const f32x4 d1 = *(const f32x4*)(&dsh[32 * s + 16 + 4 * lq]);
+      const f32x4 w0 = *(const f32x4*)(&wsh[32 * s + 4 * lq]);
+      const f32x4 w1 = *(const f32x4*)(&wsh[32 * s + 16 + 4 * lq]);
       f32x4 x0, x1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x0[e] = r.xv[8 * s + e] * (d0[e] * exp2_hw(glast - g0[e]));
-        x1[e] = r.xv[8 * s + 4 + e] * (d1[e] * exp2_hw(glast - g1[e]));
+        x0[e] = r.xv[8 * s + e] * w0[e];
+        x1[e] = r.xv[8 * s + 4 + e] * w1[e];
       }
       u32x4 xp[3];
       split8(x0, x1, xp);
@@ -782,7 +810,10 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[nb]), fres,
                                                so_lane + 64 * nb, 0, 0);
     }
-    __syncthreads();  // every wave's L' blocks are in LDS
+    __syncthreads();  // every wave's L' blocks are in LDS; B, C, g, dt reads are done
+
+    // the next step's operands, while the other waves multiply by L'
+    if (has_next) commit(rn);
 
     // ---- Y^T += X^T L'^T over the 32-token k-steps on or below the
     //      diagonal; rows past the end of the sequence fall outside the range
@@ -811,11 +842,12 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
                                                0);
       }
     }
+    __syncthreads();  // the next step's operands are staged; this step's L' reads are done
   };
 
   for (int k = 0; k < nsteps; k += 2) {
-    body(ra);
-    if (k + 1 < nsteps) body(rb);
+    body(ra, rb, k + 1 < nsteps);
+    if (k + 1 < nsteps) body(rb, ra, k + 2 < nsteps);
   }
 }
 
