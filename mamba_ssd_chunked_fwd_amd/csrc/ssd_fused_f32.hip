@@ -701,6 +701,10 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     prepare(cur.st, nxt);
     r.st = cur.st;
     advance(cur);
+    // B, C, g, dt and D of the step two ahead (their registers were staged
+    // already); x follows once this step's x is consumed
+#pragma unroll
+    for (int j = XV; j < NLOAD; ++j) issue_slot(j, nxt, r);
 
     // ---- this wave's blocks of C B^T (A = B rows j, B = C rows i, k slots
     //      in accumulator order) and from them L' of both heads -> LDS
@@ -757,8 +761,6 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
       split8(sacc[2 * kk], sacc[2 * kk + 1], sf);
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
-        const int j = XV + 4 * kk + ib;
-        if (j < NLOAD) issue_slot(j, nxt, r);
         const int oc = (16 * ib + lr) * CS + 32 * kk + 8 * lq;
         const u32x4 cf[3] = {*(const u32x4*)(cp[0] + oc), *(const u32x4*)(cp[1] + oc),
                              *(const u32x4*)(cp[2] + oc)};
