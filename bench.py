@@ -58,7 +58,7 @@ CONFIG_ORDER = ["tiny_fp32", "small_bf16", "large_bf16", "long_bf16", "wide_fp32
 STAGE_SOURCES = {"chunk_cumsum": ["ssd_chunk_cumsum.hip"],
                  "fwd_pass_state": ["ssd_fwd_pass_state.hip", "ssd_state_two_level.hip"],
                  "compute_out": ["ssd_compute_out.hip"],
-                 "state_and_out": ["ssd_fused_f32.hip"]}
+                 "state_and_out": ["ssd_fused_f32.hip", "ssd_fused_bf16.hip"]}
 THREE_STAGES = ["chunk_cumsum", "fwd_pass_state", "compute_out"]
 FUSED_STAGES = ["chunk_cumsum", "state_and_out"]
 
@@ -68,10 +68,34 @@ def heads_per_pair(w) -> int:
 
 
 def fused(w, cus: int = 256) -> bool:
-    """Whether ssd_forward runs stages 2 and 3 as one kernel for this
-    workload (the library's own rule)."""
-    return (w.dtype == "fp32" and w.chunk_size == 64 and w.dstate == 64
-            and w.batch * w.nheads // heads_per_pair(w) >= cus)
+    """Whether ssd_forward runs stages 2 and 3 as one pass for this
+    workload (the library's own rule): fp32 with 64-token chunks, N = 64 and
+    a (batch, head pair) per CU; or bf16 with N = 128 and an even group
+    size."""
+    if w.dtype == "fp32":
+        return (w.chunk_size == 64 and w.dstate == 64
+                and w.batch * w.nheads // heads_per_pair(w) >= cus)
+    return (w.dstate == 128 and w.headdim == 64 and w.chunk_size in (64, 128, 256)
+            and (w.nheads // w.ngroups) % 2 == 0)
+
+
+def run_plan(w, cus: int = 256) -> dict:
+    """The bf16 fused pass's cut of each chain into runs (the library's own
+    rule): nr runs of R chunks, the run pass over sub-runs of R1 chunks."""
+    nc = w.nchunks
+    pairs = w.batch * w.nheads // 2
+    nr = 1 if pairs >= cus else min(nc, max(1, cus // pairs))
+    R = -(-nc // nr)
+    nr = -(-nc // R)
+    R1 = R
+    if nr > 1:
+        R1 = 1
+        for d in range(R, 0, -1):
+            if R % d == 0 and 2 * pairs * (nr - 1) * (R // d) >= cus:
+                R1 = d
+                break
+    return {"runs": nr, "run_chunks": R, "subrun_chunks": R1,
+            "subruns": (nr - 1) * (R // R1) if nr > 1 else 0}
 
 
 def step_kernels(w, cus: int = 256) -> list:
@@ -152,11 +176,24 @@ def issued_mfma_flop(w) -> dict:
     else:
         out = b * nc * H * (2 * T * P * N + lx16) + b * nc * G * cb
         a2 = 2 * b * L * H * P * N
-    # the fused pass (fp32 on bf16 instructions, six per product): C S^T,
-    # X^T L'^T and the state update per (batch, chunk, head), C B^T once per
-    # (batch, chunk, work item of heads_per_pair heads)
-    fused_issued = 6 * (b * nc * H * (2 * 2 * T * P * N + lx32)
-                        + b * nc * (H // heads_per_pair(w)) * cb)
+    if w.dtype == "fp32":
+        # the fused pass (fp32 on bf16 instructions, six per product): C S^T,
+        # X^T L'^T and the state update per (batch, chunk, head), C B^T once
+        # per (batch, chunk, work item of heads_per_pair heads)
+        fused_issued = 6 * (b * nc * H * (2 * 2 * T * P * N + lx32)
+                            + b * nc * (H // heads_per_pair(w)) * cb)
+    else:
+        # the bf16 fused pass, per 64-token block of each (batch, head): C S^T
+        # and the update with hi + lo of S and of w o x, X^T L'^T with hi + lo
+        # of L' (six 32-token k-steps), C B^T once per head pair (ten 16x16
+        # blocks); plus the run pass over its sub-runs (update only)
+        nblk = -(-L // 64)
+        lx64 = sum(ib // 2 + 1 for ib in range(4)) * 32 * 16 * P * 2
+        cb64 = 10 * 16 * 16 * N * 2
+        per_block = 2 * (2 * 64 * P * N) * 2 + 2 * lx64
+        pl = run_plan(w)
+        run_pass = b * H * pl["subruns"] * pl["subrun_chunks"] * (T // 64) * 2 * (2 * 64 * P * N)
+        fused_issued = b * H * nblk * per_block + b * (H // 2) * nblk * cb64 + run_pass
     return {"fwd_pass_state": a2, "compute_out": out, "state_and_out": fused_issued}
 
 

@@ -1,0 +1,787 @@
+// Stages 2 and 3 in one pass for bf16 inputs (N = 128 state columns, heads
+// of 64, chunks of 64, 128 or 256 tokens), with each (b, h) chain of chunks
+// cut into runs so that enough workgroups walk chains at once.
+//
+// For each (b, h) the state entering chunk c is S_c and
+//   S_{c+1} = 2^{g_last(c)} S_c + sum_{t in c} 2^{g_last(c) - g_t} dt_t x_t B_t^T
+//   Y_c     = 2^{g_i} (C S_c^T) + L' X + D_h X
+// ("Accelerating Mamba-2 with High-Performance Forward Pass Kernels in NVIDIA
+// CUDA Tile": the recurrence of "Kernel 2: fwd_pass_state" and the output of
+// "Kernel 3: compute_out, the Fused Output Kernel" with "Step 2" and
+// "Step 3").  As in the fp32 fused pass, walking the chunks of a (b, h) in
+// order with the state in registers writes every S_c once and never reads
+// one back, and reads x once.  The bf16 layers have too few (b, h) pairs for
+// one walk per pair to fill the chip (96, 160 and 32 of them), so the chunks
+// of a chain are cut into nr runs of R chunks, walked at once:
+//
+// 1. run_state_bf16: for every sub-run k of R1 chunks (R1 divides R) that
+//    lies before the last run, E_k = the state after the sub-run from a zero
+//    start, parked in the states slot of the chunk that follows it.
+// 2. run_passing: S at the sub-run starts, S_{(k+1) R1} = 2^{d_k} S_{k R1} +
+//    E_k with d_k the sum of the sub-run's g_last, in place; only the run
+//    starts are written back (the slots in between are rewritten by 3).
+//    The same jump as stage 2's, over R1 chunks instead of one.
+// 3. fused_pair_bf16: one workgroup per (b, head pair, run), starting from
+//    the run's first state and walking its chunks in 64-token blocks.
+// With one run per chain (enough pairs for the chip) 1 and 2 do not run.
+//
+// A chunk of 128 or 256 tokens is evaluated as 2 or 4 blocks of 64 tokens
+// with the state carried between them in registers: for the tokens of a
+// block, the earlier tokens of the chunk act through the state at the block's
+// start exactly as the earlier chunks act through S_c, so y and the states
+// at chunk boundaries are the same sums, in another order.  g is the
+// chunk's cumulative sum; a block that starts inside a chunk subtracts g of
+// the token before it, which turns g into the block's own cumulative sum.
+#include "ssd_device.h"
+#include "ssd_host.h"
+#include "ssd_launch.h"
+
+#include <type_traits>
+
+namespace ssd {
+namespace {
+
+constexpr int kN = 128;   // state columns of the bf16 fused pass
+constexpr int kTB = 64;   // tokens per block
+
+// Consecutive logical items on one XCD (blocks are dealt round-robin).
+__device__ __forceinline__ int xcd_map(int bid, int total) {
+  if (total % 8) return bid;
+  return (bid % 8) * (total / 8) + bid / 8;
+}
+
+// k-slot order of the columns of C (and the second copy of B): slot
+// position of state column n, as the accumulator layout of S sets it.
+__device__ __forceinline__ int kpos(int c) {
+  return (c & ~31) + 8 * ((c >> 2) & 3) + 4 * ((c >> 4) & 1) + (c & 3);
+}
+
+// eight consecutive fp32 values split into bf16 hi + lo fragments
+__device__ __forceinline__ void split8_2(const f32x4& v0, const f32x4& v1, u32x4& hi,
+                                         u32x4& lo) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    uint32_t h, l;
+    split_bf16(v0[2 * q], v0[2 * q + 1], h, l);
+    hi[q] = h;
+    lo[q] = l;
+    split_bf16(v1[2 * q], v1[2 * q + 1], h, l);
+    hi[2 + q] = h;
+    lo[2 + q] = l;
+  }
+}
+
+// ------------------------------------------------------------------ 1
+// One workgroup (8 waves) per (b, sub-run k, head pair); wave 4 hh + w owns
+// rows 16w..16w+15 of head hh and all N columns, transposed in the
+// accumulators as in the other state kernels (lane: column p, four
+// consecutive n).  The sub-run is consumed in 64-token tiles: w o x (split
+// hi + lo) of both heads and B staged in LDS, read with the transpose read;
+// the tiles two ahead are loading into registers meanwhile.  At each chunk
+// start the accumulated state is decayed by the chunk's 2^{g_last}, then the
+// chunk's tokens add with weights dt_t 2^{g_last - g_t}.  The sub-runs lie
+// before the last run, so every chunk is whole.
+template <int N>
+__global__ __launch_bounds__(512) void run_state_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
+    const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
+    int L, int H, int G, int T, int nc, int R1, int nsub) {
+  constexpr int NT = 512, ST = 64;
+  constexpr int XS = kHeadDim + 16;   // w o x row stride (bf16)
+  constexpr int BS = N + 16;          // B row stride (bf16)
+  constexpr int NB = N / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t whs[2][ST * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t wls[2][ST * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t bts[ST * BS];
+
+  const int npr = H / 2;
+  const int item = xcd_map(blockIdx.x, gridDim.x);
+  const int h0 = (item % npr) * 2;
+  const int k = (item / npr) % nsub;
+  const int b = item / (npr * nsub);
+  const int grp = h0 / (H / G);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = wave >> 2, wr = wave & 3;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int spc = T / ST;          // tiles per chunk
+  const int nst = R1 * spc;        // tiles of the sub-run
+  const int tb = k * R1 * T;       // its first token
+
+  const uint32_t xrow = (uint32_t)H * kHeadDim * 2, brow = (uint32_t)G * N * 2;
+  const uint32_t span = (uint32_t)(R1 * T);
+  const rsrc_t xr = make_rsrc(x + ((size_t)(b * (size_t)L + tb) * H + h0) * kHeadDim,
+                              (span - 1) * xrow + 2 * kHeadDim * 2);
+  const rsrc_t br = make_rsrc(Bm + ((size_t)(b * (size_t)L + tb) * G + grp) * N,
+                              (span - 1) * brow + N * 2);
+  // x unit e = tid + 512 u: token e >> 4, 16-byte piece e & 15 of the pair's
+  // 256-byte row (head (e >> 3) & 1, columns 8 (e & 7)..); the thread's head
+  // picks its g and dt row by offset, so the descriptors stay uniform
+  const int th = (tid >> 3) & 1;
+  const size_t grow = ((size_t)b * H + h0) * L + tb;
+  const rsrc_t gr = make_rsrc(g + grow, ((uint32_t)L + span) * 4);
+  const rsrc_t dr = make_rsrc(dt_t + grow, ((uint32_t)L + span) * 4);
+  const float* gw = g + grow + (size_t)hh * L;   // this wave's head
+
+  uint32_t xo[2], bo[2], go[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + NT * u;
+    xo[u] = (uint32_t)(e >> 4) * xrow + 16 * (e & 15);
+    bo[u] = (uint32_t)(e >> 4) * brow + 16 * (e & 15);
+    go[u] = 4 * ((uint32_t)(e >> 4) + (uint32_t)th * L);
+  }
+  const uint32_t gl_lane = 4 * (uint32_t)th * L;
+
+  struct Regs {
+    u32x4 xv[2], bv[2];
+    float gv[2], dv[2], gl;
+  };
+  auto issue = [&](int s, Regs& r) {
+    const uint32_t t0 = (uint32_t)(s * ST);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      r.xv[u] = load_b128(xr, t0 * xrow + xo[u]);
+      r.bv[u] = load_b128(br, t0 * brow + bo[u]);
+      r.gv[u] = load_f32(gr, 4 * t0 + go[u]);
+      r.dv[u] = load_f32(dr, 4 * t0 + go[u]);
+    }
+    r.gl = load_f32(gr, gl_lane + 4u * (uint32_t)((s / spc) * T + T - 1));   // chunk's g_last
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = (f32x4){0, 0, 0, 0};
+  const int rsel = 4 * lq + (lr >> 2), csel = 4 * (lr & 3);
+
+  auto step = [&](int s, Regs& r) {
+    if (s > 0) __syncthreads();   // the previous tile's LDS reads are done
+    if (s > 0 && s % spc == 0) {
+      const float dec = exp2_hw(gw[(s / spc) * T + T - 1]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[j] *= dec;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + NT * u, t = e >> 4, c8 = e & 7;
+      const float wt = r.dv[u] * exp2_hw(r.gl - r.gv[u]);
+      uint32_t hv[4], lv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        split_bf16(bf16_lo(r.xv[u][q]) * wt, bf16_hi(r.xv[u][q]) * wt, hv[q], lv[q]);
+      *(u32x4*)(whs[th] + t * XS + 8 * c8) = make_u32x4(hv);
+      *(u32x4*)(wls[th] + t * XS + 8 * c8) = make_u32x4(lv);
+      *(u32x4*)(bts + t * BS + 8 * (e & 15)) = r.bv[u];
+    }
+    // the tile two ahead; past the sub-run the loads read zero or unused
+    // words of the same rows, so every path issues the same loads
+    issue(s + 2, r);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < ST / 32; ++kk) {
+      const int wo = (32 * kk + rsel) * XS + 16 * wr + csel;
+      const u32x2 a0 = lds_read_tr16(whs[hh] + wo), a1 = lds_read_tr16(whs[hh] + wo + 16 * XS);
+      const u32x2 c0 = lds_read_tr16(wls[hh] + wo), c1 = lds_read_tr16(wls[hh] + wo + 16 * XS);
+      const u32x4 wxh = {a0[0], a0[1], a1[0], a1[1]};
+      const u32x4 wxl = {c0[0], c0[1], c1[0], c1[1]};
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int bb = (32 * kk + rsel) * BS + 16 * j + csel;
+        const u32x2 e0 = lds_read_tr16(bts + bb), e1 = lds_read_tr16(bts + bb + 16 * BS);
+        const u32x4 bt = {e0[0], e0[1], e1[0], e1[1]};
+        acc[j] = mfma_bf16(bt, wxh, acc[j]);
+        acc[j] = mfma_bf16(bt, wxl, acc[j]);
+      }
+    }
+  };
+
+  Regs ra, rb;
+  issue(0, ra);
+  issue(1, rb);
+#pragma unroll 1
+  for (int s = 0; s + 1 < nst; s += 2) {
+    step(s, ra);
+    step(s + 1, rb);
+  }
+  if (nst & 1) step(nst - 1, ra);
+
+  // E_k into the slot of the chunk after the sub-run
+  float* dst = states + (((size_t)b * H + h0 + hh) * nc + (size_t)(k + 1) * R1) * kHeadDim * N;
+  const int p = 16 * wr + lr;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) *(f32x4*)(dst + (size_t)p * N + 16 * j + 4 * lq) = acc[j];
+}
+
+// ------------------------------------------------------------------ 2
+// A thread owns one 16-byte unit (four consecutive n of one row p) of one
+// (b, h) and walks the sub-runs: S_0 = init (or zero) is written to slot 0,
+// then S_{k R1} = 2^{d_{k-1}} S_{(k-1) R1} + E_{k-1}, stored where k R1
+// starts a run.  The sub-runs' decay sums d_k (sums of their chunks'
+// g_last) are formed first, one sub-run per thread, into LDS.
+template <int N>
+__global__ __launch_bounds__(256) void run_passing_kernel(
+    const float* __restrict__ g, const float* __restrict__ init, float* __restrict__ states,
+    int L, int T, int nc, int R1, int nsub, int spr) {
+  constexpr int UNITS = kHeadDim * N / 4;
+  constexpr int WPB = UNITS / 256;
+  constexpr int D = 4;
+  constexpr int MAXS = 1024;   // sub-runs per pass over the decay sums
+  __shared__ float dsum[MAXS];
+  const int bh = blockIdx.x / WPB;
+  const int u = (blockIdx.x % WPB) * 256 + threadIdx.x;
+  const size_t ss = (size_t)kHeadDim * N;
+  float* st = states + (size_t)bh * nc * ss + 4 * (size_t)u;
+  const float* gh = g + (size_t)bh * L;
+  f32x4 s = init ? *(const f32x4*)(init + bh * ss + 4 * (size_t)u) : (f32x4){0, 0, 0, 0};
+  *(f32x4*)st = s;
+#pragma unroll 1
+  for (int k0 = 0; k0 < nsub; k0 += MAXS) {
+    const int kn = min(MAXS, nsub - k0);
+    __syncthreads();
+    for (int k = threadIdx.x; k < kn; k += 256) {
+      const float* q = gh + (size_t)(k0 + k) * R1 * T + T - 1;
+      float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+      int c = 0;
+      for (; c + 4 <= R1; c += 4) {
+        s0 += q[(size_t)c * T];
+        s1 += q[(size_t)(c + 1) * T];
+        s2 += q[(size_t)(c + 2) * T];
+        s3 += q[(size_t)(c + 3) * T];
+      }
+      for (; c < R1; ++c) s0 += q[(size_t)c * T];
+      dsum[k] = (s0 + s1) + (s2 + s3);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int j0 = 0; j0 < kn; j0 += D) {
+      f32x4 e[D];
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int k = k0 + j0 + j + 1;
+        e[j] = j0 + j < kn ? *(const f32x4*)(st + (size_t)k * R1 * ss) : (f32x4){0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const int k = k0 + j0 + j + 1;
+        if (j0 + j < kn) {
+          s = exp2_hw(dsum[j0 + j]) * s + e[j];
+          if (k % spr == 0) *(f32x4*)(st + (size_t)k * R1 * ss) = s;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 3
+// Head-pair form (8 waves, two per SIMD): waves 4q..4q+3 on head q of the
+// pair, wave 4q + w owning rows p = 16w..16w+15 of that head's state and of
+// its Y^T[p][i] over the block's 64 tokens.
+// * The state stays in accumulators, S[p][16 nb + 4 lq + rr] in lane
+//   (p, lq), and feeds C S^T directly after a hi + lo split: its k slots
+//   follow that layout, n = 32 kk + 16 (e / 4) + 4 lq + e % 4, and C is
+//   staged with its columns in that order.
+// * x of both heads, B and C are staged once per block; x is read back with
+//   the transpose read straight into the operand of X^T L'^T (exact bf16)
+//   and, scaled by w_t = dt_t 2^{g_last - g_t} and split, of the update.
+// * Each of the ten lower 16x16 blocks of C B^T (exact bf16 operands) is
+//   formed once, by one wave (two for waves 0 and 1), and turned into L' of
+//   both heads (hi + lo) in LDS.
+// * Every step's operands are loaded two steps ahead into one of two
+//   register sets, staged after the step's L' barrier while the other waves
+//   multiply by L'.  Uniform address parts go into the buffer descriptors;
+//   their ranges end at the sequence, so rows past it read zero and their
+//   stores are dropped.
+// * Work items are (b, head pair, run), pairs fastest, taken with a stride of
+//   the grid size; a run's blocks are the steps.
+template <bool YBF16>
+__global__ __launch_bounds__(512) void fused_pair_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
+    const uint16_t* __restrict__ Cm, const float* __restrict__ dt_t, const float* __restrict__ g,
+    const float* __restrict__ Dv, const float* __restrict__ init, float* __restrict__ states,
+    float* __restrict__ final_state, void* __restrict__ y, int L, int H, int G, int T, int nc,
+    int R, int nr, int items) {
+  constexpr int NT = 512, TB = kTB, N = kN, NIB = TB / 16, KN = N / 32;
+  constexpr int XS = kHeadDim + 16;   // x tile row stride (bf16)
+  constexpr int BS = N + 16;          // B row stride (bf16), natural column order
+  constexpr int CS = N + 8;           // C and B row stride (bf16), columns in k-slot order
+  constexpr int LS = TB + 8;          // L' row stride (bf16), columns in k-slot order
+  constexpr uint32_t kYB = YBF16 ? 2 : 4;
+  constexpr uint32_t kStateBytes = kHeadDim * N * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][TB * XS];
+  __shared__ __attribute__((aligned(16))) uint16_t bp[TB * BS];
+  __shared__ __attribute__((aligned(16))) uint16_t bq[TB * CS];
+  __shared__ __attribute__((aligned(16))) uint16_t cp[TB * CS];
+  __shared__ __attribute__((aligned(16))) uint16_t lp[2][2][TB * LS];
+  __shared__ __attribute__((aligned(16))) float gs[2][TB], ds[2][TB];
+  __shared__ __attribute__((aligned(16))) float ws[2][TB];   // w_t = dt_t 2^{g_last - g_t}
+  constexpr int YS = 2 * kHeadDim + 4;   // Y tile row stride (fp32): both heads' 64 columns
+  __shared__ __attribute__((aligned(16))) float ys[TB * YS];
+
+  const int nwg = gridDim.x;
+  const int wg = xcd_map(blockIdx.x, nwg);
+  if (wg >= items) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = wave >> 2, w = wave & 3;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int hpg = H / G, npr = H / 2;
+  const int RT = R * T;   // tokens per run
+  const uint32_t xrow = (uint32_t)H * kHeadDim * 2;   // bytes per token of x
+  const uint32_t brow = (uint32_t)G * N * 2;          // bytes per token of B and C
+  const int p = 16 * w + lr;   // this lane's state row (operand row)
+
+  auto run_blocks = [&](int r) {
+    const int tb = r * RT, te = min(tb + RT, L);
+    return (te - tb + TB - 1) / TB;
+  };
+  int nsteps = 0;
+  for (int it = wg; it < items; it += nwg) nsteps += run_blocks((it / npr) % nr);
+
+  // loop-invariant lane offsets (bytes) from each step's descriptor bases:
+  // unit e = tid + 512 u is token e >> 4, 16-byte piece e & 15 of the row
+  // (for x: the pair's two 128-byte head rows side by side)
+  uint32_t xo_lane[2], bo_lane[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + NT * u;
+    xo_lane[u] = (uint32_t)(e >> 4) * xrow + 16 * (e & 15);
+    bo_lane[u] = (uint32_t)(e >> 4) * brow + 16 * (e & 15);
+  }
+  const uint32_t gd_lane = 4 * (uint32_t)lane;
+  const uint32_t so_lane = ((uint32_t)p * N + 4 * lq) * 4;
+
+  // this wave's blocks (ib, jb) of C B^T: waves 0-3 (3, 3-w), waves 4-6
+  // (2, 6-w), wave 7 (1, 0); waves 0 and 1 also (w, w)
+  const int ncb = wave < 2 ? 2 : 1;
+  auto blk_i = [&](int sl) { return sl == 1 ? wave : (wave < 4 ? 3 : (wave < 7 ? 2 : 1)); };
+  auto blk_j = [&](int sl) {
+    return sl == 1 ? wave : (wave < 4 ? 3 - wave : (wave < 7 ? 6 - wave : 0));
+  };
+
+  struct StepP {
+    int b, h0, grp, r, t0;
+    bool live, first;
+  };
+  struct Cursor {
+    int k, blk, nb, it;
+    StepP st;
+  };
+  auto at_item = [&](Cursor& cu) {
+    const int pr = cu.it % npr;
+    cu.st.r = (cu.it / npr) % nr;
+    cu.st.b = cu.it / (npr * nr);
+    cu.st.h0 = 2 * pr;
+    cu.st.grp = cu.st.h0 / hpg;
+    cu.nb = run_blocks(cu.st.r);
+  };
+  auto set_step = [&](Cursor& cu) {
+    cu.st.t0 = cu.st.r * RT + TB * cu.blk;
+    cu.st.first = cu.blk == 0;
+    cu.st.live = cu.k < nsteps;
+  };
+  auto advance = [&](Cursor& cu) {
+    ++cu.k;
+    if (++cu.blk == cu.nb) {
+      cu.blk = 0;
+      cu.it += nwg;
+      if (cu.k < nsteps) at_item(cu);
+    }
+    set_step(cu);
+  };
+
+  struct Regs {
+    u32x4 xu[2], bu[2], cu[2];
+    float gv, dv;   // g and dt (waves 0 and 2: heads 0 and 1)
+    StepP st;       // the step these registers were loaded for
+  };
+  constexpr int NLOAD = 8;
+  struct Src {
+    rsrc_t xr, br, crr, gr, dr;
+  };
+  const bool gwave = wave == 0 || wave == 2;
+  auto prepare = [&](const StepP& st, Src& sc) {
+    const int t0 = st.t0;
+    const uint32_t rows = (uint32_t)(L - t0);
+    sc.xr = make_rsrc(x + (((size_t)st.b * L + t0) * H + st.h0) * kHeadDim,
+                      st.live ? (rows * H - st.h0) * (kHeadDim * 2) : 0u);
+    const size_t bcb = (((size_t)st.b * L + t0) * G + st.grp) * N;
+    const uint32_t bcr = st.live ? (rows * G - st.grp) * (N * 2) : 0u;
+    sc.br = make_rsrc(Bm + bcb, bcr);
+    sc.crr = make_rsrc(Cm + bcb, bcr);
+    // g and dt of both heads: wave 0 head 0, wave 2 head 1
+    const size_t gro = ((size_t)st.b * H + st.h0 + ((wave >> 1) & 1)) * L + t0;
+    const bool gl = st.live && gwave;
+    sc.gr = make_rsrc(g + gro, gl ? rows * 4 : 0u);
+    sc.dr = make_rsrc(dt_t + gro, gl ? rows * 4 : 0u);
+  };
+  auto issue_slot = [&](int j, const Src& sc, Regs& r) {
+    if (j < 2) {
+      r.xu[j] = load_b128(sc.xr, xo_lane[j]);
+    } else if (j < 4) {
+      r.bu[j - 2] = load_b128(sc.br, bo_lane[j - 2]);
+    } else if (j < 6) {
+      r.cu[j - 4] = load_b128(sc.crr, bo_lane[j - 4]);
+    } else if (j == 6) {
+      r.gv = load_f32(sc.gr, gd_lane);
+    } else {
+      r.dv = load_f32(sc.dr, gd_lane);
+    }
+  };
+
+  f32x4 sacc[N / 16];   // S[p][16 nb + 4 lq + rr] of this wave's head
+  f32x4 cbr[2];         // (B C^T)[16 jb + 4 lq + rr][16 ib + lr] of this wave's blocks
+
+  // L' blocks that stay zero: (ib 0, jb 1) and (ib 2, jb 3), read as the
+  // upper halves of 32-token k-steps on the diagonal
+  for (int e = tid; e < 2 * 2 * 16 * 16; e += NT) {
+    const int hh = e >> 9, blk = (e >> 8) & 1, r = (e >> 4) & 15, c = e & 15;
+    const int i = blk == 0 ? r : 32 + r, j = blk == 0 ? 16 + c : 48 + c;
+    lp[hh][0][i * LS + kpos(j)] = 0;
+    lp[hh][1][i * LS + kpos(j)] = 0;
+  }
+
+  // D_h of the pair's heads for the step being computed (set when a step is
+  // staged: an item's first step reads them); raw g of the last token of
+  // the staged block (waves 0 and 2), the g before the next block when
+  // that block continues a chunk
+  float dcur[2] = {0.0f, 0.0f};
+  float gprev = 0.0f;
+
+  Regs ra, rb;
+  Cursor cur;
+  cur.k = 0;
+  cur.blk = 0;
+  cur.it = wg;
+  at_item(cur);
+  set_step(cur);
+  {
+    Src sc;
+    prepare(cur.st, sc);
+    ra.st = cur.st;
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) issue_slot(j, sc, ra);
+    advance(cur);
+    prepare(cur.st, sc);
+    rb.st = cur.st;
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) issue_slot(j, sc, rb);
+    advance(cur);
+  }
+
+  // Staging of a step from its registers: x, B, C, g, dt and w of both
+  // heads; the run's first state into the accumulators at a run start; S
+  // to the states at a chunk start.  It runs in the previous step's last
+  // phase, which reads only the L' planes.
+  auto commit = [&](const Regs& r) {
+    const StepP st = r.st;
+    const size_t hrow = (size_t)st.b * H + st.h0 + hq;
+    if (st.first) {
+      dcur[0] = Dv[st.h0];
+      dcur[1] = Dv[st.h0 + 1];
+      // the run's first state: init_state (or zero: an empty range) for a
+      // single run, else the slot the run passing wrote
+      rsrc_t ires;
+      if (nr > 1)
+        ires = make_rsrc(states + (hrow * nc + (size_t)st.r * R) * (kHeadDim * N), kStateBytes);
+      else
+        ires = init ? make_rsrc(init + hrow * (kHeadDim * N), kStateBytes)
+                    : make_rsrc(states, 0u);
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb) sacc[nb] = load_f32x4(ires, so_lane + 64 * nb);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + NT * u, t = e >> 4, c = e & 15;
+      *(u32x4*)(xs[(e >> 3) & 1] + t * XS + 8 * (e & 7)) = r.xu[u];
+      *(u32x4*)(bp + t * BS + 8 * c) = r.bu[u];
+      const int o0 = t * CS + kpos(8 * c), o1 = t * CS + kpos(8 * c + 4);
+      *(u32x2*)(bq + o0) = (u32x2){r.bu[u][0], r.bu[u][1]};
+      *(u32x2*)(bq + o1) = (u32x2){r.bu[u][2], r.bu[u][3]};
+      *(u32x2*)(cp + o0) = (u32x2){r.cu[u][0], r.cu[u][1]};
+      *(u32x2*)(cp + o1) = (u32x2){r.cu[u][2], r.cu[u][3]};
+    }
+    if (gwave) {
+      // g relative to the block, dt and the update weight of one head:
+      // lane = token; tokens past the end read g = dt = 0 (w = 0) and get
+      // g = 0
+      const int hh = wave >> 1;
+      const int nt = min(TB, L - st.t0);
+      const int gl = __builtin_amdgcn_readlane(__float_as_int(r.gv), nt - 1);
+      // a block inside a chunk follows a whole block of the same chunk
+      const float gb = st.t0 % T != 0 ? gprev : 0.0f;
+      gprev = __int_as_float(gl);
+      gs[hh][lane] = lane < nt ? r.gv - gb : 0.0f;
+      ds[hh][lane] = r.dv;
+      ws[hh][lane] = r.dv * exp2_hw(__int_as_float(gl) - r.gv);
+    }
+    if (st.t0 % T == 0) {
+      const rsrc_t sres =
+          make_rsrc(states + (hrow * nc + st.t0 / T) * (kHeadDim * N), kStateBytes);
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[nb]), sres,
+                                               so_lane + 64 * nb, 0, 0);
+    }
+  };
+  commit(ra);
+  __syncthreads();
+
+  // step k from the registers r (staged already); rn holds step k + 1
+  auto body = [&](Regs& r, const Regs& rn, bool has_next) {
+    const StepP st = r.st;
+    const int h = st.h0 + hq;
+    const int t0 = st.t0;
+    const int nt = min(TB, L - t0);
+    const size_t hrow = (size_t)st.b * H + h;
+    const float Dh[2] = {dcur[0], dcur[1]};
+    Src nxt;
+    prepare(cur.st, nxt);
+    r.st = cur.st;
+    advance(cur);
+    // every operand of the step two ahead, in one burst
+#pragma unroll
+    for (int j = 0; j < NLOAD; ++j) issue_slot(j, nxt, r);
+
+    // ---- this wave's blocks of C B^T (A = B rows j, B = C rows i, k slots
+    //      in accumulator order) and from them L' of both heads -> LDS
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (sl < ncb) {
+        const int ib = blk_i(sl), jb = blk_j(sl);
+        f32x4 acc = (f32x4){0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk) {
+          const u32x4 bf = *(const u32x4*)(bq + (16 * jb + lr) * CS + 32 * kk + 8 * lq);
+          const u32x4 cf = *(const u32x4*)(cp + (16 * ib + lr) * CS + 32 * kk + 8 * lq);
+          acc = mfma_bf16(bf, cf, acc);
+        }
+        cbr[sl] = acc;
+      }
+    }
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      if (sl < ncb) {
+        const int ib = blk_i(sl), jb = blk_j(sl);
+        const int i = 16 * ib + lr, j0 = 16 * jb + 4 * lq;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float gi = gs[hh][i];
+          const f32x4 gj = *(const f32x4*)(&gs[hh][j0]);
+          const f32x4 dj = *(const f32x4*)(&ds[hh][j0]);
+          f32x4 v;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int j = j0 + rr;
+            float wv = cbr[sl][rr] * (exp2_hw(gi - gj[rr]) * dj[rr]);
+            if (j == i) wv += Dh[hh];
+            v[rr] = j <= i ? wv : 0.0f;
+          }
+          uint32_t h0, l0, h1, l1;
+          split_bf16(v[0], v[1], h0, l0);
+          split_bf16(v[2], v[3], h1, l1);
+          const int o = i * LS + kpos(j0);
+          *(u32x2*)(lp[hh][0] + o) = (u32x2){h0, h1};
+          *(u32x2*)(lp[hh][1] + o) = (u32x2){l0, l1};
+        }
+      }
+    }
+
+    // ---- this head's x tile as X^T fragments: lane (p, lq) holds tokens
+    //      32 s + 16 (e / 4) + 4 lq + e % 4 of column p
+    u32x4 xa[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int xo = (32 * s + 4 * lq + (lr >> 2)) * XS + 16 * w + 4 * (lr & 3);
+      const u32x2 a0 = lds_read_tr16(xs[hq] + xo);
+      const u32x2 a1 = lds_read_tr16(xs[hq] + xo + 16 * XS);
+      xa[s] = (u32x4){a0[0], a0[1], a1[0], a1[1]};
+    }
+
+    // ---- Y^T = S C^T, A = S from the accumulators (hi + lo), B = C rows
+    f32x4 yacc[NIB];
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) yacc[ib] = (f32x4){0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < KN; ++kk) {
+      u32x4 sh, sl;
+      split8_2(sacc[2 * kk], sacc[2 * kk + 1], sh, sl);
+#pragma unroll
+      for (int ib = 0; ib < NIB; ++ib) {
+        const u32x4 cf = *(const u32x4*)(cp + (16 * ib + lr) * CS + 32 * kk + 8 * lq);
+        yacc[ib] = mfma_bf16(sh, cf, yacc[ib]);
+        yacc[ib] = mfma_bf16(sl, cf, yacc[ib]);
+      }
+    }
+    const float* gsh = gs[hq];
+    const float* wsh = ws[hq];
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) yacc[ib] *= exp2_hw(gsh[16 * ib + lr]);
+
+    // ---- state: S <- 2^{g_last} S + B^T X', X' = w o x on this lane's tokens
+    const float dec = exp2_hw(gsh[nt - 1]);
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) sacc[nb] *= dec;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f32x4 w0 = *(const f32x4*)(&wsh[32 * s + 4 * lq]);
+      const f32x4 w1 = *(const f32x4*)(&wsh[32 * s + 16 + 4 * lq]);
+      const f32x4 x0 = {bf16_lo(xa[s][0]) * w0[0], bf16_hi(xa[s][0]) * w0[1],
+                        bf16_lo(xa[s][1]) * w0[2], bf16_hi(xa[s][1]) * w0[3]};
+      const f32x4 x1 = {bf16_lo(xa[s][2]) * w1[0], bf16_hi(xa[s][2]) * w1[1],
+                        bf16_lo(xa[s][3]) * w1[2], bf16_hi(xa[s][3]) * w1[3]};
+      u32x4 xh, xl;
+      split8_2(x0, x1, xh, xl);
+      const int bo = (32 * s + 4 * lq + (lr >> 2)) * BS + 4 * (lr & 3);
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb) {
+        const u32x2 a0 = lds_read_tr16(bp + bo + 16 * nb);
+        const u32x2 a1 = lds_read_tr16(bp + bo + 16 * BS + 16 * nb);
+        const u32x4 bt = {a0[0], a0[1], a1[0], a1[1]};
+        sacc[nb] = mfma_bf16(bt, xh, sacc[nb]);
+        sacc[nb] = mfma_bf16(bt, xl, sacc[nb]);
+      }
+    }
+    if (t0 + TB >= L && final_state) {
+      const rsrc_t fres = make_rsrc(final_state + hrow * (kHeadDim * N), kStateBytes);
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[nb]), fres,
+                                               so_lane + 64 * nb, 0, 0);
+    }
+    __syncthreads();  // every wave's L' blocks are in LDS; x, B, C, g, dt reads are done
+
+    // the next step's operands, while the other waves multiply by L'
+    if (has_next) commit(rn);
+
+    // ---- Y^T += X^T L'^T over the 32-token k-steps on or below the
+    //      diagonal, into the block's Y tile in LDS (token rows, both heads'
+    //      columns side by side)
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (2 * s <= ib) {
+          const int ol = (16 * ib + lr) * LS + 32 * s + 8 * lq;
+          const u32x4 lh = *(const u32x4*)(lp[hq][0] + ol);
+          const u32x4 ll = *(const u32x4*)(lp[hq][1] + ol);
+          yacc[ib] = mfma_bf16(xa[s], lh, yacc[ib]);
+          yacc[ib] = mfma_bf16(xa[s], ll, yacc[ib]);
+        }
+      }
+      *(f32x4*)(ys + (16 * ib + lr) * YS + hq * kHeadDim + p - lr + 4 * lq) = yacc[ib];
+    }
+    __syncthreads();  // the next step's operands and the Y tile are staged; L' reads are done
+
+    // ---- the Y tile to y in whole rows: the pair's two head rows of a
+    //      token are one 512-byte run (256 with bf16 y), so a wave writes two
+    //      such runs per instruction; rows past the end of the sequence fall
+    //      outside the range.  (The tile is rewritten only after the next
+    //      step's first barrier, which every wave reaches after these reads.)
+    const rsrc_t yres =
+        make_rsrc((char*)y + (((size_t)st.b * L + t0) * H + st.h0) * kHeadDim * kYB,
+                  ((uint32_t)(L - t0) * H - st.h0) * kHeadDim * kYB);
+#pragma unroll
+    for (int j = 0; j < TB * 2 * kHeadDim / 4 / NT; ++j) {
+      const int c = tid + NT * j, i = c >> 5, c4 = c & 31;
+      const f32x4 v = *(const f32x4*)(ys + i * YS + 4 * c4);
+      const uint32_t yo = ((uint32_t)i * H * kHeadDim + 4 * c4) * kYB;
+      if constexpr (YBF16) {
+        __builtin_amdgcn_raw_buffer_store_b64(
+            (u32x2){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, yres, yo, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yres, yo, 0, 0);
+      }
+    }
+  };
+
+  for (int k = 0; k < nsteps; k += 2) {
+    body(ra, rb, k + 1 < nsteps);
+    if (k + 1 < nsteps) body(rb, ra, k + 2 < nsteps);
+  }
+}
+
+// Runs per chain and sub-runs for the shape: as many runs as keep one
+// workgroup (b, head pair, run) per CU, of equal length; sub-runs the
+// longest divisor of the run that still gives the first kernel a
+// workgroup for every second CU.
+struct RunPlan {
+  int nr, R, R1, nsub;
+};
+
+RunPlan plan_runs(const Shape& s, int cus) {
+  const int nc = (int)s.nchunks();
+  const int64_t pairs = s.batch * s.nheads / 2;
+  int nr = pairs >= cus ? 1 : (int)(cus / pairs);
+  if (nr > nc) nr = nc;
+  if (nr < 1) nr = 1;
+  const int R = (nc + nr - 1) / nr;
+  nr = (nc + R - 1) / R;
+  RunPlan pl{nr, R, R, 0};
+  if (nr > 1) {
+    pl.R1 = 1;
+    for (int d = R; d >= 1; --d) {
+      if (R % d == 0 && 2 * pairs * ((int64_t)(nr - 1) * (R / d)) >= cus) {
+        pl.R1 = d;
+        break;
+      }
+    }
+    pl.nsub = (nr - 1) * (R / pl.R1);
+  }
+  return pl;
+}
+
+template <bool YBF16>
+int launch_pair_bf16(const void* x, const void* B, const void* C, const float* dt_t,
+                     const float* g, const float* D, const float* init, float* states,
+                     float* fin, void* y, const Shape& s, const RunPlan& pl, hipStream_t st) {
+  static PerDeviceInt resident;
+  const int slots = resident.get([&](int dev) {
+    return resident_slots((const void*)fused_pair_bf16<YBF16>, 512, dev);
+  });
+  if (slots <= 0) return (int)hipErrorInvalidDevice;
+  const int items = (int)(s.batch * (s.nheads / 2) * pl.nr);
+  const unsigned grid = (unsigned)(items < slots ? items : slots);
+  hipLaunchKernelGGL((fused_pair_bf16<YBF16>), dim3(grid), dim3(512), 0, st,
+                     (const uint16_t*)x, (const uint16_t*)B, (const uint16_t*)C, dt_t, g, D,
+                     init, states, fin, y, (int)s.seqlen, (int)s.nheads, (int)s.ngroups,
+                     (int)s.chunk, (int)s.nchunks(), pl.R, pl.nr, items);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+bool fused_bf16_applies(const Shape& s, bool bf16_in) {
+  return bf16_in && s.dstate == kN && s.headdim == kHeadDim &&
+         (s.chunk == 64 || s.chunk == 128 || s.chunk == 256) &&
+         (s.nheads / s.ngroups) % 2 == 0;
+}
+
+int launch_fused_bf16(const void* x, const void* B, const void* C, const float* dt_t,
+                      const float* g, const float* D, const float* init, float* states,
+                      float* fin, void* y, bool bf16_out, const Shape& s, void* stream) {
+  clear_launch_error();
+  hipStream_t st = (hipStream_t)stream;
+  static PerDeviceInt cus_cache;
+  int cus = cus_cache.get(query_cus);
+  if (cus <= 0) cus = 256;
+  const RunPlan pl = plan_runs(s, cus);
+  if (pl.nr > 1) {
+    const int nc = (int)s.nchunks();
+    const unsigned g1 = (unsigned)(s.batch * (s.nheads / 2) * pl.nsub);
+    hipLaunchKernelGGL((run_state_bf16<kN>), dim3(g1), dim3(512), 0, st, (const uint16_t*)x,
+                       (const uint16_t*)B, dt_t, g, states, (int)s.seqlen, (int)s.nheads,
+                       (int)s.ngroups, (int)s.chunk, nc, pl.R1, pl.nsub);
+    int err = (int)hipGetLastError();
+    if (err) return err;
+    const unsigned g2 = (unsigned)(s.batch * s.nheads * (kHeadDim * kN / 4 / 256));
+    hipLaunchKernelGGL((run_passing_kernel<kN>), dim3(g2), dim3(256), 0, st, g, init, states,
+                       (int)s.seqlen, (int)s.chunk, nc, pl.R1, pl.nsub, pl.R / pl.R1);
+    err = (int)hipGetLastError();
+    if (err) return err;
+  }
+  if (bf16_out) return launch_pair_bf16<true>(x, B, C, dt_t, g, D, init, states, fin, y, s, pl, st);
+  return launch_pair_bf16<false>(x, B, C, dt_t, g, D, init, states, fin, y, s, pl, st);
+}
+
+}  // namespace ssd

@@ -912,6 +912,9 @@ int launch_state_and_out(const void* x, const void* B, const void* C, const floa
     return launch_fused((const float*)x, (const float*)B, (const float*)C, dt_t, g, D,
                         init_state, states, final_state, y, bf16_out, s, (hipStream_t)stream);
   }
+  if (fused_bf16_applies(s, bf16_in))
+    return launch_fused_bf16(x, B, C, dt_t, g, D, init_state, states, final_state, y, bf16_out,
+                             s, stream);
   int err = launch_fwd_pass_state(x, B, dt_t, g, init_state, states, final_state, bf16_in, s,
                                   stream);
   if (err == 0)

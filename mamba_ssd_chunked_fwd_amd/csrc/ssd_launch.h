@@ -41,6 +41,16 @@ int launch_state_and_out(const void* x, const void* B, const void* C, const floa
                          float* final_state, void* y, bool bf16_in, bool bf16_out,
                          const Shape& s, void* stream);
 
+// Stages 2 and 3 as one pass for bf16 inputs with N = 128 and an even group
+// size (heads taken in pairs): a run pass and a run passing (when the chains
+// are cut into runs), then the fused head-pair kernel.  The states buffer
+// holds the runs' intermediate results until the fused kernel overwrites
+// them, so no other memory is used.
+bool fused_bf16_applies(const Shape& s, bool bf16_in);
+int launch_fused_bf16(const void* x, const void* B, const void* C, const float* dt_t,
+                      const float* g, const float* D, const float* init, float* states,
+                      float* fin, void* y, bool bf16_out, const Shape& s, void* stream);
+
 // The two-level form of stage 2 (chunk_state writes each chunk's zero-state
 // contribution into the slot of the state it feeds; state_passing turns the
 // slots into the states in place).  With park / parked, the last chunk's
