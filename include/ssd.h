@@ -177,11 +177,16 @@ ssd_status ssd_compute_out(const void *x, const void *B, const void *C,
 /*
  * Stages 2 and 3 in one call: ssd_fwd_pass_state then ssd_compute_out on the
  * same arguments, with the same results (equal up to the order of fp32
- * roundings).  For fp32 inputs, 64-token chunks and dstate 64, when the
- * batch holds at least one (b, head pair) per compute unit, the two run as
- * one kernel that carries each head's state from chunk to chunk in
- * registers, so x is read once and the states are written but not read back
- * (the pages' two kernels, fused; [P1 "Kernel 2"; P1 "Kernel 3"]).
+ * roundings).  Two shape classes run as one pass that carries each head's
+ * state from chunk to chunk in registers, so x is read once and the states
+ * are written but not read back (the pages' two kernels, fused; [P1
+ * "Kernel 2"; P1 "Kernel 3"]):
+ *   - fp32 inputs, 64-token chunks and dstate 64, when the batch holds at
+ *     least one (b, head pair) per compute unit;
+ *   - bf16 inputs with dstate 128 and an even number of heads per group;
+ *     the chains of chunks are cut into runs walked at once, each run
+ *     starting from a state that two short kernels compute first (they
+ *     use the states buffer as their only working memory).
  *   x, B, C, dt_t, g, D as for the two stages; init_state [b, H, P, N] fp32
  *   or NULL; states [b, H, nc, P, N] fp32 (written); final_state [b, H, P, N]
  *   fp32 or NULL; y [b, L, H, P] in y_dtype (written).
