@@ -75,24 +75,27 @@ __device__ __forceinline__ void split8_2(const f32x4& v0, const f32x4& v1, u32x4
 // One workgroup (8 waves) per (b, sub-run k, head pair); wave 4 hh + w owns
 // rows 16w..16w+15 of head hh and all N columns, transposed in the
 // accumulators as in the other state kernels (lane: column p, four
-// consecutive n).  The sub-run is consumed in 64-token tiles: w o x (split
-// hi + lo) of both heads and B staged in LDS, read with the transpose read;
-// the tiles two ahead are loading into registers meanwhile.  At each chunk
-// start the accumulated state is decayed by the chunk's 2^{g_last}, then the
-// chunk's tokens add with weights dt_t 2^{g_last - g_t}.  The sub-runs lie
-// before the last run, so every chunk is whole.
+// consecutive n).  The sub-run is consumed in 64-token tiles through two
+// LDS buffers: while the waves multiply tile s out of one, they stage tile
+// s + 1 (x of both heads as loaded, B, and the weights w_t = dt_t
+// 2^{g_last - g_t}) into the other from registers, and the loads of tile
+// s + 3 go out; one barrier per tile.  Each wave reads its x columns with
+// the transpose read, scales them by w and splits them (hi + lo) itself, as
+// the fused kernel's update does.  At each chunk start the accumulated
+// state is decayed by the chunk's 2^{g_last} before the chunk's tokens add.
+// The sub-runs lie before the last run, so every chunk is whole.
 template <int N>
 __global__ __launch_bounds__(512) void run_state_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
     int L, int H, int G, int T, int nc, int R1, int nsub) {
   constexpr int NT = 512, ST = 64;
-  constexpr int XS = kHeadDim + 16;   // w o x row stride (bf16)
+  constexpr int XS = kHeadDim + 16;   // x row stride (bf16)
   constexpr int BS = N + 16;          // B row stride (bf16)
   constexpr int NB = N / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t whs[2][ST * XS];
-  __shared__ __attribute__((aligned(16))) uint16_t wls[2][ST * XS];
-  __shared__ __attribute__((aligned(16))) uint16_t bts[ST * BS];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][2][ST * XS];   // [buffer][head]
+  __shared__ __attribute__((aligned(16))) uint16_t bts[2][ST * BS];
+  __shared__ __attribute__((aligned(16))) float wts[2][2][ST];          // [buffer][head]
 
   const int npr = H / 2;
   const int item = xcd_map(blockIdx.x, gridDim.x);
@@ -114,10 +117,13 @@ __global__ __launch_bounds__(512) void run_state_bf16(
                               (span - 1) * xrow + 2 * kHeadDim * 2);
   const rsrc_t br = make_rsrc(Bm + ((size_t)(b * (size_t)L + tb) * G + grp) * N,
                               (span - 1) * brow + N * 2);
-  // x unit e = tid + 512 u: token e >> 4, 16-byte piece e & 15 of the pair's
-  // 256-byte row (head (e >> 3) & 1, columns 8 (e & 7)..); the thread's head
-  // picks its g and dt row by offset, so the descriptors stay uniform
+  // unit e = tid + 512 u: token e >> 4, 16-byte piece e & 15 of the pair's
+  // 256-byte x row (head (e >> 3) & 1, columns 8 (e & 7)..) and of the B
+  // row; the thread's head picks its g and dt row by offset, so the
+  // descriptors stay uniform.  One thread in eight (e & 7 == 0) also forms
+  // w_t of its (head, token).
   const int th = (tid >> 3) & 1;
+  const bool wthr = (tid & 7) == 0;
   const size_t grow = ((size_t)b * H + h0) * L + tb;
   const rsrc_t gr = make_rsrc(g + grow, ((uint32_t)L + span) * 4);
   const rsrc_t dr = make_rsrc(dt_t + grow, ((uint32_t)L + span) * 4);
@@ -137,6 +143,8 @@ __global__ __launch_bounds__(512) void run_state_bf16(
     u32x4 xv[2], bv[2];
     float gv[2], dv[2], gl;
   };
+  // loads of tile s; past the sub-run they read zero (x, B) or words of the
+  // same rows (g, dt) that are never used
   auto issue = [&](int s, Regs& r) {
     const uint32_t t0 = (uint32_t)(s * ST);
 #pragma unroll
@@ -148,62 +156,73 @@ __global__ __launch_bounds__(512) void run_state_bf16(
     }
     r.gl = load_f32(gr, gl_lane + 4u * (uint32_t)((s / spc) * T + T - 1));   // chunk's g_last
   };
+  auto stage = [&](const Regs& r, int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + NT * u, t = e >> 4;
+      *(u32x4*)(xs[buf][th] + t * XS + 8 * (e & 7)) = r.xv[u];
+      *(u32x4*)(bts[buf] + t * BS + 8 * (e & 15)) = r.bv[u];
+      if (wthr) wts[buf][th][t] = r.dv[u] * exp2_hw(r.gl - r.gv[u]);
+    }
+  };
 
   f32x4 acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = (f32x4){0, 0, 0, 0};
   const int rsel = 4 * lq + (lr >> 2), csel = 4 * (lr & 3);
 
-  auto step = [&](int s, Regs& r) {
-    if (s > 0) __syncthreads();   // the previous tile's LDS reads are done
+  // tile s from buffer s & 1; stage tile s + 1 from rn into the other
+  // buffer, then load tile s + 3 into rn
+  auto step = [&](int s, Regs& rn) {
+    const int buf = s & 1;
+    stage(rn, buf ^ 1);
+    issue(s + 3, rn);
     if (s > 0 && s % spc == 0) {
       const float dec = exp2_hw(gw[(s / spc) * T + T - 1]);
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[j] *= dec;
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = tid + NT * u, t = e >> 4, c8 = e & 7;
-      const float wt = r.dv[u] * exp2_hw(r.gl - r.gv[u]);
-      uint32_t hv[4], lv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        split_bf16(bf16_lo(r.xv[u][q]) * wt, bf16_hi(r.xv[u][q]) * wt, hv[q], lv[q]);
-      *(u32x4*)(whs[th] + t * XS + 8 * c8) = make_u32x4(hv);
-      *(u32x4*)(wls[th] + t * XS + 8 * c8) = make_u32x4(lv);
-      *(u32x4*)(bts + t * BS + 8 * (e & 15)) = r.bv[u];
-    }
-    // the tile two ahead; past the sub-run the loads read zero or unused
-    // words of the same rows, so every path issues the same loads
-    issue(s + 2, r);
-    __syncthreads();
-#pragma unroll
     for (int kk = 0; kk < ST / 32; ++kk) {
-      const int wo = (32 * kk + rsel) * XS + 16 * wr + csel;
-      const u32x2 a0 = lds_read_tr16(whs[hh] + wo), a1 = lds_read_tr16(whs[hh] + wo + 16 * XS);
-      const u32x2 c0 = lds_read_tr16(wls[hh] + wo), c1 = lds_read_tr16(wls[hh] + wo + 16 * XS);
-      const u32x4 wxh = {a0[0], a0[1], a1[0], a1[1]};
-      const u32x4 wxl = {c0[0], c0[1], c1[0], c1[1]};
+      // this wave's x columns, tokens 32 kk + 16 (e / 4) + 4 lq + e % 4,
+      // scaled by w and split
+      const int xo2 = (32 * kk + rsel) * XS + 16 * wr + csel;
+      const u32x2 a0 = lds_read_tr16(xs[buf][hh] + xo2);
+      const u32x2 a1 = lds_read_tr16(xs[buf][hh] + xo2 + 16 * XS);
+      const f32x4 w0 = *(const f32x4*)(&wts[buf][hh][32 * kk + 4 * lq]);
+      const f32x4 w1 = *(const f32x4*)(&wts[buf][hh][32 * kk + 16 + 4 * lq]);
+      const f32x4 x0 = {bf16_lo(a0[0]) * w0[0], bf16_hi(a0[0]) * w0[1], bf16_lo(a0[1]) * w0[2],
+                        bf16_hi(a0[1]) * w0[3]};
+      const f32x4 x1 = {bf16_lo(a1[0]) * w1[0], bf16_hi(a1[0]) * w1[1], bf16_lo(a1[1]) * w1[2],
+                        bf16_hi(a1[1]) * w1[3]};
+      u32x4 wxh, wxl;
+      split8_2(x0, x1, wxh, wxl);
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int bb = (32 * kk + rsel) * BS + 16 * j + csel;
-        const u32x2 e0 = lds_read_tr16(bts + bb), e1 = lds_read_tr16(bts + bb + 16 * BS);
+        const u32x2 e0 = lds_read_tr16(bts[buf] + bb), e1 = lds_read_tr16(bts[buf] + bb + 16 * BS);
         const u32x4 bt = {e0[0], e0[1], e1[0], e1[1]};
         acc[j] = mfma_bf16(bt, wxh, acc[j]);
         acc[j] = mfma_bf16(bt, wxl, acc[j]);
       }
     }
+    __syncthreads();   // tile s + 1 is staged; tile s's reads are done
   };
 
   Regs ra, rb;
   issue(0, ra);
   issue(1, rb);
+  stage(ra, 0);
+  issue(2, ra);
+  __syncthreads();
+  // steps alternate register sets: step s stages tile s + 1 from the set
+  // that holds it (rb for even s) and reloads that set with tile s + 3
 #pragma unroll 1
   for (int s = 0; s + 1 < nst; s += 2) {
-    step(s, ra);
-    step(s + 1, rb);
+    step(s, rb);
+    step(s + 1, ra);
   }
-  if (nst & 1) step(nst - 1, ra);
+  if (nst & 1) step(nst - 1, rb);
 
   // E_k into the slot of the chunk after the sub-run
   float* dst = states + (((size_t)b * H + h0 + hh) * nc + (size_t)(k + 1) * R1) * kHeadDim * N;
