@@ -127,7 +127,6 @@ __global__ __launch_bounds__(512) void run_state_bf16(
   const size_t grow = ((size_t)b * H + h0) * L + tb;
   const rsrc_t gr = make_rsrc(g + grow, ((uint32_t)L + span) * 4);
   const rsrc_t dr = make_rsrc(dt_t + grow, ((uint32_t)L + span) * 4);
-  const float* gw = g + grow + (size_t)hh * L;   // this wave's head
 
   uint32_t xo[2], bo[2], go[2];
 #pragma unroll
@@ -138,10 +137,12 @@ __global__ __launch_bounds__(512) void run_state_bf16(
     go[u] = 4 * ((uint32_t)(e >> 4) + (uint32_t)th * L);
   }
   const uint32_t gl_lane = 4 * (uint32_t)th * L;
+  const uint32_t gl_wave = 4 * (uint32_t)hh * L;
 
   struct Regs {
     u32x4 xv[2], bv[2];
-    float gv[2], dv[2], gl;
+    float gv[2], dv[2], gl;   // g, dt of the thread's units; g_last of their head's chunk
+    float glw;                // g_last of this wave's head's chunk
   };
   // loads of tile s; past the sub-run they read zero (x, B) or words of the
   // same rows (g, dt) that are never used
@@ -154,7 +155,9 @@ __global__ __launch_bounds__(512) void run_state_bf16(
       r.gv[u] = load_f32(gr, 4 * t0 + go[u]);
       r.dv[u] = load_f32(dr, 4 * t0 + go[u]);
     }
-    r.gl = load_f32(gr, gl_lane + 4u * (uint32_t)((s / spc) * T + T - 1));   // chunk's g_last
+    const uint32_t tl = 4u * (uint32_t)((s / spc) * T + T - 1);   // the chunk's last token
+    r.gl = load_f32(gr, gl_lane + tl);
+    r.glw = load_f32(gr, gl_wave + tl);
   };
   auto stage = [&](const Regs& r, int buf) {
 #pragma unroll
@@ -171,14 +174,20 @@ __global__ __launch_bounds__(512) void run_state_bf16(
   for (int j = 0; j < NB; ++j) acc[j] = (f32x4){0, 0, 0, 0};
   const int rsel = 4 * lq + (lr >> 2), csel = 4 * (lr & 3);
 
+  // g_last of the chunk of the tile being multiplied (this wave's head),
+  // taken from the tile's registers when it is staged
+  float glw_cur = 0.0f;
+
   // tile s from buffer s & 1; stage tile s + 1 from rn into the other
   // buffer, then load tile s + 3 into rn
   auto step = [&](int s, Regs& rn) {
     const int buf = s & 1;
+    const float glw = glw_cur;
     stage(rn, buf ^ 1);
+    glw_cur = rn.glw;
     issue(s + 3, rn);
     if (s > 0 && s % spc == 0) {
-      const float dec = exp2_hw(gw[(s / spc) * T + T - 1]);
+      const float dec = exp2_hw(glw);
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[j] *= dec;
     }
@@ -195,15 +204,19 @@ __global__ __launch_bounds__(512) void run_state_bf16(
                         bf16_hi(a0[1]) * w0[3]};
       const f32x4 x1 = {bf16_lo(a1[0]) * w1[0], bf16_hi(a1[0]) * w1[1], bf16_lo(a1[1]) * w1[2],
                         bf16_hi(a1[1]) * w1[3]};
-      u32x4 wxh, wxl;
-      split8_2(x0, x1, wxh, wxl);
+      u32x4 bt[NB];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int bb = (32 * kk + rsel) * BS + 16 * j + csel;
         const u32x2 e0 = lds_read_tr16(bts[buf] + bb), e1 = lds_read_tr16(bts[buf] + bb + 16 * BS);
-        const u32x4 bt = {e0[0], e0[1], e1[0], e1[1]};
-        acc[j] = mfma_bf16(bt, wxh, acc[j]);
-        acc[j] = mfma_bf16(bt, wxl, acc[j]);
+        bt[j] = (u32x4){e0[0], e0[1], e1[0], e1[1]};
+      }
+      u32x4 wxh, wxl;
+      split8_2(x0, x1, wxh, wxl);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        acc[j] = mfma_bf16(bt[j], wxh, acc[j]);
+        acc[j] = mfma_bf16(bt[j], wxl, acc[j]);
       }
     }
     __syncthreads();   // tile s + 1 is staged; tile s's reads are done
@@ -213,6 +226,7 @@ __global__ __launch_bounds__(512) void run_state_bf16(
   issue(0, ra);
   issue(1, rb);
   stage(ra, 0);
+  glw_cur = ra.glw;
   issue(2, ra);
   __syncthreads();
   // steps alternate register sets: step s stages tile s + 1 from the set
