@@ -518,6 +518,23 @@ def side_fields(ssd, run, dev, stream, steps, y_dtype, with_gdn):
     return out
 
 
+def bf16_y_entry(ssd, w, dev, nlaunch: int) -> dict:
+    """ssd_forward of a bf16 workload writing y in bf16, the output type the
+    pages' bf16 problem uses (inputs and outputs bf16, states fp32): tokens/s
+    and the step's fraction of 8 TB/s on its algorithmic bytes with 2-byte y.
+    The configs entry itself keeps fp32 y."""
+    import torch
+    r = WorkloadRun(ssd, w, torch.bfloat16, dev)
+    for i in range(max(3, r.nsets)):
+        r.forward(i)
+    ms = graph_time_ms([lambda i=i: r.forward(i) for i in range(nlaunch)])
+    step_bytes = sum(r.by[n] for n in r.kernels)
+    del r
+    return {"tokens_per_s": round(w.tokens / (ms * 1e-3), 1), "step_us": round(ms * 1e3, 2),
+            "step_alg_bytes": step_bytes,
+            "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def copy_rate(dev) -> float:
     """A 1 GiB device-to-device copy (read + write), timed from a graph of 5
     copies: the runtime's own streaming rate on this GPU, for context."""
@@ -603,6 +620,9 @@ def main() -> int:
             configs[name] = r.summary(r.time_all(nlaunch))
             del r
             torch.cuda.empty_cache()
+            if WORKLOADS[name].dtype == "bf16" and ty != torch.bfloat16:
+                configs[name]["bf16_y"] = bf16_y_entry(ssd, WORKLOADS[name], dev, nlaunch)
+                torch.cuda.empty_cache()
 
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = w.tokens / (wall / args.steps)

@@ -3,7 +3,8 @@
 * ssd_forward on one (batch, head) whose sequence is the longest a chunk of
   256 allows for P = N = 64: (L + T) * H * P * 4 bytes must stay below 2^31,
   so L = 2^23 - 256 - 1 tokens (32767 chunks, the last one 255 tokens).  One
-  token more is rejected.  Inputs are drawn on the device from a seeded
+  token more is rejected.  The same on one head pair with N = 128 and
+  128-token chunks (L = 2^22 - 128 - 1), which takes the bf16 fused pass.  Inputs are drawn on the device from a seeded
   generator with the distributions of the workloads.  Checked against the
   fp64 oracle on the first 16 chunks (states and y depend on the prefix
   only), and at the end through the split property the oracle is pinned
@@ -41,15 +42,18 @@ def _np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def test_forward_at_the_longest_sequence(ssd):
-    T, P, N, H, G = 256, 64, 64, 1, 1
-    L = (1 << 23) - T - 1
+def _longest_forward(ssd, T, N, H, G, seed):
+    """ssd_forward on one batch row at the longest sequence the per-sequence
+    extent rule allows for (T, N, H, G); checked as the module docstring
+    describes."""
+    P = 64
+    L = (1 << 31) // (H * P * 4) - T - 1
     # the library sizes the workspace for L and refuses L + 1 (0 = invalid)
     ws = ssd.workspace_bytes(ssd.SsdDims(1, L, H, P, N, G, T))
     assert ws == 8 * L * H
     assert ssd.workspace_bytes(ssd.SsdDims(1, L + 1, H, P, N, G, T)) == 0
-    log(f"[limits] ssd_forward b=1 L={L} H={H} P={P} N={N} T={T}")
-    gen = _gen(31)
+    log(f"[limits] ssd_forward b=1 L={L} H={H} P={P} N={N} G={G} T={T}")
+    gen = _gen(seed)
     bf = torch.bfloat16
     x = torch.randn(1, L, H, P, device=DEV, generator=gen).to(bf)
     B = torch.randn(1, L, G, N, device=DEV, generator=gen).to(bf)
@@ -86,6 +90,17 @@ def test_forward_at_the_longest_sequence(ssd):
         e = float(np.max(np.abs(g_ - w_)) / np.sqrt(np.mean(w_ ** 2)))
         log(f"  {what}: max|d|/RMS={e:.3e}")
         assert e <= 2e-3, (what, e)
+
+
+def test_forward_at_the_longest_sequence(ssd):
+    # one head, N = 64: the stage kernels (the two-level state pass)
+    _longest_forward(ssd, T=256, N=64, H=1, G=1, seed=31)
+
+
+def test_forward_at_the_longest_sequence_bf16_fused_pass(ssd):
+    # one head pair, N = 128: the bf16 fused pass, its chain cut into 256
+    # runs of 128 chunks (4 194 175 tokens, 2 GiB of states)
+    _longest_forward(ssd, T=128, N=128, H=2, G=1, seed=33)
 
 
 def test_conv1d_at_the_longest_row(ssd):
