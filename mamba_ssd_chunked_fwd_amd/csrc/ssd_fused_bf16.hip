@@ -43,6 +43,7 @@ namespace {
 
 constexpr int kN = 128;   // state columns of the bf16 fused pass
 constexpr int kTB = 64;   // tokens per block
+constexpr int kNontemporal = 2;   // cache-policy operand of a buffer store: the nt bit
 
 // Consecutive logical items on one XCD (blocks are dealt round-robin).
 __device__ __forceinline__ int xcd_map(int bid, int total) {
@@ -711,6 +712,7 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
     //      such runs per instruction; rows past the end of the sequence fall
     //      outside the range.  (The tile is rewritten only after the next
     //      step's first barrier, which every wave reaches after these reads.)
+    //      The stores are nontemporal: y is written once and not read back.
     const rsrc_t yres =
         make_rsrc((char*)y + (((size_t)st.b * L + t0) * H + st.h0) * kHeadDim * kYB,
                   ((uint32_t)(L - t0) * H - st.h0) * kHeadDim * kYB);
@@ -721,9 +723,10 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
       const uint32_t yo = ((uint32_t)i * H * kHeadDim + 4 * c4) * kYB;
       if constexpr (YBF16) {
         __builtin_amdgcn_raw_buffer_store_b64(
-            (u32x2){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, yres, yo, 0, 0);
+            (u32x2){pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, yres, yo, 0, kNontemporal);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yres, yo, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yres, yo, 0,
+                                               kNontemporal);
       }
     }
   };
