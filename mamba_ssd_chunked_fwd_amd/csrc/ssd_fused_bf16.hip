@@ -73,8 +73,8 @@ __device__ __forceinline__ void split8_2(const f32x4& v0, const f32x4& v1, u32x4
 }
 
 // ------------------------------------------------------------------ 1
-// One workgroup (8 waves) per (b, sub-run k, head pair); wave 4 hh + w owns
-// rows 16w..16w+15 of head hh and all N columns, transposed in the
+// One workgroup (4 waves per head) per (b, sub-run k, block of HB heads);
+// wave 4 hh + w owns rows 16w..16w+15 of head hh and all N columns, transposed in the
 // accumulators as in the other state kernels (lane: column p, four
 // consecutive n).  The sub-run is consumed in 64-token tiles through two
 // LDS buffers: while the waves multiply tile s out of one, they stage tile
@@ -85,22 +85,24 @@ __device__ __forceinline__ void split8_2(const f32x4& v0, const f32x4& v1, u32x4
 // the fused kernel's update does.  At each chunk start the accumulated
 // state is decayed by the chunk's 2^{g_last} before the chunk's tokens add.
 // The sub-runs lie before the last run, so every chunk is whole.
-template <int N>
-__global__ __launch_bounds__(512) void run_state_bf16(
+template <int N, int HB>
+__global__ __launch_bounds__(256 * HB) void run_state_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
     int L, int H, int G, int T, int nc, int R1, int nsub) {
-  constexpr int NT = 512, ST = 64;
+  constexpr int NT = 256 * HB, ST = 64;
   constexpr int XS = kHeadDim + 16;   // x row stride (bf16)
   constexpr int BS = N + 16;          // B row stride (bf16)
   constexpr int NB = N / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][2][ST * XS];   // [buffer][head]
+  constexpr int PPT = 8 * HB;         // 16-byte pieces of x per token
+  constexpr int BU = ST * N / 8 / NT; // 16-byte units of B per thread
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][HB][ST * XS];   // [buffer][head]
   __shared__ __attribute__((aligned(16))) uint16_t bts[2][ST * BS];
-  __shared__ __attribute__((aligned(16))) float wts[2][2][ST];          // [buffer][head]
+  __shared__ __attribute__((aligned(16))) float wts[2][HB][ST];          // [buffer][head]
 
-  const int npr = H / 2;
+  const int npr = H / HB;
   const int item = xcd_map(blockIdx.x, gridDim.x);
-  const int h0 = (item % npr) * 2;
+  const int h0 = (item % npr) * HB;
   const int k = (item / npr) % nsub;
   const int b = item / (npr * nsub);
   const int grp = h0 / (H / G);
@@ -115,33 +117,37 @@ __global__ __launch_bounds__(512) void run_state_bf16(
   const uint32_t xrow = (uint32_t)H * kHeadDim * 2, brow = (uint32_t)G * N * 2;
   const uint32_t span = (uint32_t)(R1 * T);
   const rsrc_t xr = make_rsrc(x + ((size_t)(b * (size_t)L + tb) * H + h0) * kHeadDim,
-                              (span - 1) * xrow + 2 * kHeadDim * 2);
+                              (span - 1) * xrow + HB * kHeadDim * 2);
   const rsrc_t br = make_rsrc(Bm + ((size_t)(b * (size_t)L + tb) * G + grp) * N,
                               (span - 1) * brow + N * 2);
-  // unit e = tid + 512 u: token e >> 4, 16-byte piece e & 15 of the pair's
-  // 256-byte x row (head (e >> 3) & 1, columns 8 (e & 7)..) and of the B
-  // row; the thread's head picks its g and dt row by offset, so the
-  // descriptors stay uniform.  One thread in eight (e & 7 == 0) also forms
-  // w_t of its (head, token).
-  const int th = (tid >> 3) & 1;
+  // x unit e = tid + NT u: token e / PPT, 16-byte piece e % PPT of the
+  // block's HB adjacent 128-byte head rows (head piece / 8, columns
+  // 8 (piece % 8)..); B unit e: token e / 16, piece e % 16.  The thread's
+  // head picks its g and dt row by offset, so the descriptors stay uniform.
+  // One thread in eight (piece % 8 == 0) also forms w_t of its (head, token).
+  const int th = HB == 1 ? 0 : (tid % PPT) >> 3;
   const bool wthr = (tid & 7) == 0;
   const size_t grow = ((size_t)b * H + h0) * L + tb;
   const rsrc_t gr = make_rsrc(g + grow, ((uint32_t)L + span) * 4);
   const rsrc_t dr = make_rsrc(dt_t + grow, ((uint32_t)L + span) * 4);
 
-  uint32_t xo[2], bo[2], go[2];
+  uint32_t xo[2], bo[BU], go[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int e = tid + NT * u;
-    xo[u] = (uint32_t)(e >> 4) * xrow + 16 * (e & 15);
+    xo[u] = (uint32_t)(e / PPT) * xrow + 16 * (e % PPT);
+    go[u] = 4 * ((uint32_t)(e / PPT) + (uint32_t)th * L);
+  }
+#pragma unroll
+  for (int u = 0; u < BU; ++u) {
+    const int e = tid + NT * u;
     bo[u] = (uint32_t)(e >> 4) * brow + 16 * (e & 15);
-    go[u] = 4 * ((uint32_t)(e >> 4) + (uint32_t)th * L);
   }
   const uint32_t gl_lane = 4 * (uint32_t)th * L;
   const uint32_t gl_wave = 4 * (uint32_t)hh * L;
 
   struct Regs {
-    u32x4 xv[2], bv[2];
+    u32x4 xv[2], bv[BU];
     float gv[2], dv[2], gl;   // g, dt of the thread's units; g_last of their head's chunk
     float glw;                // g_last of this wave's head's chunk
   };
@@ -152,10 +158,11 @@ __global__ __launch_bounds__(512) void run_state_bf16(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       r.xv[u] = load_b128(xr, t0 * xrow + xo[u]);
-      r.bv[u] = load_b128(br, t0 * brow + bo[u]);
       r.gv[u] = load_f32(gr, 4 * t0 + go[u]);
       r.dv[u] = load_f32(dr, 4 * t0 + go[u]);
     }
+#pragma unroll
+    for (int u = 0; u < BU; ++u) r.bv[u] = load_b128(br, t0 * brow + bo[u]);
     const uint32_t tl = 4u * (uint32_t)((s / spc) * T + T - 1);   // the chunk's last token
     r.gl = load_f32(gr, gl_lane + tl);
     r.glw = load_f32(gr, gl_wave + tl);
@@ -163,10 +170,14 @@ __global__ __launch_bounds__(512) void run_state_bf16(
   auto stage = [&](const Regs& r, int buf) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int e = tid + NT * u, t = e >> 4;
+      const int e = tid + NT * u, t = e / PPT;
       *(u32x4*)(xs[buf][th] + t * XS + 8 * (e & 7)) = r.xv[u];
-      *(u32x4*)(bts[buf] + t * BS + 8 * (e & 15)) = r.bv[u];
       if (wthr) wts[buf][th][t] = r.dv[u] * exp2_hw(r.gl - r.gv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < BU; ++u) {
+      const int e = tid + NT * u;
+      *(u32x4*)(bts[buf] + (e >> 4) * BS + 8 * (e & 15)) = r.bv[u];
     }
   };
 
@@ -739,8 +750,8 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
 
 // Runs per chain and sub-runs for the shape: as many runs as keep one
 // workgroup (b, head pair, run) per CU, of equal length; sub-runs the
-// longest divisor of the run that still gives the first kernel a
-// workgroup for every second CU.
+// longest divisor of the run that still gives the run pass (one workgroup
+// per (b, head, sub-run)) a workgroup per CU.
 struct RunPlan {
   int nr, R, R1, nsub;
 };
@@ -804,8 +815,10 @@ int launch_fused_bf16(const void* x, const void* B, const void* C, const float* 
   const RunPlan pl = plan_runs(s, cus);
   if (pl.nr > 1) {
     const int nc = (int)s.nchunks();
-    const unsigned g1 = (unsigned)(s.batch * (s.nheads / 2) * pl.nsub);
-    hipLaunchKernelGGL((run_state_bf16<kN>), dim3(g1), dim3(512), 0, st, (const uint16_t*)x,
+    // one head per workgroup (4 waves, two workgroups per CU): measured a
+    // little faster than head pairs sharing B (large -3%, long -1%)
+    const unsigned g1 = (unsigned)(s.batch * s.nheads * pl.nsub);
+    hipLaunchKernelGGL((run_state_bf16<kN, 1>), dim3(g1), dim3(256), 0, st, (const uint16_t*)x,
                        (const uint16_t*)B, dt_t, g, states, (int)s.seqlen, (int)s.nheads,
                        (int)s.ngroups, (int)s.chunk, nc, pl.R1, pl.nsub);
     int err = (int)hipGetLastError();
