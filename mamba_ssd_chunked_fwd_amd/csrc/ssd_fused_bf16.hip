@@ -372,6 +372,7 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
   const int lr = lane & 15, lq = lane >> 4;
   const int hpg = H / G, npr = H / 2;
   const int RT = R * T;   // tokens per run
+  const int lgT = 31 - __builtin_clz((unsigned)T);   // T is 64, 128 or 256
   const uint32_t xrow = (uint32_t)H * kHeadDim * 2;   // bytes per token of x
   const uint32_t brow = (uint32_t)G * N * 2;          // bytes per token of B and C
   const int p = 16 * w + lr;   // this lane's state row (operand row)
@@ -554,15 +555,15 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
       const int nt = min(TB, L - st.t0);
       const int gl = __builtin_amdgcn_readlane(__float_as_int(r.gv), nt - 1);
       // a block inside a chunk follows a whole block of the same chunk
-      const float gb = st.t0 % T != 0 ? gprev : 0.0f;
+      const float gb = (st.t0 & (T - 1)) != 0 ? gprev : 0.0f;
       gprev = __int_as_float(gl);
       gs[hh][lane] = lane < nt ? r.gv - gb : 0.0f;
       ds[hh][lane] = r.dv;
       ws[hh][lane] = r.dv * exp2_hw(__int_as_float(gl) - r.gv);
     }
-    if (st.t0 % T == 0) {
+    if ((st.t0 & (T - 1)) == 0) {
       const rsrc_t sres =
-          make_rsrc(states + (hrow * nc + st.t0 / T) * (kHeadDim * N), kStateBytes);
+          make_rsrc(states + (hrow * nc + (st.t0 >> lgT)) * (kHeadDim * N), kStateBytes);
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb)
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[nb]), sres,
