@@ -110,7 +110,8 @@ __global__ __launch_bounds__(256 * HB) void run_state_bf16(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = wave >> 2, wr = wave & 3;
   const int lr = lane & 15, lq = lane >> 4;
-  const int spc = T / ST;          // tiles per chunk
+  const int spc = T / ST;          // tiles per chunk (1, 2 or 4)
+  const int lgspc = 31 - __builtin_clz((unsigned)spc);
   const int nst = R1 * spc;        // tiles of the sub-run
   const int tb = k * R1 * T;       // its first token
 
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256 * HB) void run_state_bf16(
     }
 #pragma unroll
     for (int u = 0; u < BU; ++u) r.bv[u] = load_b128(br, t0 * brow + bo[u]);
-    const uint32_t tl = 4u * (uint32_t)((s / spc) * T + T - 1);   // the chunk's last token
+    const uint32_t tl = 4u * (uint32_t)((s >> lgspc) * T + T - 1);   // the chunk's last token
     r.gl = load_f32(gr, gl_lane + tl);
     r.glw = load_f32(gr, gl_wave + tl);
   };
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256 * HB) void run_state_bf16(
     stage(rn, buf ^ 1);
     glw_cur = rn.glw;
     issue(s + 3, rn);
-    if (s > 0 && s % spc == 0) {
+    if (s > 0 && (s & (spc - 1)) == 0) {
       const float dec = exp2_hw(glw);
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[j] *= dec;
