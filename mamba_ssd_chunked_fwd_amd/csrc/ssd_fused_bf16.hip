@@ -334,9 +334,11 @@ __global__ __launch_bounds__(256) void run_passing_kernel(
 //   both heads (hi + lo) in LDS.
 // * Every step's operands are loaded two steps ahead into one of two
 //   register sets, staged after the step's L' barrier while the other waves
-//   multiply by L'.  Uniform address parts go into the buffer descriptors;
-//   their ranges end at the sequence, so rows past it read zero and their
-//   stores are dropped.
+//   multiply by L'.  Within a step each product's LDS fragments are read
+//   one group ahead of it (scheduling barriers keep the reads early), so a
+//   wave waits on LDS once per phase rather than once per product.
+// * Uniform address parts go into the buffer descriptors; their ranges end
+//   at the sequence, so rows past it read zero and their stores are dropped.
 // * Work items are (b, head pair, run), pairs fastest, taken with a stride of
 //   the grid size; a run's blocks are the steps.
 template <bool YBF16>
@@ -349,7 +351,10 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
   constexpr int NT = 512, TB = kTB, N = kN, NIB = TB / 16, KN = N / 32;
   constexpr int XS = kHeadDim + 16;   // x tile row stride (bf16)
   constexpr int BS = N + 16;          // B row stride (bf16), natural column order
-  constexpr int CS = N + 8;           // C and B row stride (bf16), columns in k-slot order
+  constexpr int CS = N + 16;          // C and B row stride (bf16), columns in k-slot order
+  // (16-byte reads of 16 rows x 4 column groups hit no bank twice when the
+  // row stride is an odd multiple of 32 bytes: 288 here; at 272 every such
+  // read took two passes)
   constexpr int LS = TB + 8;          // L' row stride (bf16), columns in k-slot order
   constexpr uint32_t kYB = YBF16 ? 2 : 4;
   constexpr uint32_t kStateBytes = kHeadDim * N * 4;
@@ -590,22 +595,52 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
 #pragma unroll
     for (int j = 0; j < NLOAD; ++j) issue_slot(j, nxt, r);
 
-    // ---- this wave's blocks of C B^T (A = B rows j, B = C rows i, k slots
-    //      in accumulator order) and from them L' of both heads -> LDS
+    // ---- operands read ahead of their products: the first C B^T block's
+    //      fragments and this head's x tile as X^T fragments (lane (p, lq)
+    //      holds tokens 32 s + 16 (e / 4) + 4 lq + e % 4 of column p)
+    auto cb_frags = [&](int sl, u32x4 (&bf)[KN], u32x4 (&cf)[KN]) {
+      const int ib = blk_i(sl), jb = blk_j(sl);
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      if (sl < ncb) {
-        const int ib = blk_i(sl), jb = blk_j(sl);
-        f32x4 acc = (f32x4){0, 0, 0, 0};
-#pragma unroll
-        for (int kk = 0; kk < KN; ++kk) {
-          const u32x4 bf = *(const u32x4*)(bq + (16 * jb + lr) * CS + 32 * kk + 8 * lq);
-          const u32x4 cf = *(const u32x4*)(cp + (16 * ib + lr) * CS + 32 * kk + 8 * lq);
-          acc = mfma_bf16(bf, cf, acc);
-        }
-        cbr[sl] = acc;
+      for (int kk = 0; kk < KN; ++kk) {
+        bf[kk] = *(const u32x4*)(bq + (16 * jb + lr) * CS + 32 * kk + 8 * lq);
+        cf[kk] = *(const u32x4*)(cp + (16 * ib + lr) * CS + 32 * kk + 8 * lq);
       }
+    };
+    u32x4 cbb[KN], cbc[KN];
+    cb_frags(0, cbb, cbc);
+    u32x4 xa[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int xo = (32 * s + 4 * lq + (lr >> 2)) * XS + 16 * w + 4 * (lr & 3);
+      const u32x2 a0 = lds_read_tr16(xs[hq] + xo);
+      const u32x2 a1 = lds_read_tr16(xs[hq] + xo + 16 * XS);
+      xa[s] = (u32x4){a0[0], a0[1], a1[0], a1[1]};
     }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      f32x4 acc = (f32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk) acc = mfma_bf16(cbb[kk], cbc[kk], acc);
+      cbr[0] = acc;
+    }
+    if (ncb > 1) {
+      cb_frags(1, cbb, cbc);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc = (f32x4){0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk) acc = mfma_bf16(cbb[kk], cbc[kk], acc);
+      cbr[1] = acc;
+    }
+    // C fragments of the first k-step of C S^T, in flight while L' is formed
+    auto c_frag = [&](int kk, int ib) {
+      return *(const u32x4*)(cp + (16 * ib + lr) * CS + 32 * kk + 8 * lq);
+    };
+    u32x4 cfa[NIB], cfb[NIB];
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) cfa[ib] = c_frag(0, ib);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- L' of both heads from this wave's blocks -> LDS
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       if (sl < ncb) {
@@ -634,30 +669,26 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
       }
     }
 
-    // ---- this head's x tile as X^T fragments: lane (p, lq) holds tokens
-    //      32 s + 16 (e / 4) + 4 lq + e % 4 of column p
-    u32x4 xa[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int xo = (32 * s + 4 * lq + (lr >> 2)) * XS + 16 * w + 4 * (lr & 3);
-      const u32x2 a0 = lds_read_tr16(xs[hq] + xo);
-      const u32x2 a1 = lds_read_tr16(xs[hq] + xo + 16 * XS);
-      xa[s] = (u32x4){a0[0], a0[1], a1[0], a1[1]};
-    }
-
-    // ---- Y^T = S C^T, A = S from the accumulators (hi + lo), B = C rows
+    // ---- Y^T = S C^T, A = S from the accumulators (hi + lo), B = C rows;
+    //      the next k-step's C fragments are read during this one's products
     f32x4 yacc[NIB];
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) yacc[ib] = (f32x4){0, 0, 0, 0};
 #pragma unroll
     for (int kk = 0; kk < KN; ++kk) {
+      u32x4(&cur)[NIB] = (kk & 1) ? cfb : cfa;
+      u32x4(&nxt)[NIB] = (kk & 1) ? cfa : cfb;
+      if (kk + 1 < KN) {
+#pragma unroll
+        for (int ib = 0; ib < NIB; ++ib) nxt[ib] = c_frag(kk + 1, ib);
+      }
       u32x4 sh, sl;
       split8_2(sacc[2 * kk], sacc[2 * kk + 1], sh, sl);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
-        const u32x4 cf = *(const u32x4*)(cp + (16 * ib + lr) * CS + 32 * kk + 8 * lq);
-        yacc[ib] = mfma_bf16(sh, cf, yacc[ib]);
-        yacc[ib] = mfma_bf16(sl, cf, yacc[ib]);
+        yacc[ib] = mfma_bf16(sh, cur[ib], yacc[ib]);
+        yacc[ib] = mfma_bf16(sl, cur[ib], yacc[ib]);
       }
     }
     const float* gsh = gs[hq];
@@ -665,28 +696,51 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) yacc[ib] *= exp2_hw(gsh[16 * ib + lr]);
 
-    // ---- state: S <- 2^{g_last} S + B^T X', X' = w o x on this lane's tokens
+    // ---- state: S <- 2^{g_last} S + B^T X', X' = w o x on this lane's tokens;
+    //      each 32-token half's B^T fragments are read ahead of its products
+    auto b_frag = [&](int s, int nb) {
+      const int bo = (32 * s + 4 * lq + (lr >> 2)) * BS + 4 * (lr & 3) + 16 * nb;
+      const u32x2 a0 = lds_read_tr16(bp + bo);
+      const u32x2 a1 = lds_read_tr16(bp + bo + 16 * BS);
+      return (u32x4){a0[0], a0[1], a1[0], a1[1]};
+    };
+    u32x4 bf0[N / 16], bf1[N / 16];
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) bf0[nb] = b_frag(0, nb);
     const float dec = exp2_hw(gsh[nt - 1]);
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb) sacc[nb] *= dec;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    auto wx_split = [&](int s, u32x4& xh, u32x4& xl) {
       const f32x4 w0 = *(const f32x4*)(&wsh[32 * s + 4 * lq]);
       const f32x4 w1 = *(const f32x4*)(&wsh[32 * s + 16 + 4 * lq]);
       const f32x4 x0 = {bf16_lo(xa[s][0]) * w0[0], bf16_hi(xa[s][0]) * w0[1],
                         bf16_lo(xa[s][1]) * w0[2], bf16_hi(xa[s][1]) * w0[3]};
       const f32x4 x1 = {bf16_lo(xa[s][2]) * w1[0], bf16_hi(xa[s][2]) * w1[1],
                         bf16_lo(xa[s][3]) * w1[2], bf16_hi(xa[s][3]) * w1[3]};
-      u32x4 xh, xl;
       split8_2(x0, x1, xh, xl);
-      const int bo = (32 * s + 4 * lq + (lr >> 2)) * BS + 4 * (lr & 3);
+    };
+    {
+      u32x4 xh, xl;
+      wx_split(0, xh, xl);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb) {
-        const u32x2 a0 = lds_read_tr16(bp + bo + 16 * nb);
-        const u32x2 a1 = lds_read_tr16(bp + bo + 16 * BS + 16 * nb);
-        const u32x4 bt = {a0[0], a0[1], a1[0], a1[1]};
-        sacc[nb] = mfma_bf16(bt, xh, sacc[nb]);
-        sacc[nb] = mfma_bf16(bt, xl, sacc[nb]);
+        sacc[nb] = mfma_bf16(bf0[nb], xh, sacc[nb]);
+        sacc[nb] = mfma_bf16(bf0[nb], xl, sacc[nb]);
+        if (nb == 1) {
+#pragma unroll
+          for (int q = 0; q < N / 16; ++q) bf1[q] = b_frag(1, q);
+        }
+      }
+    }
+    {
+      u32x4 xh, xl;
+      wx_split(1, xh, xl);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb) {
+        sacc[nb] = mfma_bf16(bf1[nb], xh, sacc[nb]);
+        sacc[nb] = mfma_bf16(bf1[nb], xl, sacc[nb]);
       }
     }
     if (t0 + TB >= L && final_state) {
@@ -698,22 +752,44 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
     }
     __syncthreads();  // every wave's L' blocks are in LDS; x, B, C, g, dt reads are done
 
+    // L' fragments of the first three row blocks, in flight during the staging
+    uint16_t(*lph)[TB * LS] = lp[hq];
+    auto l_frag = [&](int ib, int s, int q) {
+      return *(const u32x4*)(lph[q] + (16 * ib + lr) * LS + 32 * s + 8 * lq);
+    };
+    u32x4 lf[4][2][2];   // [ib][s][hi, lo]
+#pragma unroll
+    for (int ib = 0; ib < 3; ++ib) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (2 * s <= ib) {
+          lf[ib][s][0] = l_frag(ib, s, 0);
+          lf[ib][s][1] = l_frag(ib, s, 1);
+        }
+      }
+    }
+
     // the next step's operands, while the other waves multiply by L'
     if (has_next) commit(rn);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- Y^T += X^T L'^T over the 32-token k-steps on or below the
     //      diagonal, into the block's Y tile in LDS (token rows, both heads'
     //      columns side by side)
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
+      if (ib == 1) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          lf[3][s][0] = l_frag(3, s, 0);
+          lf[3][s][1] = l_frag(3, s, 1);
+        }
+      }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (2 * s <= ib) {
-          const int ol = (16 * ib + lr) * LS + 32 * s + 8 * lq;
-          const u32x4 lh = *(const u32x4*)(lp[hq][0] + ol);
-          const u32x4 ll = *(const u32x4*)(lp[hq][1] + ol);
-          yacc[ib] = mfma_bf16(xa[s], lh, yacc[ib]);
-          yacc[ib] = mfma_bf16(xa[s], ll, yacc[ib]);
+          yacc[ib] = mfma_bf16(xa[s], lf[ib][s][0], yacc[ib]);
+          yacc[ib] = mfma_bf16(xa[s], lf[ib][s][1], yacc[ib]);
         }
       }
       *(f32x4*)(ys + (16 * ib + lr) * YS + hq * kHeadDim + p - lr + 4 * lq) = yacc[ib];

@@ -459,6 +459,9 @@ __global__ __launch_bounds__(kThreads) void fused_state_out_f32(
 //   descriptors (scalar arithmetic); the lanes' offsets are loop-invariant.
 //   The ranges end at the sequence, so rows past its end read zero and their
 //   stores are dropped.
+// * Each product's LDS fragments are read one group ahead of it (scheduling
+//   barriers keep the reads early), so a wave waits on LDS once per group
+//   of products with the next group's reads already in flight.
 template <bool YBF16>
 __global__ __launch_bounds__(512) void fused_pair_f32(
     const float* __restrict__ x, const float* __restrict__ Bm, const float* __restrict__ Cm,
@@ -468,7 +471,9 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
   constexpr int NT = 512;
   constexpr int T = 64, N = 64, NIB = 4, KN = N / 32;
   constexpr int BS = 80;                 // B plane row stride (bf16)
-  constexpr int CS = N + 8;              // C plane row stride (bf16), columns in k-slot order
+  constexpr int CS = N + 16;             // C plane row stride (bf16), columns in k-slot order
+  // (160 bytes: 16-byte reads of 16 rows x 4 column groups then hit no bank
+  // twice, where 144 took two passes)
   constexpr int LS = T + 8;              // L' plane row stride (bf16), columns in k-slot order
   constexpr int BU = T * 16 / NT;        // 16-byte units of the B and C tiles per thread
   constexpr int XV = 16;                 // x values per lane
@@ -707,24 +712,27 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     for (int j = XV; j < NLOAD; ++j) issue_slot(j, nxt, r);
 
     // ---- this wave's blocks of C B^T (A = B rows j, B = C rows i, k slots
-    //      in accumulator order) and from them L' of both heads -> LDS
+    //      in accumulator order) and from them L' of both heads -> LDS; a
+    //      block's fragments are all read before its products
 #pragma unroll
     for (int sl = 0; sl < 2; ++sl) {
       if (sl < nblk) {
         const int ib = blk_i(sl), jb = blk_j(sl);
-        f32x4 acc = (f32x4){0, 0, 0, 0};
+        u32x4 bf[KN][3], cf[KN][3];
 #pragma unroll
         for (int kk = 0; kk < KN; ++kk) {
           const int ob = (16 * jb + lr) * CS + 32 * kk + 8 * lq;
           const int oc = (16 * ib + lr) * CS + 32 * kk + 8 * lq;
-          u32x4 bf[3], cf[3];
 #pragma unroll
           for (int q = 0; q < 3; ++q) {
-            bf[q] = *(const u32x4*)(bq[q] + ob);
-            cf[q] = *(const u32x4*)(cp[q] + oc);
+            bf[kk][q] = *(const u32x4*)(bq[q] + ob);
+            cf[kk][q] = *(const u32x4*)(cp[q] + oc);
           }
-          acc = mfma6(bf, cf, acc);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 acc = (f32x4){0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KN; ++kk) acc = mfma6(bf[kk], cf[kk], acc);
         cbr[sl] = acc;
       }
     }
@@ -751,20 +759,28 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
       }
     }
 
-    // ---- Y^T = S C^T, A = S from the accumulators (split), B = C rows
+    // ---- Y^T = S C^T, A = S from the accumulators (split), B = C rows; each
+    //      row block's C fragments are read during the previous one's products
     f32x4 yacc[NIB];
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) yacc[ib] = (f32x4){0, 0, 0, 0};
+    auto c_frags = [&](int kk, int ib, u32x4 (&cf)[3]) {
+      const int oc = (16 * ib + lr) * CS + 32 * kk + 8 * lq;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) cf[q] = *(const u32x4*)(cp[q] + oc);
+    };
+    u32x4 cfr[2][3];
+    c_frags(0, 0, cfr[0]);
 #pragma unroll
     for (int kk = 0; kk < KN; ++kk) {
       u32x4 sf[3];
       split8(sacc[2 * kk], sacc[2 * kk + 1], sf);
 #pragma unroll
       for (int ib = 0; ib < NIB; ++ib) {
-        const int oc = (16 * ib + lr) * CS + 32 * kk + 8 * lq;
-        const u32x4 cf[3] = {*(const u32x4*)(cp[0] + oc), *(const u32x4*)(cp[1] + oc),
-                             *(const u32x4*)(cp[2] + oc)};
-        yacc[ib] = mfma6(sf, cf, yacc[ib]);
+        const int g = kk * NIB + ib;
+        if (g + 1 < KN * NIB) c_frags((g + 1) / NIB, (g + 1) % NIB, cfr[(g + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        yacc[ib] = mfma6(sf, cfr[g & 1], yacc[ib]);
       }
     }
     const float* gsh = gs[hq];
@@ -773,6 +789,17 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
     for (int ib = 0; ib < NIB; ++ib) yacc[ib] *= exp2_hw(gsh[16 * ib + lr]);
 
     // ---- state: S <- 2^{g_last} S + B^T X', X' = w o x on this lane's tokens
+    auto b_frags = [&](int s, int nb, u32x4 (&bt)[3]) {
+      const int bo = (32 * s + 4 * lq + (lr >> 2)) * BS + 4 * (lr & 3) + 16 * nb;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const u32x2 a0 = lds_read_tr16(bp[q] + bo);
+        const u32x2 a1 = lds_read_tr16(bp[q] + bo + 16 * BS);
+        bt[q] = (u32x4){a0[0], a0[1], a1[0], a1[1]};
+      }
+    };
+    u32x4 btr[2][3];
+    b_frags(0, 0, btr[0]);
     const float glast = gsh[nt - 1];
     const float dec = exp2_hw(glast);
 #pragma unroll
@@ -789,17 +816,12 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
       }
       u32x4 xp[3];
       split8(x0, x1, xp);
-      const int bo = (32 * s + 4 * lq + (lr >> 2)) * BS + 4 * (lr & 3);
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb) {
-        u32x4 bt[3];
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          const u32x2 a0 = lds_read_tr16(bp[q] + bo + 16 * nb);
-          const u32x2 a1 = lds_read_tr16(bp[q] + bo + 16 * BS + 16 * nb);
-          bt[q] = (u32x4){a0[0], a0[1], a1[0], a1[1]};
-        }
-        sacc[nb] = mfma6(bt, xp, sacc[nb]);
+        const int g = s * (N / 16) + nb;
+        if (g + 1 < 2 * (N / 16)) b_frags((g + 1) / (N / 16), (g + 1) % (N / 16), btr[(g + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        sacc[nb] = mfma6(btr[g & 1], xp, sacc[nb]);
       }
     }
     // x of the step two ahead, now that this step's x is consumed
@@ -823,15 +845,24 @@ __global__ __launch_bounds__(512) void fused_pair_f32(
         make_rsrc((char*)y + (((size_t)st.b * L + t0) * H + h) * kHeadDim * kYB,
                   ((uint32_t)(L - t0) * H - h) * kHeadDim * kYB);
     uint16_t(*lph)[T * LS] = lp[hq];
+    // the six (row block, k-step) pairs on or below the diagonal, in order
+    constexpr int kIb[6] = {0, 1, 2, 2, 3, 3}, kS[6] = {0, 0, 0, 1, 0, 1};
+    auto l_frags = [&](int g, u32x4 (&lf)[3]) {
+      const int ol = (16 * kIb[g] + lr) * LS + 32 * kS[g] + 8 * lq;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) lf[q] = *(const u32x4*)(lph[q] + ol);
+    };
+    u32x4 lfr[2][3];
+    l_frags(0, lfr[0]);
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         if (2 * s <= ib) {
-          const int ol = (16 * ib + lr) * LS + 32 * s + 8 * lq;
-          const u32x4 lf[3] = {*(const u32x4*)(lph[0] + ol), *(const u32x4*)(lph[1] + ol),
-                               *(const u32x4*)(lph[2] + ol)};
-          yacc[ib] = mfma6(xa[s], lf, yacc[ib]);
+          const int g = ib == 0 ? 0 : (ib == 1 ? 1 : 2 * ib - 2 + s);
+          if (g + 1 < 6) l_frags(g + 1, lfr[(g + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          yacc[ib] = mfma6(xa[s], lfr[g & 1], yacc[ib]);
         }
       }
       const uint32_t yo = ((uint32_t)(16 * ib + lr) * H * kHeadDim + p - lr + 4 * lq) * kYB;
