@@ -828,8 +828,8 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
 
 // Runs per chain and sub-runs for the shape: as many runs as keep one
 // workgroup (b, head pair, run) per CU, of equal length; sub-runs the
-// longest divisor of the run that still gives the run pass (one workgroup
-// per (b, head, sub-run)) a workgroup per CU.
+// longest divisor of the run that still gives the run pass at least one
+// (b, head, sub-run) per CU (its workgroups take the heads in pairs).
 struct RunPlan {
   int nr, R, R1, nsub;
 };
@@ -893,10 +893,11 @@ int launch_fused_bf16(const void* x, const void* B, const void* C, const float* 
   const RunPlan pl = plan_runs(s, cus);
   if (pl.nr > 1) {
     const int nc = (int)s.nchunks();
-    // one head per workgroup (4 waves, two workgroups per CU): measured a
-    // little faster than head pairs sharing B (large -3%, long -1%)
-    const unsigned g1 = (unsigned)(s.batch * s.nheads * pl.nsub);
-    hipLaunchKernelGGL((run_state_bf16<kN, 1>), dim3(g1), dim3(256), 0, st, (const uint16_t*)x,
+    // head pairs sharing each staged B tile (8 waves, one workgroup per CU):
+    // with the read-ahead fused kernel, 2-4% faster than one head per
+    // workgroup at two workgroups per CU (interleaved same-box timings)
+    const unsigned g1 = (unsigned)(s.batch * (s.nheads / 2) * pl.nsub);
+    hipLaunchKernelGGL((run_state_bf16<kN, 2>), dim3(g1), dim3(512), 0, st, (const uint16_t*)x,
                        (const uint16_t*)B, dt_t, g, states, (int)s.seqlen, (int)s.nheads,
                        (int)s.ngroups, (int)s.chunk, nc, pl.R1, pl.nsub);
     int err = (int)hipGetLastError();
