@@ -81,21 +81,20 @@ def fused(w, cus: int = 256) -> bool:
 
 def run_plan(w, cus: int = 256) -> dict:
     """The bf16 fused pass's cut of each chain into runs (the library's own
-    rule): nr runs of R chunks, the run pass over sub-runs of R1 chunks."""
+    rule): R = the chunk steps per CU if the walk were spread evenly, a lead
+    run of R0 = nc - (nr - 1) R chunks and nr - 1 runs of R; the run pass
+    walks every run but the last."""
     nc = w.nchunks
     pairs = w.batch * w.nheads // 2
-    nr = 1 if pairs >= cus else min(nc, max(1, cus // pairs))
-    R = -(-nc // nr)
-    nr = -(-nc // R)
-    R1 = R
-    if nr > 1:
-        R1 = 1
-        for d in range(R, 0, -1):
-            if R % d == 0 and 2 * pairs * (nr - 1) * (R // d) >= cus:
-                R1 = d
-                break
-    return {"runs": nr, "run_chunks": R, "subrun_chunks": R1,
-            "subruns": (nr - 1) * (R // R1) if nr > 1 else 0}
+    per = -(-pairs * nc // cus)
+    if per >= nc:
+        nr, R, R0 = 1, nc, nc
+    else:
+        R = per
+        nr = 1 + (nc - 1) // R
+        R0 = nc - (nr - 1) * R
+    return {"runs": nr, "run_chunks": R, "lead_chunks": R0,
+            "run_pass_chunks": nc - R if nr > 1 else 0}
 
 
 def step_kernels(w, cus: int = 256) -> list:
@@ -186,13 +185,13 @@ def issued_mfma_flop(w) -> dict:
         # the bf16 fused pass, per 64-token block of each (batch, head): C S^T
         # and the update with hi + lo of S and of w o x, X^T L'^T with hi + lo
         # of L' (six 32-token k-steps), C B^T once per head pair (ten 16x16
-        # blocks); plus the run pass over its sub-runs (update only)
+        # blocks); plus the run pass over the runs before the last (update only)
         nblk = -(-L // 64)
         lx64 = sum(ib // 2 + 1 for ib in range(4)) * 32 * 16 * P * 2
         cb64 = 10 * 16 * 16 * N * 2
         per_block = 2 * (2 * 64 * P * N) * 2 + 2 * lx64
         pl = run_plan(w)
-        run_pass = b * H * pl["subruns"] * pl["subrun_chunks"] * (T // 64) * 2 * (2 * 64 * P * N)
+        run_pass = b * H * pl["run_pass_chunks"] * (T // 64) * 2 * (2 * 64 * P * N)
         fused_issued = b * H * nblk * per_block + b * (H // 2) * nblk * cb64 + run_pass
     return {"fwd_pass_state": a2, "compute_out": out, "state_and_out": fused_issued}
 

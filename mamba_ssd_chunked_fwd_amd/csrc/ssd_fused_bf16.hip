@@ -12,17 +12,21 @@
 // order with the state in registers writes every S_c once and never reads
 // one back, and reads x once.  The bf16 layers have too few (b, h) pairs for
 // one walk per pair to fill the chip (96, 160 and 32 of them), so the chunks
-// of a chain are cut into nr runs of R chunks, walked at once:
+// of a chain are cut into runs, walked at once: a lead run of R0 chunks and
+// nr - 1 runs of R chunks (1 <= R0 <= R), R being the chunk steps per CU if
+// the whole walk were spread evenly over the CUs.  The (b, head pair) lead
+// runs that do not get a CU of their own share the spare ones, a few per
+// workgroup, so no workgroup walks much more than R chunks:
 //
-// 1. run_state_bf16: for every sub-run k of R1 chunks (R1 divides R) that
-//    lies before the last run, E_k = the state after the sub-run from a zero
-//    start, parked in the states slot of the chunk that follows it.
-// 2. run_passing: S at the sub-run starts, S_{(k+1) R1} = 2^{d_k} S_{k R1} +
-//    E_k with d_k the sum of the sub-run's g_last, in place; only the run
-//    starts are written back (the slots in between are rewritten by 3).
-//    The same jump as stage 2's, over R1 chunks instead of one.
-// 3. fused_pair_bf16: one workgroup per (b, head pair, run), starting from
-//    the run's first state and walking its chunks in 64-token blocks.
+// 1. run_state_bf16: for every run r but the last, E_r = the state after the
+//    run from a zero start, parked in the states slot of the next run's
+//    first chunk.
+// 2. run_passing: S at the run starts, S_{c(r+1)} = 2^{d_r} S_{c(r)} + E_r
+//    with c(r) the run's first chunk and d_r the sum of its g_last, in
+//    place.  The same jump as stage 2's, over a run instead of one chunk.
+// 3. fused_pair_bf16: one workgroup per (b, head pair, run) -- or per few
+//    lead runs -- starting from each run's first state and walking its
+//    chunks in 64-token blocks.
 // With one run per chain (enough pairs for the chip) 1 and 2 do not run.
 //
 // A chunk of 128 or 256 tokens is evaluated as 2 or 4 blocks of 64 tokens
@@ -84,12 +88,12 @@ __device__ __forceinline__ void split8_2(const f32x4& v0, const f32x4& v1, u32x4
 // the transpose read, scales them by w and splits them (hi + lo) itself, as
 // the fused kernel's update does.  At each chunk start the accumulated
 // state is decayed by the chunk's 2^{g_last} before the chunk's tokens add.
-// The sub-runs lie before the last run, so every chunk is whole.
+// The runs it walks lie before the last run, so every chunk is whole.
 template <int N, int HB>
 __global__ __launch_bounds__(256 * HB) void run_state_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const float* __restrict__ dt_t, const float* __restrict__ g, float* __restrict__ states,
-    int L, int H, int G, int T, int nc, int R1, int nsub) {
+    int L, int H, int G, int T, int nc, int R, int R0, int nsub) {
   constexpr int NT = 256 * HB, ST = 64;
   constexpr int XS = kHeadDim + 16;   // x row stride (bf16)
   constexpr int BS = N + 16;          // B row stride (bf16)
@@ -103,8 +107,10 @@ __global__ __launch_bounds__(256 * HB) void run_state_bf16(
   const int npr = H / HB;
   const int item = xcd_map(blockIdx.x, gridDim.x);
   const int h0 = (item % npr) * HB;
-  const int k = (item / npr) % nsub;
+  const int k = (item / npr) % nsub;   // the run
   const int b = item / (npr * nsub);
+  const int c0 = k == 0 ? 0 : R0 + (k - 1) * R;   // its first chunk
+  const int rl = k == 0 ? R0 : R;                  // its chunks
   const int grp = h0 / (H / G);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,11 +118,11 @@ __global__ __launch_bounds__(256 * HB) void run_state_bf16(
   const int lr = lane & 15, lq = lane >> 4;
   const int spc = T / ST;          // tiles per chunk (1, 2 or 4)
   const int lgspc = 31 - __builtin_clz((unsigned)spc);
-  const int nst = R1 * spc;        // tiles of the sub-run
-  const int tb = k * R1 * T;       // its first token
+  const int nst = rl * spc;        // tiles of the run
+  const int tb = c0 * T;           // its first token
 
   const uint32_t xrow = (uint32_t)H * kHeadDim * 2, brow = (uint32_t)G * N * 2;
-  const uint32_t span = (uint32_t)(R1 * T);
+  const uint32_t span = (uint32_t)(rl * T);
   const rsrc_t xr = make_rsrc(x + ((size_t)(b * (size_t)L + tb) * H + h0) * kHeadDim,
                               (span - 1) * xrow + HB * kHeadDim * 2);
   const rsrc_t br = make_rsrc(Bm + ((size_t)(b * (size_t)L + tb) * G + grp) * N,
@@ -251,8 +257,8 @@ __global__ __launch_bounds__(256 * HB) void run_state_bf16(
   }
   if (nst & 1) step(nst - 1, rb);
 
-  // E_k into the slot of the chunk after the sub-run
-  float* dst = states + (((size_t)b * H + h0 + hh) * nc + (size_t)(k + 1) * R1) * kHeadDim * N;
+  // E_k into the slot of the chunk after the run
+  float* dst = states + (((size_t)b * H + h0 + hh) * nc + (size_t)(c0 + rl)) * kHeadDim * N;
   const int p = 16 * wr + lr;
 #pragma unroll
   for (int j = 0; j < NB; ++j) *(f32x4*)(dst + (size_t)p * N + 16 * j + 4 * lq) = acc[j];
@@ -260,18 +266,20 @@ __global__ __launch_bounds__(256 * HB) void run_state_bf16(
 
 // ------------------------------------------------------------------ 2
 // A thread owns one 16-byte unit (four consecutive n of one row p) of one
-// (b, h) and walks the sub-runs: S_0 = init (or zero) is written to slot 0,
-// then S_{k R1} = 2^{d_{k-1}} S_{(k-1) R1} + E_{k-1}, stored where k R1
-// starts a run.  The sub-runs' decay sums d_k (sums of their chunks'
-// g_last) are formed first, one sub-run per thread, into LDS.
+// (b, h) and walks the runs: S_0 = init (or zero) is written to slot 0,
+// then S_{c(r+1)} = 2^{d_r} S_{c(r)} + E_r into the slot of run r + 1's
+// first chunk, where E_r is parked.  The runs' decay sums d_r (sums of their
+// chunks' g_last) are formed first, one run per thread, into LDS.  Run r
+// starts at chunk c(r) = 0 for r = 0, else R0 + (r - 1) R, and has R0
+// chunks for r = 0, else R; nsub runs precede the last one.
 template <int N>
 __global__ __launch_bounds__(256) void run_passing_kernel(
     const float* __restrict__ g, const float* __restrict__ init, float* __restrict__ states,
-    int L, int T, int nc, int R1, int nsub, int spr) {
+    int L, int T, int nc, int R, int R0, int nsub) {
   constexpr int UNITS = kHeadDim * N / 4;
   constexpr int WPB = UNITS / 256;
   constexpr int D = 4;
-  constexpr int MAXS = 1024;   // sub-runs per pass over the decay sums
+  constexpr int MAXS = 1024;   // runs per pass over the decay sums
   __shared__ float dsum[MAXS];
   const int bh = blockIdx.x / WPB;
   const int u = (blockIdx.x % WPB) * 256 + threadIdx.x;
@@ -280,21 +288,24 @@ __global__ __launch_bounds__(256) void run_passing_kernel(
   const float* gh = g + (size_t)bh * L;
   f32x4 s = init ? *(const f32x4*)(init + bh * ss + 4 * (size_t)u) : (f32x4){0, 0, 0, 0};
   *(f32x4*)st = s;
+  // slot of run k + 1's first chunk, where E_k is parked and S goes
+  auto slot = [&](int k) { return (size_t)(R0 + k * R) * ss; };
 #pragma unroll 1
   for (int k0 = 0; k0 < nsub; k0 += MAXS) {
     const int kn = min(MAXS, nsub - k0);
     __syncthreads();
     for (int k = threadIdx.x; k < kn; k += 256) {
-      const float* q = gh + (size_t)(k0 + k) * R1 * T + T - 1;
+      const int r = k0 + k, c0 = r == 0 ? 0 : R0 + (r - 1) * R, rl = r == 0 ? R0 : R;
+      const float* q = gh + (size_t)c0 * T + T - 1;
       float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
       int c = 0;
-      for (; c + 4 <= R1; c += 4) {
+      for (; c + 4 <= rl; c += 4) {
         s0 += q[(size_t)c * T];
         s1 += q[(size_t)(c + 1) * T];
         s2 += q[(size_t)(c + 2) * T];
         s3 += q[(size_t)(c + 3) * T];
       }
-      for (; c < R1; ++c) s0 += q[(size_t)c * T];
+      for (; c < rl; ++c) s0 += q[(size_t)c * T];
       dsum[k] = (s0 + s1) + (s2 + s3);
     }
     __syncthreads();
@@ -302,16 +313,13 @@ __global__ __launch_bounds__(256) void run_passing_kernel(
     for (int j0 = 0; j0 < kn; j0 += D) {
       f32x4 e[D];
 #pragma unroll
-      for (int j = 0; j < D; ++j) {
-        const int k = k0 + j0 + j + 1;
-        e[j] = j0 + j < kn ? *(const f32x4*)(st + (size_t)k * R1 * ss) : (f32x4){0, 0, 0, 0};
-      }
+      for (int j = 0; j < D; ++j)
+        e[j] = j0 + j < kn ? *(const f32x4*)(st + slot(k0 + j0 + j)) : (f32x4){0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < D; ++j) {
-        const int k = k0 + j0 + j + 1;
         if (j0 + j < kn) {
           s = exp2_hw(dsum[j0 + j]) * s + e[j];
-          if (k % spr == 0) *(f32x4*)(st + (size_t)k * R1 * ss) = s;
+          *(f32x4*)(st + slot(k0 + j0 + j)) = s;
         }
       }
     }
@@ -339,15 +347,18 @@ __global__ __launch_bounds__(256) void run_passing_kernel(
 //   wave waits on LDS once per phase rather than once per product.
 // * Uniform address parts go into the buffer descriptors; their ranges end
 //   at the sequence, so rows past it read zero and their stores are dropped.
-// * Work items are (b, head pair, run), pairs fastest, taken with a stride of
-//   the grid size; a run's blocks are the steps.
+// * Work items are (b, head pair, run) with the runs r >= 1 first (pairs
+//   fastest) and then the lead runs.  Workgroup w < (number of runs r >= 1)
+//   takes that one item; each of the others takes ks consecutive lead runs
+//   (ks = 0: every workgroup takes items with a stride of the grid size).
+//   A run's blocks are the steps.
 template <bool YBF16>
 __global__ __launch_bounds__(512) void fused_pair_bf16(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ Bm,
     const uint16_t* __restrict__ Cm, const float* __restrict__ dt_t, const float* __restrict__ g,
     const float* __restrict__ Dv, const float* __restrict__ init, float* __restrict__ states,
     float* __restrict__ final_state, void* __restrict__ y, int L, int H, int G, int T, int nc,
-    int R, int nr, int items) {
+    int R, int R0, int nr, int chains, int ks) {
   constexpr int NT = 512, TB = kTB, N = kN, NIB = TB / 16, KN = N / 32;
   constexpr int XS = kHeadDim + 16;   // x tile row stride (bf16)
   constexpr int BS = N + 16;          // B row stride (bf16), natural column order
@@ -370,25 +381,40 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
 
   const int nwg = gridDim.x;
   const int wg = xcd_map(blockIdx.x, nwg);
-  if (wg >= items) return;
+  // this workgroup's items: it0 + istride j, j < icount
+  const int n_long = chains * (nr - 1), total = n_long + chains;
+  int it0 = wg, istride = nwg, icount = wg < total ? (total - 1 - wg) / nwg + 1 : 0;
+  if (ks > 0) {
+    istride = 1;
+    if (wg < n_long) {
+      icount = 1;
+    } else {
+      it0 = n_long + (wg - n_long) * ks;
+      icount = max(0, min(ks, total - it0));
+    }
+  }
+  if (icount <= 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = wave >> 2, w = wave & 3;
   const int lr = lane & 15, lq = lane >> 4;
   const int hpg = H / G, npr = H / 2;
-  const int RT = R * T;   // tokens per run
   const int lgT = 31 - __builtin_clz((unsigned)T);   // T is 64, 128 or 256
   const uint32_t xrow = (uint32_t)H * kHeadDim * 2;   // bytes per token of x
   const uint32_t brow = (uint32_t)G * N * 2;          // bytes per token of B and C
   const int p = 16 * w + lr;   // this lane's state row (operand row)
 
+  // run r: first chunk, blocks
+  auto run_c0 = [&](int r) { return r == 0 ? 0 : R0 + (r - 1) * R; };
   auto run_blocks = [&](int r) {
-    const int tb = r * RT, te = min(tb + RT, L);
+    const int tb = run_c0(r) * T, te = min(tb + (r == 0 ? R0 : R) * T, L);
     return (te - tb + TB - 1) / TB;
   };
+  const int nrm = max(nr - 1, 1);
+  auto item_run = [&](int it) { return it < n_long ? 1 + (it / npr) % nrm : 0; };
   int nsteps = 0;
-  for (int it = wg; it < items; it += nwg) nsteps += run_blocks((it / npr) % nr);
+  for (int j = 0; j < icount; ++j) nsteps += run_blocks(item_run(it0 + istride * j));
 
   // loop-invariant lane offsets (bytes) from each step's descriptor bases:
   // unit e = tid + 512 u is token e >> 4, 16-byte piece e & 15 of the row
@@ -416,19 +442,21 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
     bool live, first;
   };
   struct Cursor {
-    int k, blk, nb, it;
+    int k, blk, nb, j;   // step, block of the item, its blocks, item of the workgroup
     StepP st;
   };
   auto at_item = [&](Cursor& cu) {
-    const int pr = cu.it % npr;
-    cu.st.r = (cu.it / npr) % nr;
-    cu.st.b = cu.it / (npr * nr);
+    const int it = it0 + istride * cu.j;
+    const int q = it < n_long ? it : it - n_long;
+    const int pr = q % npr;
+    cu.st.r = item_run(it);
+    cu.st.b = it < n_long ? q / (npr * nrm) : q / npr;
     cu.st.h0 = 2 * pr;
     cu.st.grp = cu.st.h0 / hpg;
     cu.nb = run_blocks(cu.st.r);
   };
   auto set_step = [&](Cursor& cu) {
-    cu.st.t0 = cu.st.r * RT + TB * cu.blk;
+    cu.st.t0 = run_c0(cu.st.r) * T + TB * cu.blk;
     cu.st.first = cu.blk == 0;
     cu.st.live = cu.k < nsteps;
   };
@@ -436,7 +464,7 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
     ++cu.k;
     if (++cu.blk == cu.nb) {
       cu.blk = 0;
-      cu.it += nwg;
+      ++cu.j;
       if (cu.k < nsteps) at_item(cu);
     }
     set_step(cu);
@@ -504,7 +532,7 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
   Cursor cur;
   cur.k = 0;
   cur.blk = 0;
-  cur.it = wg;
+  cur.j = 0;
   at_item(cur);
   set_step(cur);
   {
@@ -535,7 +563,8 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
       // single run, else the slot the run passing wrote
       rsrc_t ires;
       if (nr > 1)
-        ires = make_rsrc(states + (hrow * nc + (size_t)st.r * R) * (kHeadDim * N), kStateBytes);
+        ires = make_rsrc(states + (hrow * nc + (size_t)run_c0(st.r)) * (kHeadDim * N),
+                         kStateBytes);
       else
         ires = init ? make_rsrc(init + hrow * (kHeadDim * N), kStateBytes)
                     : make_rsrc(states, 0u);
@@ -826,34 +855,22 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
   }
 }
 
-// Runs per chain and sub-runs for the shape: as many runs as keep one
-// workgroup (b, head pair, run) per CU, of equal length; sub-runs the
-// longest divisor of the run that still gives the run pass at least one
-// (b, head, sub-run) per CU (its workgroups take the heads in pairs).
+// Runs per chain for the shape: R = the chunk steps per CU if every chain's
+// walk were spread evenly over the CUs; a lead run of R0 = nc - (nr - 1) R
+// chunks (1 <= R0 <= R) and nr - 1 runs of R.  nr = 1 when there are enough
+// (b, head pair) chains for the CUs.
 struct RunPlan {
-  int nr, R, R1, nsub;
+  int nr, R, R0;
 };
 
 RunPlan plan_runs(const Shape& s, int cus) {
   const int nc = (int)s.nchunks();
   const int64_t pairs = s.batch * s.nheads / 2;
-  int nr = pairs >= cus ? 1 : (int)(cus / pairs);
-  if (nr > nc) nr = nc;
-  if (nr < 1) nr = 1;
-  const int R = (nc + nr - 1) / nr;
-  nr = (nc + R - 1) / R;
-  RunPlan pl{nr, R, R, 0};
-  if (nr > 1) {
-    pl.R1 = 1;
-    for (int d = R; d >= 1; --d) {
-      if (R % d == 0 && 2 * pairs * ((int64_t)(nr - 1) * (R / d)) >= cus) {
-        pl.R1 = d;
-        break;
-      }
-    }
-    pl.nsub = (nr - 1) * (R / pl.R1);
-  }
-  return pl;
+  const int64_t per = (pairs * nc + cus - 1) / cus;
+  if (per >= nc) return RunPlan{1, nc, nc};
+  const int R = (int)per;
+  const int nr = 1 + (nc - 1) / R;
+  return RunPlan{nr, R, nc - (nr - 1) * R};
 }
 
 template <bool YBF16>
@@ -865,12 +882,16 @@ int launch_pair_bf16(const void* x, const void* B, const void* C, const float* d
     return resident_slots((const void*)fused_pair_bf16<YBF16>, 512, dev);
   });
   if (slots <= 0) return (int)hipErrorInvalidDevice;
-  const int items = (int)(s.batch * (s.nheads / 2) * pl.nr);
-  const unsigned grid = (unsigned)(items < slots ? items : slots);
-  hipLaunchKernelGGL((fused_pair_bf16<YBF16>), dim3(grid), dim3(512), 0, st,
+  const int chains = (int)(s.batch * (s.nheads / 2));
+  const int items = chains * pl.nr;
+  const int grid = items < slots ? items : slots;
+  // lead runs per spare workgroup (0: a stride of the grid over all items)
+  const int n_long = chains * (pl.nr - 1), spare = grid - n_long;
+  const int ks = pl.nr > 1 && spare > 0 ? (chains + spare - 1) / spare : 0;
+  hipLaunchKernelGGL((fused_pair_bf16<YBF16>), dim3((unsigned)grid), dim3(512), 0, st,
                      (const uint16_t*)x, (const uint16_t*)B, (const uint16_t*)C, dt_t, g, D,
                      init, states, fin, y, (int)s.seqlen, (int)s.nheads, (int)s.ngroups,
-                     (int)s.chunk, (int)s.nchunks(), pl.R, pl.nr, items);
+                     (int)s.chunk, (int)s.nchunks(), pl.R, pl.R0, pl.nr, chains, ks);
   return (int)hipGetLastError();
 }
 
@@ -896,15 +917,16 @@ int launch_fused_bf16(const void* x, const void* B, const void* C, const float* 
     // head pairs sharing each staged B tile (8 waves, one workgroup per CU):
     // with the read-ahead fused kernel, 2-4% faster than one head per
     // workgroup at two workgroups per CU (interleaved same-box timings)
-    const unsigned g1 = (unsigned)(s.batch * (s.nheads / 2) * pl.nsub);
+    const int nsub = pl.nr - 1;   // the runs before the last
+    const unsigned g1 = (unsigned)(s.batch * (s.nheads / 2) * nsub);
     hipLaunchKernelGGL((run_state_bf16<kN, 2>), dim3(g1), dim3(512), 0, st, (const uint16_t*)x,
                        (const uint16_t*)B, dt_t, g, states, (int)s.seqlen, (int)s.nheads,
-                       (int)s.ngroups, (int)s.chunk, nc, pl.R1, pl.nsub);
+                       (int)s.ngroups, (int)s.chunk, nc, pl.R, pl.R0, nsub);
     int err = (int)hipGetLastError();
     if (err) return err;
     const unsigned g2 = (unsigned)(s.batch * s.nheads * (kHeadDim * kN / 4 / 256));
     hipLaunchKernelGGL((run_passing_kernel<kN>), dim3(g2), dim3(256), 0, st, g, init, states,
-                       (int)s.seqlen, (int)s.chunk, nc, pl.R1, pl.nsub, pl.R / pl.R1);
+                       (int)s.seqlen, (int)s.chunk, nc, pl.R, pl.R0, nsub);
     err = (int)hipGetLastError();
     if (err) return err;
   }

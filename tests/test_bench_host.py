@@ -100,27 +100,27 @@ def test_fused_pass_accounting_of_the_wide_layer():
 
 def test_bf16_fused_pass_plans_and_accounting():
     """The bf16 layers run stages 2 and 3 as the bf16 fused pass.  On 256
-    CUs their chains are cut into runs of equal length, one workgroup per
-    (batch, head pair, run): small 48 pairs x 5 runs of 7 chunks, large 80 x
-    3 runs of 11, long 16 x 16 runs of 32; the run pass takes whole runs
-    (every second CU busy or more).  Issued matrix work per 64-token block
-    of a head: C S^T and the update, 2 T P N each with hi + lo, X^T L'^T
-    over six 32-token k-steps with hi + lo; C B^T (ten 16x16 blocks) per
-    head pair; the run pass's update over the runs before the last."""
+    CUs each chain is cut into a lead run and runs of R chunks, R the chunk
+    steps per CU if the walk were spread evenly: small 48 pairs x 32 chunks
+    -> R 6, lead 2 + 5 runs of 6; large 80 x 32 -> R 10, lead 2 + 3 runs of
+    10; long 16 x 512 -> 16 runs of 32; the run pass walks every run but the
+    last.  Issued matrix work per 64-token block of a head: C S^T and the
+    update, 2 T P N each with hi + lo, X^T L'^T over six 32-token k-steps
+    with hi + lo; C B^T (ten 16x16 blocks) per head pair; the run pass's
+    update over the runs before the last."""
     import bench
     from ssd_workloads import WORKLOADS
-    plans = {"small_bf16": (5, 7, 7, 4), "large_bf16": (3, 11, 11, 2),
-             "long_bf16": (16, 32, 32, 15)}
-    for name, (nr, R, R1, nsub) in plans.items():
+    plans = {"small_bf16": (6, 6, 2), "large_bf16": (4, 10, 2), "long_bf16": (16, 32, 32)}
+    for name, (nr, R, R0) in plans.items():
         w = WORKLOADS[name]
         assert bench.step_kernels(w) == ["chunk_cumsum", "state_and_out"], name
-        assert bench.run_plan(w) == {"runs": nr, "run_chunks": R, "subrun_chunks": R1,
-                                     "subruns": nsub}, name
-        assert nr * R >= w.nchunks > (nr - 1) * R
+        assert bench.run_plan(w) == {"runs": nr, "run_chunks": R, "lead_chunks": R0,
+                                     "run_pass_chunks": w.nchunks - R}, name
+        assert R0 + (nr - 1) * R == w.nchunks and 1 <= R0 <= R
     w = WORKLOADS["small_bf16"]
     b, L, H, P, N = 4, 2048, 24, 64, 128
     nblk = L // 64
     per_block = 2 * 2 * (2 * 64 * P * N) + 2 * 6 * 32 * 16 * P * 2
-    run_pass = b * H * 4 * 7 * 2 * (2 * 64 * P * N)
+    run_pass = b * H * (32 - 6) * 2 * (2 * 64 * P * N)
     assert bench.issued_mfma_flop(w)["state_and_out"] == \
         b * H * nblk * per_block + b * (H // 2) * nblk * 10 * 16 * 16 * N * 2 + run_pass

@@ -470,8 +470,11 @@ def test_fused_forward_bf16_output(ssd):
 #  * 128-token chunks, groups of 4 heads, init.
 FUSED_BF16 = [
     _wl("persistent_pairs_T64", "bf16", 32, 200, 24, 1, 128, 64, False),
-    _wl("runs_of_3_T64_ragged_init", "bf16", 1, 2553, 32, 1, 128, 64, True),
-    _wl("subruns_of_1_T64_grouped", "bf16", 1, 380, 200, 2, 128, 64, True),
+    _wl("runs_of_3_lead_1_T64_ragged_init", "bf16", 1, 2553, 32, 1, 128, 64, True),
+    _wl("two_runs_T64_grouped", "bf16", 1, 380, 200, 2, 128, 64, True),
+    # lead runs shorter than the others, three (two) to a workgroup
+    _wl("lead_runs_3_per_wg_T64_ragged_init", "bf16", 2, 2000, 48, 1, 128, 64, True),
+    _wl("lead_runs_2_per_wg_T256_init", "bf16", 1, 4000, 88, 1, 128, 256, True),
     _wl("blocks_in_T256_ragged_init", "bf16", 1, 1380, 4, 1, 128, 256, True),
     _wl("T128_groups_of_4_init", "bf16", 3, 1000, 8, 2, 128, 128, True),
 ]
