@@ -77,10 +77,10 @@ __device__ __forceinline__ void split8_2(const f32x4& v0, const f32x4& v1, u32x4
 }
 
 // ------------------------------------------------------------------ 1
-// One workgroup (4 waves per head) per (b, sub-run k, block of HB heads);
+// One workgroup (4 waves per head) per (b, run k, block of HB heads);
 // wave 4 hh + w owns rows 16w..16w+15 of head hh and all N columns, transposed in the
 // accumulators as in the other state kernels (lane: column p, four
-// consecutive n).  The sub-run is consumed in 64-token tiles through two
+// consecutive n).  The run is consumed in 64-token tiles through two
 // LDS buffers: while the waves multiply tile s out of one, they stage tile
 // s + 1 (x of both heads as loaded, B, and the weights w_t = dt_t
 // 2^{g_last - g_t}) into the other from registers, and the loads of tile
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256 * HB) void run_state_bf16(
     float gv[2], dv[2], gl;   // g, dt of the thread's units; g_last of their head's chunk
     float glw;                // g_last of this wave's head's chunk
   };
-  // loads of tile s; past the sub-run they read zero (x, B) or words of the
+  // loads of tile s; past the run they read zero (x, B) or words of the
   // same rows (g, dt) that are never used
   auto issue = [&](int s, Regs& r) {
     const uint32_t t0 = (uint32_t)(s * ST);

@@ -460,12 +460,14 @@ def test_fused_forward_bf16_output(ssd):
 
 # ------------------------------------------------- bf16 fused pass (runs)
 # Shapes that give the bf16 fused pass each plan on a 256-CU device (pairs =
-# batch x heads / 2; runs nr = min(chunks, CUs / pairs), R chunks each;
-# sub-runs of R1 chunks for the run pass):
+# batch x heads / 2; R = ceil(pairs x chunks / CUs) chunk steps per CU, a
+# lead run of R0 = chunks - (nr - 1) R and nr - 1 runs of R):
 #  * one run per chain, more pairs than workgroups (a workgroup takes several
 #    (b, pair) items in turn): 32 x 24 heads = 384 pairs;
-#  * runs of several chunks, sub-runs as long as the runs (R = R1 = 3);
-#  * runs of 3 chunks in sub-runs of one (100 pairs: nr = 2, R1 = 1);
+#  * 16 pairs, 40 chunks: runs of 3 after a lead run of 1, ragged, init;
+#  * 100 pairs, 6 chunks: two runs of 3, groups of 2 heads;
+#  * lead runs of 2 (1) chunks, three (two) of them to a workgroup, as at the
+#    small and large layers;
 #  * 256-token chunks walked as four 64-token blocks, ragged, one chunk a run;
 #  * 128-token chunks, groups of 4 heads, init.
 FUSED_BF16 = [
