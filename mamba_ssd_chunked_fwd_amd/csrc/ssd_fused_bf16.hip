@@ -366,7 +366,9 @@ __global__ __launch_bounds__(512) void fused_pair_bf16(
   // (16-byte reads of 16 rows x 4 column groups hit no bank twice when the
   // row stride is an odd multiple of 32 bytes: 288 here; at 272 every such
   // read took two passes)
-  constexpr int LS = TB + 8;          // L' row stride (bf16), columns in k-slot order
+  constexpr int LS = TB + 16;         // L' row stride (bf16), columns in k-slot order
+  // (160 bytes: the 16-byte reads of X^T L'^T hit no bank twice; the fewer
+  // 8-byte L' writes take more passes than at 144, which measured slower)
   constexpr uint32_t kYB = YBF16 ? 2 : 4;
   constexpr uint32_t kStateBytes = kHeadDim * N * 4;
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TB * XS];
