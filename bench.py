@@ -342,7 +342,41 @@ class WorkloadRun:
                                              for i in range(nlaunch)])}
         names = list(dict.fromkeys(self.kernels + THREE_STAGES))
         for n in names:
+            if n == "chunk_cumsum":
+                continue
             out[n] = graph_time_ms([lambda i=i, n=n: self.stage(n, i) for i in range(nlaunch)])
+        out.update(self.time_cumsum(nlaunch))
+        return out
+
+    def time_cumsum(self, nlaunch: int) -> dict:
+        """Stage 1 over its own rotating dt / g / dt_t sets (>= 1 GiB in
+        total, so no launch finds its operands in the last-level cache: the
+        stage's footprint is a few tens of MB, which one set of the step's
+        buffers would leave cache-resident), and two device-to-device copies
+        over rotating buffers as its floor: one moving the stage's own bytes
+        (dt read, g and dt_t written: 12 bytes per (token, head), half read
+        and half written) and one moving only its algorithmic bytes (8)."""
+        import torch
+        w, ssd, dev = self.w, self.ssd, self.dev
+        n = w.batch * w.seqlen * w.nheads
+        k = max(2, min(64, -(-(1 << 30) // (12 * n))))
+        dt0, A, T = self.sets[0]["dt"], self.sets[0]["A"], w.chunk_size
+        b, L, H = w.batch, w.seqlen, w.nheads
+        sets = [(dt0.clone(), torch.empty(b, H, L, device=dev), torch.empty(b, H, L, device=dev))
+                for _ in range(k)]
+        for i in range(k):
+            ssd.ssd_chunk_cumsum(sets[i][0], A, sets[i][1], sets[i][2], T)
+        calls = [lambda s=s: ssd.ssd_chunk_cumsum(s[0], A, s[1], s[2], T) for s in sets]
+        out = {"chunk_cumsum": graph_time_ms(calls * max(1, nlaunch // k))}
+        del sets
+        for key, words in (("copy_same_bytes", 3 * n // 2), ("copy_alg_bytes", n)):
+            bufs = [(torch.empty(words, device=dev), torch.empty(words, device=dev))
+                    for _ in range(k)]
+            calls = [lambda b=b: b[1].copy_(b[0]) for b in bufs]
+            for c in calls:
+                c()
+            out[key] = graph_time_ms(calls * max(1, nlaunch // k))
+            del bufs
         return out
 
     def summary(self, dur: dict) -> dict:
@@ -362,6 +396,16 @@ class WorkloadRun:
                 e["design_extra_bytes"] = extra
                 e["hbm_frac_with_extra"] = round(
                     (self.by[n] + extra) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            if n == "chunk_cumsum" and "copy_alg_bytes" in dur:
+                same, alg = dur["copy_same_bytes"], dur["copy_alg_bytes"]
+                e["copy_floor"] = {
+                    "same_bytes_us": round(same * 1e3, 2),
+                    "alg_bytes_us": round(alg * 1e3, 2),
+                    "alg_bytes_hbm_frac": round(
+                        self.by[n] / (alg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "note": "device copies over rotating buffers moving the stage's own "
+                            "bytes and only its algorithmic bytes: what a kernel with no "
+                            "arithmetic reaches at this size"}
             if n in issued:
                 peak_tf = BF16_MFMA_TFLOPS if kind[n] == "bf16" else FP32_MFMA_TFLOPS
                 tf_alg = self.fl[n] / (ms * 1e-3) / 1e12
