@@ -379,6 +379,9 @@ class WorkloadRun:
             del bufs
         return out
 
+    def targets(self, dur: dict) -> dict:
+        return _targets(self.w, self.by, dur)
+
     def summary(self, dur: dict) -> dict:
         """The configs-map entry: tokens/s, per-stage microseconds, HBM
         fractions and the output stage's matrix-core fractions."""
@@ -427,7 +430,8 @@ class WorkloadRun:
         if "state_and_out" in self.kernels:
             extra["two_kernel_path_us"] = {n: round(dur[n] * 1e3, 2)
                                            for n in ("fwd_pass_state", "compute_out")}
-        return {"shape": {"batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+        return {"north_star_targets": self.targets(dur),
+                "shape": {"batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                           "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                           "chunk_size": w.chunk_size, "dtype": w.dtype},
                 "tokens_per_s": round(w.tokens / (step_ms * 1e-3), 1),
@@ -437,6 +441,35 @@ class WorkloadRun:
                 "hbm_floor_us": round(step_bytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
                 "step_kernels": self.kernels,
                 "stages": stages, **extra}
+
+
+def _targets(w, by, dur) -> dict:
+    """The per-stage targets (stage 1 and the state pass at >= 0.6 of the HBM
+    peak on their algorithmic bytes; the output stage at >= 40% of the bf16
+    matrix peak) against this run's stage kernels, whether or not ssd_forward
+    runs stages 2 and 3 fused at this workload.  For the output stage also
+    the matrix fraction its issued work would reach if the kernel ran at the
+    HBM peak: the most any kernel of that design can show."""
+    def hbm(n):
+        return by[n] / (dur[n] * 1e-3) / 1e9 / HBM_PEAK_GBS
+    issued = issued_mfma_flop(w)["compute_out"]
+    # the peak of the instruction the output stage issues (bf16 unless fp32
+    # inputs come in 256-token chunks)
+    peak = BF16_MFMA_TFLOPS if mfma_kind(w)["compute_out"] == "bf16" else FP32_MFMA_TFLOPS
+    a1, a2 = hbm("chunk_cumsum"), hbm("fwd_pass_state")
+    iss = issued / (dur["compute_out"] * 1e-3) / 1e12 / peak
+    at_peak = issued / (by["compute_out"] / (HBM_PEAK_GBS * 1e9)) / 1e12 / peak
+    rec = committed_profile(w.name, "compute_out", "mfma")
+    busy = rec["mfma_busy_frac"] if rec is not None else None
+    a3 = busy if busy is not None else iss
+    return {"a1_chunk_cumsum_hbm_frac": round(a1, 4), "a1_met": a1 >= 0.6,
+            "a2_fwd_pass_state_hbm_frac": round(a2, 4), "a2_met": a2 >= 0.6,
+            "a3_compute_out_mfma_busy_frac": None if busy is None else round(busy, 4),
+            "a3_compute_out_mfma_issued_frac": round(iss, 4),
+            "a3_mfma_issued_frac_at_hbm_peak": round(min(1.0, at_peak), 4),
+            "a3_met": a3 >= 0.4, "a3_reachable_at_hbm_peak": at_peak >= 0.4,
+            "targets": {"a1": "hbm >= 0.6", "a2": "hbm >= 0.6",
+                        "a3": f"{mfma_kind(w)['compute_out']} mfma >= 0.4"}}
 
 
 def gdn_bench(ssd, c, make, dev, stream, nrep):

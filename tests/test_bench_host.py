@@ -124,3 +124,33 @@ def test_bf16_fused_pass_plans_and_accounting():
     run_pass = b * H * (32 - 6) * 2 * (2 * 64 * P * N)
     assert bench.issued_mfma_flop(w)["state_and_out"] == \
         b * H * nblk * per_block + b * (H // 2) * nblk * 10 * 16 * 16 * N * 2 + run_pass
+
+
+def test_north_star_target_summary():
+    """The targets object: stage 1 and the state pass against 0.6 of the
+    HBM peak on their algorithmic bytes, the output stage against 40% of the
+    matrix peak, with the fraction the output stage's issued work would reach
+    at the HBM peak (the large layer with fp32 y: 91.8 issued GFLOP over
+    690 MB, about 43% of the bf16 peak, so reachable there)."""
+    import bench
+    from ssd_workloads import WORKLOADS
+    w = WORKLOADS["large_bf16"]
+    by, _ = bench.algorithmic(w, 4)
+    # durations (ms) putting stage 1 at exactly 0.6 and the state pass at 0.3
+    dur = {"chunk_cumsum": by["chunk_cumsum"] / (0.6 * 8e12) * 1e3,
+           "fwd_pass_state": by["fwd_pass_state"] / (0.3 * 8e12) * 1e3,
+           "compute_out": 0.2}
+    t = bench._targets(w, by, dur)
+    assert abs(t["a1_chunk_cumsum_hbm_frac"] - 0.6) < 1e-3 and t["a1_met"]
+    assert abs(t["a2_fwd_pass_state_hbm_frac"] - 0.3) < 1e-3 and not t["a2_met"]
+    iss = bench.issued_mfma_flop(w)["compute_out"]
+    assert abs(t["a3_compute_out_mfma_issued_frac"] - iss / 0.2e-3 / 2.5e15) < 1e-3
+    at_peak = iss / (by["compute_out"] / 8e12) / 2.5e15
+    assert 0.4 < at_peak < 0.45
+    assert t["a3_reachable_at_hbm_peak"]
+    # the small layer's output stage cannot reach 40% even at the HBM peak
+    ws = WORKLOADS["small_bf16"]
+    bys, _ = bench.algorithmic(ws, 4)
+    ts = bench._targets(ws, bys, {k: 1.0 for k in ("chunk_cumsum", "fwd_pass_state",
+                                                   "compute_out")})
+    assert not ts["a3_reachable_at_hbm_peak"]
