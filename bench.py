@@ -56,7 +56,8 @@ CONFIG_ORDER = ["tiny_fp32", "small_bf16", "large_bf16", "long_bf16", "wide_fp32
 # the kernel sources of each stage (the state pass runs as one kernel or as
 # chunk_state + state_passing, chosen by shape)
 STAGE_SOURCES = {"chunk_cumsum": ["ssd_chunk_cumsum.hip"],
-                 "fwd_pass_state": ["ssd_fwd_pass_state.hip", "ssd_state_two_level.hip"],
+                 "fwd_pass_state": ["ssd_fwd_pass_state.hip", "ssd_state_two_level.hip",
+                                    "ssd_state_pair_f32.hip"],
                  "compute_out": ["ssd_compute_out.hip"],
                  "state_and_out": ["ssd_fused_f32.hip", "ssd_fused_bf16.hip"]}
 THREE_STAGES = ["chunk_cumsum", "fwd_pass_state", "compute_out"]
@@ -142,12 +143,21 @@ def design_extra_bytes(w) -> dict:
     return {"chunk_cumsum": 4 * w.batch * w.seqlen * w.nheads}
 
 
+def state_pair(w, cus: int = 256) -> bool:
+    """Whether stage 2 runs the fp32 head-pair kernel (the library's own
+    rule): fp32 inputs, 64-token chunks, N = 64, an even group size and a
+    (batch, head pair) per CU."""
+    return (w.dtype == "fp32" and w.chunk_size == 64 and w.dstate == 64
+            and (w.nheads // w.ngroups) % 2 == 0 and w.batch * w.nheads // 2 >= cus)
+
+
 def mfma_kind(w) -> dict:
     """The matrix instruction each stage issues: bf16 (16x16x32) or fp32
     (16x16x4).  fp32 inputs run stage 3 on bf16 instructions (three-term
-    splits) for chunks of up to 128 tokens."""
+    splits) for chunks of up to 128 tokens, and stage 2 where the head-pair
+    kernel applies."""
     out_bf16 = w.dtype == "bf16" or w.chunk_size <= 128
-    return {"fwd_pass_state": "bf16" if w.dtype == "bf16" else "fp32",
+    return {"fwd_pass_state": "bf16" if w.dtype == "bf16" or state_pair(w) else "fp32",
             "compute_out": "bf16" if out_bf16 else "fp32",
             "state_and_out": "bf16"}
 
@@ -171,7 +181,10 @@ def issued_mfma_flop(w) -> dict:
         a2 = 2 * (2 * b * L * H * P * N)                          # P^T: w o x hi + lo
     elif mfma_kind(w)["compute_out"] == "bf16":
         out = 6 * (b * nc * H * (2 * T * P * N + lx32) + b * nc * G * cb)
-        a2 = 2 * b * L * H * P * N
+        # the head-pair state kernel: six bf16 products per fp32 product,
+        # over whole 64-token chunks
+        a2 = (6 * 2 * b * nc * T * H * P * N if state_pair(w)
+              else 2 * b * L * H * P * N)
     else:
         out = b * nc * H * (2 * T * P * N + lx16) + b * nc * G * cb
         a2 = 2 * b * L * H * P * N

@@ -28,7 +28,7 @@ SOURCES = ["ssd_api.cpp", "ssd_chunk_cumsum.hip", "ssd_fwd_pass_state.hip",
            "ssd_compute_out.hip", "ssd_decode_step.hip",
            "ssd_causal_conv1d.hip", "ssd_gdn.hip",
            "ssd_state_two_level.hip", "ssd_forward_noalloc.hip",
-           "ssd_fused_f32.hip", "ssd_fused_bf16.hip"]
+           "ssd_fused_f32.hip", "ssd_fused_bf16.hip", "ssd_state_pair_f32.hip"]
 
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -698,6 +698,9 @@ int launch_fwd_pass_state(const void* x, const void* B, const float* dt_t,
   }
   if (bf16_in)
     return launch_chunk<true>(x, B, dt_t, g, init_state, states, final_state, s, st);
+  if (state_pair_f32_applies(s, false))
+    return launch_state_pair_f32((const float*)x, (const float*)B, dt_t, g, init_state, states,
+                                 final_state, s, stream);
   return launch_chunk<false>(x, B, dt_t, g, init_state, states, final_state, s, st);
 }
 

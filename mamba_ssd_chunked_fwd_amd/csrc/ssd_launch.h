@@ -32,6 +32,15 @@ int launch_compute_out(const void* x, const void* B, const void* C,
                        const float* D, void* y, bool bf16_in, bool bf16_out,
                        const Shape& s, void* stream);
 
+// Stage 2 for fp32 inputs with 64-token chunks, N = 64, an even group size
+// and at least one (b, head pair) per compute unit: one workgroup per head
+// pair sharing each staged B tile, on bf16 matrix instructions with exact
+// three-term splits (launch_fwd_pass_state takes it where it applies).
+bool state_pair_f32_applies(const Shape& s, bool bf16_in);
+int launch_state_pair_f32(const float* x, const float* B, const float* dt_t, const float* g,
+                          const float* init, float* states, float* fin, const Shape& s,
+                          void* stream);
+
 // Stages 2 and 3 of ssd_forward: the fused single-pass kernel where it
 // applies (fp32 inputs, 64-token chunks, N = 64, at least one (b, head pair)
 // per compute unit), otherwise launch_fwd_pass_state then

@@ -60,14 +60,20 @@ def test_issued_matrix_work_of_the_output_stage():
         by, fl = bench.algorithmic(w, 4)
         iss = bench.issued_mfma_flop(w)
         assert iss["compute_out"] >= fl["compute_out"], name
-        assert iss["fwd_pass_state"] == (2 if w.dtype == "bf16" else 1) * fl["fwd_pass_state"]
+        # bf16: hi + lo of w o x; the wide fp32 layer's stage 2 runs the
+        # head-pair kernel on bf16 instructions, six products per product
+        assert iss["fwd_pass_state"] == (2 if w.dtype == "bf16" else 6) * fl["fwd_pass_state"]
     # wide fp32 on bf16 instructions (three-term splits, six products):
     # T = 64, 4 row blocks; C S^T 2 T P N per (b, c, h); L'X in 32-token
     # steps, 1 + 1 + 2 + 2 of them over the row blocks; C B^T 10 of 16 blocks
     # once per (b, c, group)
     w = WORKLOADS["wide_fp32"]
-    assert bench.mfma_kind(w) == {"fwd_pass_state": "fp32", "compute_out": "bf16",
+    assert bench.mfma_kind(w) == {"fwd_pass_state": "bf16", "compute_out": "bf16",
                                   "state_and_out": "bf16"}
+    # the tiny fp32 layer (one head pair) keeps the fp32-instruction state pass
+    assert bench.mfma_kind(WORKLOADS["tiny_fp32"])["fwd_pass_state"] == "fp32"
+    assert bench.issued_mfma_flop(WORKLOADS["tiny_fp32"])["fwd_pass_state"] == \
+        bench.algorithmic(WORKLOADS["tiny_fp32"], 4)[1]["fwd_pass_state"]
     b, H, G, P, N, nc = 64, 48, 8, 64, 64, 16
     per_item = 2 * 64 * P * N + 6 * 32 * 16 * P * 2
     assert bench.issued_mfma_flop(w)["compute_out"] == \

@@ -80,6 +80,10 @@ SMALL = [
     _wl("fp32_T64_N64_fused_two_pairs_per_workgroup_init", "fp32", 128, 130, 8, 1, 64, 64, True),
     _wl("fp32_T64_N64_fused_weak_decay_short", "fp32", 96, 40, 6, 3, 64, 64, True,
         -4.0, (-6.0, -5.0)),
+    # groups of three heads: the stage-2 head-triple kernel (one item per
+    # three heads, 288 items), ragged, with init
+    _wl("fp32_T64_N64_head_triples_ragged_init", "fp32", 96, 200, 9, 3, 64, 64, True,
+        -1.0, (-1.0, 2.0)),
 ]
 
 
@@ -113,6 +117,14 @@ def test_small_end_to_end(ssd, w):
 # N = 128 (ssd_forward runs those as the fused pass, so the state-pass tiles
 # they were chosen to select are reached through the stage calls here)
 STAGE_CASES = SMALL[:8] + [w for w in SMALL[8:] if w.dtype == "bf16" and w.dstate == 128]
+# fp32 shapes with 64-token chunks, N = 64, a group size of a multiple of 2
+# or 3 heads and at least one item of that many heads per compute unit: the
+# stage-2 call runs the head-pair or head-triple state kernel on them (ragged
+# and single partial chunks, init, several items per workgroup)
+STAGE_CASES += [w for w in SMALL if w.name in (
+    "fp32_T64_N64_3head_shared_B_one_chunk", "fp32_T64_N64_fused_pairs_ragged_init",
+    "fp32_T64_N64_fused_two_pairs_per_workgroup_init", "fp32_T64_N64_fused_weak_decay_short",
+    "fp32_T64_N64_head_triples_ragged_init")]
 
 
 @pytest.mark.parametrize("w", STAGE_CASES, ids=lambda w: w.name)
@@ -446,6 +458,66 @@ def test_fused_forward_init_aliases_final(ssd):
     ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
                          inp["init_state"], chunk_size=T)
     assert_close(_np(outs[1][2]), ref["final"], "fp32", "final (aliased)")
+
+
+def test_state_pass_init_aliases_final(ssd):
+    """ssd_fwd_pass_state with init_state and final_state as one buffer (a
+    sequence continued in place) gives what separate buffers give, on the
+    head-pair fp32 state kernel (280 pairs, 4 chunks, ragged)."""
+    w, inp = _fused_case(36)
+    dev = device_inputs(inp, "fp32")
+    T = w.chunk_size
+    b, L, H, nc = w.batch, w.seqlen, w.nheads, w.nchunks
+    g = torch.empty(b, H, L, device=DEV)
+    dt_t = torch.empty(b, H, L, device=DEV)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, dt_t, T)
+    outs = []
+    for alias in (False, True):
+        st = torch.full((b, H, nc, 64, 64), float("nan"), device=DEV)
+        init = dev["init_state"].clone()
+        fin = init if alias else torch.empty_like(init)
+        ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dt_t, g, init, st, fin, T)
+        torch.cuda.synchronize()
+        outs.append((st, fin))
+    for a, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a, b_)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                         inp["init_state"], chunk_size=T)
+    assert_close(_np(outs[1][0]), ref["states"], "fp32", "stage-2 states (aliased)")
+    assert_close(_np(outs[1][1]), ref["final"], "fp32", "stage-2 final (aliased)")
+
+
+def test_wide_state_pass_full_size(ssd):
+    """The stage-2 call alone at the wide fp32 layer's full size (64 x 1024
+    tokens, 48 heads in 8 groups: the head-pair state kernel), every state
+    and final element against the oracle."""
+    w = WORKLOADS["wide_fp32"]
+    log(f"[full stage 2] {w}")
+    inp = make_inputs(w)
+    dev = device_inputs(inp, w.dtype)
+    T = w.chunk_size
+    b, L, H, P, N, nc = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.nchunks
+    g = torch.empty(b, H, L, device=DEV)
+    dt_t = torch.empty(b, H, L, device=DEV)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, dt_t, T)
+    states = torch.full((b, H, nc, P, N), float("nan"), device=DEV)
+    final = torch.full((b, H, P, N), float("nan"), device=DEV)
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dt_t, g, dev["init_state"], states, final, T)
+    torch.cuda.synchronize()
+    sp = states.reshape(b * H, nc, P, N)
+    fp = final.reshape(b * H, P, N)
+
+    def ref(p0, p1):
+        r = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                           inp["init_state"], chunk_size=T, pairs=list(range(p0, p1)),
+                           want_y=False)
+        return {"states": r["states"], "final": r["final"]}
+
+    def got(p0, p1):
+        return {"states": _np(sp[p0:p1]), "final": _np(fp[p0:p1])}
+
+    compare_all_pairs(ref, got, b * H, pairs_per_batch(w), w.dtype, ("states", "final"),
+                      label="stage 2: ")
 
 
 def test_fused_forward_bf16_output(ssd):
