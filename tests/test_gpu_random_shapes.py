@@ -70,6 +70,49 @@ def test_random_shape(ssd, case):
     assert_close(_np(y), ref["y"], dtype, "y", y_bf16=ybf16)
 
 
+# ---- fp32 layers with many (batch, head) chains: 64-token chunks, N = 64,
+# at least 512 chains, so ssd_forward runs the fused pass and the stage-2
+# call the head-pair state kernel (where the group size is even) or the
+# fp32-instruction one; both against the oracle
+
+def _draw_many(n=8, seed=2028):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        H = int(rng.choice([2, 4, 6, 8, 12]))
+        G = int(rng.choice([g for g in range(1, H + 1) if H % g == 0]))
+        b = -(-512 // H) + int(rng.integers(0, 40))
+        L = int(rng.integers(1, 301))
+        out.append((i, b, L, H, G, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", _draw_many(), ids=lambda c: "m%02d_b%d_L%d_H%d_G%d%s" % (
+    c[0], c[1], c[2], c[3], c[4], "_init" if c[5] else ""))
+def test_random_many_chains_fp32(ssd, case):
+    i, b, L, H, G, init = case
+    w = Workload("many", b, L, H, 64, 64, G, 64, "fp32", -1.0, -1.0, 2.0, 0.1 if init else None)
+    log(f"[random many] {case}")
+    inp = make_inputs(w, seed=700 + i)
+    ref = oracle.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                         inp["init_state"], chunk_size=64)
+    dev = device_inputs(inp, "fp32")
+    y, states, final = ssd.forward(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"],
+                                   dev["D"], dev["init_state"], chunk_size=64)
+    g = torch.empty(b, H, L, device=DEV)
+    dt_t = torch.empty(b, H, L, device=DEV)
+    ssd.ssd_chunk_cumsum(dev["dt"], dev["A"], g, dt_t, 64)
+    s2 = torch.full_like(states, float("nan"))
+    f2 = torch.full_like(final, float("nan"))
+    ssd.ssd_fwd_pass_state(dev["x"], dev["B"], dt_t, g, dev["init_state"], s2, f2, 64)
+    torch.cuda.synchronize()
+    assert_close(_np(states), ref["states"], "fp32", "states")
+    assert_close(_np(final), ref["final"], "fp32", "final")
+    assert_close(_np(y), ref["y"], "fp32", "y")
+    assert_close(_np(s2), ref["states"], "fp32", "stage-2 states")
+    assert_close(_np(f2), ref["final"], "fp32", "stage-2 final")
+
+
 # ---- the other entry points, drawn the same way
 
 def _draw_conv(n=16, seed=2025):
