@@ -19,8 +19,10 @@
 //   XCD walk consecutive pairs of a group at once and share B in its L2.
 // * 8 waves: waves 4q..4q+3 on head q of the pair, wave 4q + w owning state
 //   rows p = 16w..16w+15 and all 64 columns, transposed in the accumulators
-//   (lane (p, lq) of block nb holds S[p][16 nb + 4 lq + 0..3]), so state
-//   stores are 16-byte writes straight from registers.
+//   (lane (p, lq) of block nb holds S[p][16 nb + 4 lq + 0..3]).  State
+//   stores pass through the wave's own rows of an x^T buffer it is done
+//   with, so each store instruction writes four whole 256-byte rows instead
+//   of 16 rows x 64 bytes (2% faster).
 // * The chunk's B tile is staged once for both heads, split exactly into
 //   three bf16 planes (v = hi + mid + lo); the update reads its transpose
 //   with the LDS transpose read.  The decay weight w_t = dt_t 2^{g_last - g_t}
@@ -217,8 +219,13 @@ __global__ __launch_bounds__(512) void state_pair_f32(
   };
   // The state entering a step's chunk: init_state (or zero) at a pair's
   // first chunk, else the accumulators as the previous step left them;
-  // stored to states.
-  auto enter = [&](const StepP& st) {
+  // stored to states.  The store goes through this wave's own 16 rows of
+  // x^T buffer fb (no other wave reads them, and the wave is done with
+  // them): each lane writes its accumulator blocks there, then reads back
+  // 16-byte pieces of whole 256-byte state rows, so each store instruction
+  // writes four consecutive rows, 1 KB of consecutive bytes, rather than
+  // 16 rows x 64 bytes.
+  auto enter = [&](const StepP& st, int fb) {
     const size_t hrow = (size_t)st.b * H + st.h0 + hq;
     if (st.c == 0) {
       // no initial state: an empty range, every load reads zero
@@ -227,15 +234,22 @@ __global__ __launch_bounds__(512) void state_pair_f32(
 #pragma unroll
       for (int nb = 0; nb < N / 16; ++nb) sacc[nb] = load_f32x4(ires, so_lane + 64 * nb);
     }
+    float* reg = xt[fb][hq] + 16 * w * XT;
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) *(f32x4*)(reg + lr * XT + 16 * nb + 4 * lq) = sacc[nb];
+    __builtin_amdgcn_wave_barrier();
     const rsrc_t sres = make_rsrc(states + (hrow * nc + st.c) * (kHeadDim * N), kStateBytes);
 #pragma unroll
-    for (int nb = 0; nb < N / 16; ++nb)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sacc[nb]), sres,
-                                             so_lane + 64 * nb, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + (lane >> 4), c = lane & 15;
+      const f32x4 v = *(const f32x4*)(reg + r * XT + 4 * c);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), sres,
+                                             (uint32_t)((16 * w + r) * N + 4 * c) * 4, 0, 0);
+    }
   };
 
   stage(ra, 0);
-  enter(ra.st);
+  enter(ra.st, 1);
   __syncthreads();
 
   // step k (staged in buffer buf); r held it and is reloaded with step
@@ -289,7 +303,7 @@ __global__ __launch_bounds__(512) void state_pair_f32(
                                                so_lane + 64 * nb, 0, 0);
     }
     // the state entering the next step's chunk
-    if (has_next) enter(rn.st);
+    if (has_next) enter(rn.st, buf);
     __syncthreads();  // buffer buf ^ 1 is staged; buffer buf's reads are done
   };
 
