@@ -267,16 +267,23 @@ def cpu_baseline(w, inp, min_seconds: float = 10.0):
                        f"{total:.1f} s in total (median run {statistics.median(times):.3f} s)")}
 
 
-def graph_time_ms(calls, nrep: int = 3) -> float:
+def graph_time_ms(calls, nrep: int = 3, settle_ms: float = 30.0) -> float:
     """Mean duration of one call: the calls are captured once in a HIP graph,
-    the graph is replayed once untimed and `nrep` times between two HIP
-    events on the current stream."""
+    the graph is replayed untimed until `settle_ms` have passed (at least
+    once; the capture leaves the GPU idle, and its clocks take some
+    milliseconds of work to come back to their steady state), then `nrep`
+    times between two HIP events on the current stream."""
     import torch
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for f in calls:
             f()
-    g.replay()
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= settle_ms:
+            break
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -652,6 +659,9 @@ def main() -> int:
                     help="skip the Gated DeltaNet kernels' timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (HBM counter scale)")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps before the warmup steps, until this much time has "
+                         "passed (the GPU's clocks reach their steady state)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
@@ -672,7 +682,17 @@ def main() -> int:
     nlaunch = max(10, min(40, args.steps // 2))
 
     run = WorkloadRun(ssd, w, ty, dev)
-    # ---- the step: ssd_forward, the whole hot path, as a user calls it
+    # ---- the step: ssd_forward, the whole hot path, as a user calls it.
+    # Before the warmup steps, untimed steps until --settle-ms have passed: a
+    # few milliseconds of work leave this GPU's clocks ramping, and the steps
+    # right after them run about 15% slower than the sustained rate.
+    settle_steps, t_settle = 0, time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(10):
+            run.forward(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for i in range(args.warmup):
         run.forward(i)
     # the timed steps carry no events between them: nothing but the step's
@@ -746,6 +766,9 @@ def main() -> int:
         "stages": stages,
         **({"two_kernel_path_us": head["two_kernel_path_us"]}
            if "two_kernel_path_us" in head else {}),
+        "settle": {"ms": round(settle_ms, 1), "steps": settle_steps,
+                   "note": "untimed steps before the warmup steps, until the GPU's clocks "
+                           "settle"},
         "ssd_forward_graph_us": head["step_us"],
         "effective_TFLOP_per_s": round(step_flop / (ms_per_step * 1e-3) / 1e12, 2),
         "hbm_floor_ms": round(head["hbm_floor_us"] / 1e3, 5),
