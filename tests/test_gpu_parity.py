@@ -80,8 +80,9 @@ SMALL = [
     _wl("fp32_T64_N64_fused_two_pairs_per_workgroup_init", "fp32", 128, 130, 8, 1, 64, 64, True),
     _wl("fp32_T64_N64_fused_weak_decay_short", "fp32", 96, 40, 6, 3, 64, 64, True,
         -4.0, (-6.0, -5.0)),
-    # groups of three heads: the stage-2 head-triple kernel (one item per
-    # three heads, 288 items), ragged, with init
+    # groups of three heads (odd group size: the stage-2 call keeps the
+    # fp32-instruction kernel, ssd_forward the single-head fused pass),
+    # ragged, with init
     _wl("fp32_T64_N64_head_triples_ragged_init", "fp32", 96, 200, 9, 3, 64, 64, True,
         -1.0, (-1.0, 2.0)),
 ]
@@ -117,10 +118,12 @@ def test_small_end_to_end(ssd, w):
 # N = 128 (ssd_forward runs those as the fused pass, so the state-pass tiles
 # they were chosen to select are reached through the stage calls here)
 STAGE_CASES = SMALL[:8] + [w for w in SMALL[8:] if w.dtype == "bf16" and w.dstate == 128]
-# fp32 shapes with 64-token chunks, N = 64, a group size of a multiple of 2
-# or 3 heads and at least one item of that many heads per compute unit: the
-# stage-2 call runs the head-pair or head-triple state kernel on them (ragged
-# and single partial chunks, init, several items per workgroup)
+# fp32 shapes with 64-token chunks and N = 64: with an even group size and
+# at least one (batch, head pair) per compute unit the stage-2 call runs the
+# head-pair state kernel on them (ragged and single partial chunks, init,
+# several pairs per workgroup; strong decay is compared path to path in
+# test_fused_forward_matches_stage_calls), with an odd one the
+# fp32-instruction kernel
 STAGE_CASES += [w for w in SMALL if w.name in (
     "fp32_T64_N64_3head_shared_B_one_chunk", "fp32_T64_N64_fused_pairs_ragged_init",
     "fp32_T64_N64_fused_two_pairs_per_workgroup_init", "fp32_T64_N64_fused_weak_decay_short",
@@ -361,7 +364,8 @@ def _fused_case(seed, init=True, dt_shift=-1.0, a=(-1.0, 2.0), H=14, G=7):
 FUSED_VS_STAGES_TOL = 2e-5
 
 
-@pytest.mark.parametrize("regime", ["moderate_decay_pairs", "extreme_decay_single_heads"])
+@pytest.mark.parametrize("regime", ["moderate_decay_pairs", "extreme_decay_single_heads",
+                                    "extreme_decay_pairs"])
 def test_fused_forward_matches_stage_calls(ssd, regime):
     """The fused pass of ssd_forward and the separate stage-2 and stage-3
     kernels agree to fp32 rounding (they sum in different orders).
@@ -373,8 +377,11 @@ def test_fused_forward_matches_stage_calls(ssd, regime):
     final state (a sum the last tokens dominate) against the oracle."""
     if regime == "moderate_decay_pairs":
         w, inp = _fused_case(31)
-    else:
+    elif regime == "extreme_decay_single_heads":
         w, inp = _fused_case(34, init=False, dt_shift=1.0, a=(2.0, 3.0), H=9, G=3)
+    else:
+        # groups of two heads: the stage-2 call runs the head-pair state kernel
+        w, inp = _fused_case(37, init=True, dt_shift=1.0, a=(2.0, 3.0))
     log(f"[fused] {regime} {w}")
     dev = device_inputs(inp, "fp32")
     T = w.chunk_size
